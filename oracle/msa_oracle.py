@@ -1,0 +1,277 @@
+"""Plain, slow CPU oracle for the MiniMax Sparse Attention (MSA) forward.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg import this module. The product path (the HIP library and its
+Python binding) never imports, calls or links it, and this module imports
+nothing from the product path.
+
+Arithmetic is float64 NumPy throughout; bfloat16 inputs are widened exactly.
+Each function writes out the definition it follows; a matrix product is the
+only library primitive used, plus a stable sort for selection.
+
+Sources (web pages; cited by title and section):
+  [MSA summary]   "MiniMax Sparse Attention (MSA): Turning Theoretical Sparse
+                  Attention Gains into Real GPU Speedups" (forum summary of the
+                  MSA paper).
+  [Flash-MSA]     "Flash-MSA: Accelerating Million-Token Training with Sparse
+                  Attention Kernels" (blog post).
+  [flash-msa pkg] "flash-msa 0.1.0" (package page).
+
+Readings taken where the pages leave a step open (each is listed with its
+reason in the design notes at the repository root):
+  R1  index score = raw dot product of the index query head and the shared
+      index key head, no scale or activation ([MSA summary] "GPU kernel
+      co-design": top-k runs on raw scores; [Flash-MSA] "Proxy attention":
+      proxy dot-product);
+  R2  block aggregation = max over the block's causally visible tokens
+      ([Flash-MSA] "About MSA" item 1: max-pooling; "Proxy attention": causal
+      local max per chunk);
+  R3  top_k counts the forced local block ([MSA summary] "Architecture":
+      k=16 blocks of 128 give about 2048 tokens per query);
+  R4  fewer visible blocks than top_k -> every visible block is selected, the
+      remaining slots hold -1;
+  R5  ties in the pooled score go to the lower block index;
+  R6  selected blocks are stored in ascending block order;
+  R7  index head g serves query heads [g*G, (g+1)*G), G = H_q / H_kv, and
+      uses KV head g ([Flash-MSA] "About MSA" item 3, "Note about scheduler":
+      MSA groups equal GQA groups);
+  R8  LSE is the natural log of sum_j exp(scale * q.k_j) over attended keys.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+DEFAULT_BLOCK = 128
+
+
+def _f64(x) -> np.ndarray:
+    """Widen an array-like (NumPy array or CPU torch tensor, any float dtype) to float64."""
+    if hasattr(x, "detach"):  # torch tensor: bf16 has no NumPy dtype, widen in torch first
+        import torch  # local import: torch is only used to unwrap tensors
+
+        return x.detach().to(device="cpu", dtype=torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def n_blocks(seqlen: int, block_size: int = DEFAULT_BLOCK) -> int:
+    return -(-seqlen // block_size)
+
+
+def _positions(seqlen: int, positions: Optional[Sequence[int]]) -> np.ndarray:
+    if positions is None:
+        return np.arange(seqlen, dtype=np.int64)
+    p = np.asarray(positions, dtype=np.int64)
+    if p.ndim != 1 or (p.size and (p.min() < 0 or p.max() >= seqlen)):
+        raise ValueError("positions must be a 1-D list of query positions inside the sequence")
+    return p
+
+
+# ---------------------------------------------------------------------------
+# Stage 1+2: index scores and causal block max-pool
+# ---------------------------------------------------------------------------
+def index_scores(q_idx, k_idx, block_size: int = DEFAULT_BLOCK,
+                 positions: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Pooled index scores.
+
+    [MSA summary] "Architecture: two-stage block-sparse attention": one index
+    query head per GQA group and one shared index key head score every visible
+    key token, and the token scores are aggregated into blocks. [Flash-MSA]
+    "About MSA" item 1 and "Proxy attention": the aggregation is a max, taken
+    causally inside the query's own block.
+
+        s[b, g, t, j]      = sum_e q_idx[b, t, g, e] * k_idx[b, j, e]     for j <= t
+        pooled[b, g, t, c] = max { s[b, g, t, j] : j in block c, j <= t }  for c <= t // B
+        pooled[b, g, t, c] = -inf                                         for c >  t // B
+
+    q_idx: [B, N, H_idx, D]; k_idx: [B, N, D].
+    Returns float64 [B, H_idx, P, nblk] for the P requested positions (all N by default).
+    """
+    q = _f64(q_idx)
+    kk = _f64(k_idx)
+    B, N, H, D = q.shape
+    if kk.shape != (B, N, D):
+        raise ValueError("k_idx must be [B, N, D] matching q_idx")
+    pos = _positions(N, positions)
+    nblk = n_blocks(N, block_size)
+    out = np.full((B, H, pos.size, nblk), -np.inf)
+    # Rows are handled in groups that share a query block only so that one
+    # matrix product serves several rows; every row still gets exactly the
+    # definition above.
+    qblocks = pos // block_size
+    for b in range(B):
+        for qb in np.unique(qblocks):
+            rows = np.nonzero(qblocks == qb)[0]
+            ts = pos[rows]
+            hi = int(ts.max()) + 1
+            s = np.einsum("rhd,jd->rhj", q[b, ts], kk[b, :hi])  # [r, H, hi]
+            visible = np.arange(hi)[None, :] <= ts[:, None]       # [r, hi]: causal mask
+            s = np.where(visible[:, None, :], s, -np.inf)
+            for c in range(int(qb) + 1):
+                lo_j, hi_j = c * block_size, min((c + 1) * block_size, hi)
+                out[b, :, rows, c] = s[:, :, lo_j:hi_j].max(axis=-1)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Stage 3: top-k block selection with the local block forced
+# ---------------------------------------------------------------------------
+def block_topk(pooled, top_k: int, block_size: int = DEFAULT_BLOCK,
+               positions: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Selected key blocks per (batch, index head, query).
+
+    [MSA summary] "Architecture": the top-k blocks are kept per query and
+    group, and the block holding the query's own position is always kept.
+    [Flash-MSA] "Proxy attention" forces the local block by giving it an
+    infinite score. [MSA summary] "GPU kernel co-design": softmax keeps the
+    order, so the selection runs on raw scores.
+
+    For query t with local block c_loc = t // B:
+      * if c_loc + 1 <= top_k: every block 0..c_loc is selected (R4);
+      * else: c_loc plus the top_k - 1 largest pooled[c] over c < c_loc,
+        ordered by (score descending, block ascending) (R5).
+    The selection is written in ascending block order (R6), padded with -1.
+
+    pooled: [B, H, P, nblk] (as from ``index_scores``); ``positions`` names
+    the query position of each of the P rows (default 0..P-1).
+    Returns int32 [B, H, P, top_k].
+    """
+    pl = _f64(pooled)
+    B, H, P, nblk = pl.shape
+    if top_k < 1:
+        raise ValueError("top_k must be >= 1")
+    pos = np.arange(P, dtype=np.int64) if positions is None else np.asarray(positions, dtype=np.int64)
+    if pos.shape != (P,) or (P and (pos.min() < 0 or pos.max() // block_size >= nblk)):
+        raise ValueError("positions must give one query position per pooled row, inside the blocks")
+    out = np.full((B, H, P, top_k), -1, dtype=np.int32)
+    cloc = pos // block_size
+    for cl in np.unique(cloc):
+        rows = np.nonzero(cloc == cl)[0]
+        cl = int(cl)
+        if cl + 1 <= top_k:
+            out[:, :, rows, : cl + 1] = np.arange(cl + 1, dtype=np.int32)
+            continue
+        cand = pl[:, :, rows, :cl]                              # non-local visible blocks
+        order = np.argsort(-cand, axis=-1, kind="stable")       # stable: lower block wins ties
+        chosen = order[..., : top_k - 1]
+        sel = np.concatenate([chosen, np.full(chosen.shape[:-1] + (1,), cl)], axis=-1)
+        out[:, :, rows, :] = np.sort(sel, axis=-1).astype(np.int32)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Stage 4: exact softmax attention over the selected blocks (main branch)
+# ---------------------------------------------------------------------------
+def attended_keys(sel: np.ndarray, t: int, block_size: int = DEFAULT_BLOCK) -> np.ndarray:
+    """Key positions a query at position t attends to: j in a selected block and j <= t."""
+    parts = [np.arange(c * block_size, min((c + 1) * block_size, t + 1)) for c in sel if c >= 0]
+    if not parts:
+        return np.zeros(0, dtype=np.int64)
+    return np.concatenate(parts)
+
+
+def sparse_attention(q, k, v, block_idx, softmax_scale: float, block_size: int = DEFAULT_BLOCK,
+                     positions: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Main-branch attention restricted to the selected blocks.
+
+    [MSA summary] "Architecture": exact softmax attention for every query head,
+    computed only over the selected blocks, with no approximation inside them.
+    [Flash-MSA] "Main attention": a block-sparse (causal) flash attention
+    forward; "Forward": the main LSE is saved for the backward.
+
+    For query head h (group g = h // G) at position t, with K(t) the attended
+    keys (selected blocks of group g, causal):
+        z_j  = scale * <q[b,t,h], k[b,j,g]>      j in K(t)
+        O    = sum_j exp(z_j) v[b,j,g] / sum_j exp(z_j)
+        LSE  = log sum_j exp(z_j)
+    (evaluated with the usual max shift for range, which leaves both unchanged).
+
+    q: [B, N, H_q, D]; k, v: [B, N, H_kv, D]; block_idx: [B, H_kv, P, top_k]
+    rows for the P requested positions. Returns O float64 [B, P, H_q, D] and
+    LSE float64 [B, H_q, P].
+    """
+    qq, kk, vv = _f64(q), _f64(k), _f64(v)
+    bi = np.asarray(block_idx)
+    B, N, Hq, D = qq.shape
+    Hkv = kk.shape[2]
+    if Hq % Hkv:
+        raise ValueError("H_q must be a multiple of H_kv")
+    G = Hq // Hkv
+    pos = _positions(N, positions)
+    if bi.shape[:3] != (B, Hkv, pos.size):
+        raise ValueError("block_idx must be [B, H_kv, P, top_k] for the requested positions")
+    O = np.zeros((B, pos.size, Hq, D))
+    LSE = np.zeros((B, Hq, pos.size))
+    for b in range(B):
+        for i, t in enumerate(pos):
+            t = int(t)
+            for g in range(Hkv):
+                keys = attended_keys(bi[b, g, i], t, block_size)
+                qg = qq[b, t, g * G:(g + 1) * G]            # [G, D]
+                z = softmax_scale * (qg @ kk[b, keys, g].T)  # [G, n]
+                m = z.max(axis=-1, keepdims=True)
+                p = np.exp(z - m)
+                l = p.sum(axis=-1)
+                O[b, i, g * G:(g + 1) * G] = (p @ vv[b, keys, g]) / l[:, None]
+                LSE[b, g * G:(g + 1) * G, i] = m[:, 0] + np.log(l)
+    return O, LSE
+
+
+def msa_forward(q_idx, k_idx, q, k, v, top_k: int, softmax_scale: float,
+                block_size: int = DEFAULT_BLOCK, positions: Optional[Sequence[int]] = None):
+    """The whole forward: index scores -> pooled -> top-k -> sparse attention.
+
+    [Flash-MSA] "Forward": proxy (index) attention first, then the sparse main
+    attention; the main output and LSE are kept, and so are the block indices.
+    Returns (block_idx int32 [B,H_idx,P,top_k], O [B,P,H_q,D], LSE [B,H_q,P], pooled).
+    """
+    N = np.shape(q)[1]
+    pos = _positions(N, positions)
+    pooled = index_scores(q_idx, k_idx, block_size, pos)
+    bi = block_topk(pooled, top_k, block_size, positions=pos)
+    O, LSE = sparse_attention(q, k, v, bi, softmax_scale, block_size, pos)
+    return bi, O, LSE, pooled
+
+
+# ---------------------------------------------------------------------------
+# Parity helpers (comparison logic; no method arithmetic beyond the definitions above)
+# ---------------------------------------------------------------------------
+def near_tie_rows(pooled_ref, sel_a, sel_b, top_k: int, block_size: int = DEFAULT_BLOCK,
+                  positions: Optional[Sequence[int]] = None, rel: float = 1e-3):
+    """Classify rows where two selections differ.
+
+    A row is a near-tie when every block in the symmetric difference of the
+    two selections has a reference pooled score within ``rel`` (relative) of
+    the boundary score -- the smallest score among the reference's selected
+    non-local blocks -- and both selections contain the local block and the
+    same number of valid entries. Returns (n_mismatch, n_near_tie,
+    list of (b, h, row) that are mismatches but NOT near-ties).
+    """
+    pl = _f64(pooled_ref)
+    A = np.asarray(sel_a)
+    Bs = np.asarray(sel_b)
+    B, H, P, _ = A.shape
+    pos = np.arange(P) if positions is None else np.asarray(positions)
+    diff = np.any(A != Bs, axis=-1)
+    bad = []
+    n_tie = 0
+    for b, h, i in zip(*np.nonzero(diff)):
+        t = int(pos[i])
+        cl = t // block_size
+        a = set(int(x) for x in A[b, h, i] if x >= 0)
+        r = set(int(x) for x in Bs[b, h, i] if x >= 0)
+        ok = cl in a and cl in r and len(a) == len(r)
+        if ok:
+            nonlocal_ref = [c for c in r if c != cl]
+            bound = min(pl[b, h, i, c] for c in nonlocal_ref) if nonlocal_ref else None
+            for c in a.symmetric_difference(r):
+                s = pl[b, h, i, c]
+                if bound is None or not np.isfinite(s) or abs(s - bound) > rel * max(abs(s), abs(bound)):
+                    ok = False
+                    break
+        if ok:
+            n_tie += 1
+        else:
+            bad.append((int(b), int(h), int(i)))
+    return int(diff.sum()), n_tie, bad

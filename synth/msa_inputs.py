@@ -1,0 +1,118 @@
+"""Seeded synthetic inputs for the MSA forward path.
+
+This module only draws random numbers and lays them out. It holds none of the
+method's arithmetic, so both the CPU oracle's tests and the GPU path may use it.
+
+Recipe (the same for every workload):
+  * one ``torch.Generator('cpu')`` seeded with the workload's seed;
+  * float32 standard-normal draws in this fixed order:
+      1. Q      [B, N, H_q, 128]
+      2. K      [B, N, H_kv, 128]
+      3. V      [B, N, H_kv, 128]
+      4. Q_idx  [B, N, H_idx, 128]
+      5. K_idx  [B, N, 128]
+      6. U      [B, nblk, 128], each row scaled to unit length
+      7. dO     [B, N, H_q, 128]   (training-step workload only)
+  * K_idx[b, j] += 0.5 * U[b, j // 128]  (a per-block offset that gives the
+    index scores a block structure, as trained index keys would have);
+  * every tensor rounded to bfloat16 (round-to-nearest-even).
+
+The pages measure on trained models and public benchmarks that are not
+available here; these inputs stand in for them with the head shapes the pages
+name (64 query heads, 4 KV heads, head dim 128 for the 109B model).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional
+
+import torch
+
+BLOCK_SIZE = 128
+HEAD_DIM = 128
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    seqlen: int
+    h_q: int
+    h_kv: int
+    h_idx: int
+    top_k: int
+    seed: int
+    head_dim: int = HEAD_DIM
+    idx_dim: int = HEAD_DIM
+    block_size: int = BLOCK_SIZE
+    with_grad: bool = False
+    offset_scale: float = 0.5
+
+    @property
+    def nblk(self) -> int:
+        return -(-self.seqlen // self.block_size)
+
+    @property
+    def group(self) -> int:
+        return self.h_q // self.h_kv
+
+    @property
+    def softmax_scale(self) -> float:
+        return self.head_dim ** -0.5
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    # 1024 tokens (8 blocks), 4 query heads on 1 KV head, top-4.
+    "tiny_n1k": Workload("tiny_n1k", batch=1, seqlen=1024, h_q=4, h_kv=1, h_idx=1, top_k=4, seed=0),
+    # 8192 tokens (64 blocks), 32 query heads on 8 KV heads, top-16.
+    "n8k": Workload("n8k", batch=1, seqlen=8192, h_q=32, h_kv=8, h_idx=8, top_k=16, seed=1),
+    # batch 2 x 32768 tokens (256 blocks), 64 query heads on 8 KV heads, top-16.
+    "n32k_b2": Workload("n32k_b2", batch=2, seqlen=32768, h_q=64, h_kv=8, h_idx=8, top_k=16, seed=2),
+    # 131072 tokens (1024 blocks), 64 query heads on 4 KV heads (the 109B model's
+    # attention shape), top-16.
+    "n128k": Workload("n128k", batch=1, seqlen=131072, h_q=64, h_kv=4, h_idx=4, top_k=16, seed=3),
+    # main-branch training step: 65536 tokens, 32 query heads on 8 KV heads, top-16.
+    "n64k_train": Workload("n64k_train", batch=1, seqlen=65536, h_q=32, h_kv=8, h_idx=8, top_k=16,
+                           seed=4, with_grad=True),
+}
+
+
+def make_inputs(w: Workload, generator_seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Draw the workload's inputs on the CPU as contiguous bfloat16 tensors.
+
+    Returns a dict with q, k, v, q_idx, k_idx (and d_o when ``w.with_grad``).
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed if generator_seed is None else generator_seed)
+    B, N = w.batch, w.seqlen
+    f32 = torch.float32
+    q = torch.randn((B, N, w.h_q, w.head_dim), generator=g, dtype=f32)
+    k = torch.randn((B, N, w.h_kv, w.head_dim), generator=g, dtype=f32)
+    v = torch.randn((B, N, w.h_kv, w.head_dim), generator=g, dtype=f32)
+    q_idx = torch.randn((B, N, w.h_idx, w.idx_dim), generator=g, dtype=f32)
+    k_idx = torch.randn((B, N, w.idx_dim), generator=g, dtype=f32)
+    u = torch.randn((B, w.nblk, w.idx_dim), generator=g, dtype=f32)
+    u = u / u.norm(dim=-1, keepdim=True)
+    block_of = torch.arange(N) // w.block_size
+    k_idx += w.offset_scale * u[:, block_of, :]
+    out = {
+        "q": q.to(torch.bfloat16),
+        "k": k.to(torch.bfloat16),
+        "v": v.to(torch.bfloat16),
+        "q_idx": q_idx.to(torch.bfloat16),
+        "k_idx": k_idx.to(torch.bfloat16),
+    }
+    del q, k, v, q_idx, k_idx
+    if w.with_grad:
+        out["d_o"] = torch.randn((B, N, w.h_q, w.head_dim), generator=g, dtype=f32).to(torch.bfloat16)
+    return out
+
+
+def small_workload(seqlen: int, h_q: int, h_kv: int, top_k: int, seed: int, batch: int = 1,
+                   h_idx: Optional[int] = None) -> Workload:
+    """A named-by-shape workload for parity tests at sizes the oracle finishes quickly."""
+    return Workload(f"b{batch}_n{seqlen}_hq{h_q}_hkv{h_kv}_k{top_k}_s{seed}", batch=batch, seqlen=seqlen,
+                    h_q=h_q, h_kv=h_kv, h_idx=h_kv if h_idx is None else h_idx, top_k=top_k, seed=seed)
