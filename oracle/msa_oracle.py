@@ -35,7 +35,10 @@ reason in the design notes at the repository root):
   R7  index head g serves query heads [g*G, (g+1)*G), G = H_q / H_kv, and
       uses KV head g ([Flash-MSA] "About MSA" item 3, "Note about scheduler":
       MSA groups equal GQA groups);
-  R8  LSE is the natural log of sum_j exp(scale * q.k_j) over attended keys.
+  R8  LSE is the natural log of sum_j exp(scale * q.k_j) over attended keys;
+  R9  a row whose selection holds no attendable key (only possible for a
+      caller-supplied selection) gets O = 0 and LSE = -inf, the limits of an
+      empty sum.
 """
 from __future__ import annotations
 
@@ -189,7 +192,7 @@ def sparse_attention(q, k, v, block_idx, softmax_scale: float, block_size: int =
 
     q: [B, N, H_q, D]; k, v: [B, N, H_kv, D]; block_idx: [B, H_kv, P, top_k]
     rows for the P requested positions. Returns O float64 [B, P, H_q, D] and
-    LSE float64 [B, H_q, P].
+    LSE float64 [B, H_q, P]. A row with no attended key gives O = 0, LSE = -inf (R9).
     """
     qq, kk, vv = _f64(q), _f64(k), _f64(v)
     bi = np.asarray(block_idx)
@@ -208,6 +211,10 @@ def sparse_attention(q, k, v, block_idx, softmax_scale: float, block_size: int =
             t = int(t)
             for g in range(Hkv):
                 keys = attended_keys(bi[b, g, i], t, block_size)
+                if keys.size == 0:  # R9: nothing to attend to
+                    O[b, i, g * G:(g + 1) * G] = 0.0
+                    LSE[b, g * G:(g + 1) * G, i] = -np.inf
+                    continue
                 qg = qq[b, t, g * G:(g + 1) * G]            # [G, D]
                 z = softmax_scale * (qg @ kk[b, keys, g].T)  # [G, n]
                 m = z.max(axis=-1, keepdims=True)

@@ -359,3 +359,19 @@ def test_near_tie_classification():
     assert (n, nt, bad) == (1, 0, [(0, 0, 0)])
     assert O.near_tie_rows(pooled, nolocal, ref, 4, positions=pos)[1] == 0
     assert O.near_tie_rows(pooled, ref, ref, 4, positions=pos) == (0, 0, [])
+
+
+def test_empty_selection_gives_zero_output_and_minus_inf_lse():
+    # R9: an empty sum of exp is 0, so LSE = log 0 = -inf; O is taken as 0.
+    rng = np.random.default_rng(13)
+    q, k, v = _rand_qkv(rng, 1, 256, 2, 1, 8)
+    sel = np.full((1, 1, 256, 2), -1, dtype=np.int32)
+    sel[0, 0, 200] = [1, -1]
+    sel[0, 0, 10] = [1, -1]   # block after the local block: nothing attendable
+    out, lse = O.sparse_attention(q, k, v, sel, 0.5)
+    empty = np.ones(256, dtype=bool)
+    empty[200] = False
+    assert np.all(out[0, empty] == 0.0) and np.all(lse[0, :, empty] == -np.inf)
+    keys = np.arange(128, 201)
+    z = 0.5 * q[0, 200] @ k[0, keys, 0].T
+    np.testing.assert_allclose(lse[0, :, 200], np.log(np.exp(z).sum(-1)), rtol=1e-12)
