@@ -1,0 +1,208 @@
+// libmsa C ABI: argument validation, workspace layout and launch order.
+#include <math.h>
+
+#include <atomic>
+
+#include "../../include/msa.h"
+#include "msa_internal.hpp"
+
+namespace msa {
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet; benign race (same value)
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int log2i(int x) {
+    int s = 0;
+    while ((1 << s) < x) ++s;
+    return s;
+}
+
+// Validates `s` and fills `d`. Host only; touches no device state.
+msa_status check_shape(const msa_shape* s, Dims* d) {
+    if (!s || !d) return MSA_ERR_INVALID_ARG;
+    if (s->batch < 1 || s->seqlen < 1 || s->h_q < 1 || s->h_kv < 1 || s->h_idx < 1 || s->top_k < 1)
+        return MSA_ERR_INVALID_ARG;
+    if (s->h_q % s->h_kv != 0) return MSA_ERR_INVALID_ARG;
+    if (!(s->softmax_scale > 0.0f) || !isfinite(s->softmax_scale)) return MSA_ERR_INVALID_ARG;
+    if (!(s->flags & MSA_CAUSAL)) return MSA_ERR_UNSUPPORTED;
+    if (s->head_dim != kDim || s->idx_dim != kDim || s->block_size != kBlock) return MSA_ERR_UNSUPPORTED;
+    if (s->h_idx != s->h_kv) return MSA_ERR_UNSUPPORTED;
+    const int G = s->h_q / s->h_kv;
+    if (!is_pow2(G) || G > kBlock) return MSA_ERR_UNSUPPORTED;
+    if (s->seqlen % kBlock != 0 || s->seqlen >= (1 << 23)) return MSA_ERR_UNSUPPORTED;
+    if (s->top_k > 256) return MSA_ERR_UNSUPPORTED;
+    // 32-bit index arithmetic bounds used inside the kernels
+    const double pairs = (double)s->batch * s->h_kv * s->seqlen * s->top_k;
+    if (pairs >= 2147483647.0) return MSA_ERR_UNSUPPORTED;
+    if ((double)s->seqlen * s->h_kv >= 2147483647.0) return MSA_ERR_UNSUPPORTED;
+    if ((double)s->batch * s->seqlen >= 2147483647.0) return MSA_ERR_UNSUPPORTED;
+    d->B = s->batch;
+    d->N = s->seqlen;
+    d->Hq = s->h_q;
+    d->Hkv = s->h_kv;
+    d->G = G;
+    d->gshift = log2i(G);
+    d->nblk = s->seqlen / kBlock;
+    d->top_k = s->top_k;
+    d->scale = s->softmax_scale;
+    return MSA_OK;
+}
+
+size_t pooled_bytes(const Dims& d) { return (size_t)d.B * d.Hkv * d.N * d.nblk * sizeof(float); }
+
+size_t ws_bytes(const Dims& d, msa_op op) {
+    switch (op) {
+        case MSA_OP_INDEX_SCORES: return 0;
+        case MSA_OP_BLOCK_TOPK: return 0;
+        case MSA_OP_SPARSE_ATTN_FWD: return sparse_ws_bytes(d);
+        case MSA_OP_FWD: return align_up(pooled_bytes(d), 256) + sparse_ws_bytes(d);
+    }
+    return 0;
+}
+
+msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
+
+}  // namespace
+
+int device_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    if (dev < kMaxDevices) {
+        const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+        if (cached > 0) return cached;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    if (dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+}  // namespace msa
+
+using namespace msa;
+
+extern "C" {
+
+msa_status msa_workspace_size(const msa_shape* shape, msa_op op, size_t* bytes) {
+    if (!bytes) return MSA_ERR_INVALID_ARG;
+    if (op < MSA_OP_INDEX_SCORES || op > MSA_OP_FWD) return MSA_ERR_INVALID_ARG;
+    Dims d;
+    const msa_status st = check_shape(shape, &d);
+    if (st != MSA_OK) return st;
+    *bytes = ws_bytes(d, op);
+    return MSA_OK;
+}
+
+msa_status msa_index_scores(const msa_shape* shape, const void* q_idx, const void* k_idx, float* pooled,
+                            hipStream_t stream) {
+    Dims d;
+    const msa_status st = check_shape(shape, &d);
+    if (st != MSA_OK) return st;
+    if (!q_idx || !k_idx || !pooled) return MSA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    const bool fill_upper = !(shape->flags & MSA_POOLED_VISIBLE_ONLY);
+    return hip_status(launch_index_pool(q_idx, k_idx, pooled, d, fill_upper, stream));
+}
+
+msa_status msa_block_topk(const msa_shape* shape, const float* pooled, int32_t* block_idx, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    Dims d;
+    const msa_status st = check_shape(shape, &d);
+    if (st != MSA_OK) return st;
+    if (!pooled || !block_idx) return MSA_ERR_INVALID_ARG;
+    if (!topk_supported(d.nblk, d.top_k)) return MSA_ERR_UNSUPPORTED;
+    (void)workspace;
+    (void)workspace_bytes;
+    (void)hipGetLastError();
+    return hip_status(launch_block_topk(pooled, block_idx, d, stream));
+}
+
+msa_status msa_sparse_attn_fwd(const msa_shape* shape, const void* q, const void* k, const void* v,
+                               const int32_t* block_idx, void* o, float* lse, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    Dims d;
+    const msa_status st = check_shape(shape, &d);
+    if (st != MSA_OK) return st;
+    if (!q || !k || !v || !block_idx || !o || !lse) return MSA_ERR_INVALID_ARG;
+    const size_t need = ws_bytes(d, MSA_OP_SPARSE_ATTN_FWD);
+    if (!workspace || workspace_bytes < need) return MSA_ERR_WORKSPACE;
+    (void)hipGetLastError();
+    const SparseWs ws = carve_sparse_ws(workspace, d);
+    hipError_t e = launch_sparse_plan(block_idx, ws, d, stream);
+    if (e == hipSuccess) e = launch_sparse_partial(q, k, v, ws, d, stream);
+    if (e == hipSuccess) e = launch_sparse_combine(block_idx, o, lse, ws, d, stream);
+    return hip_status(e);
+}
+
+msa_status msa_sparse_attn_plan(const msa_shape* shape, const int32_t* block_idx, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    Dims d;
+    const msa_status st = check_shape(shape, &d);
+    if (st != MSA_OK) return st;
+    if (!block_idx) return MSA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < ws_bytes(d, MSA_OP_SPARSE_ATTN_FWD)) return MSA_ERR_WORKSPACE;
+    (void)hipGetLastError();
+    return hip_status(launch_sparse_plan(block_idx, carve_sparse_ws(workspace, d), d, stream));
+}
+
+msa_status msa_sparse_attn_partial(const msa_shape* shape, const void* q, const void* k, const void* v,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    Dims d;
+    const msa_status st = check_shape(shape, &d);
+    if (st != MSA_OK) return st;
+    if (!q || !k || !v) return MSA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < ws_bytes(d, MSA_OP_SPARSE_ATTN_FWD)) return MSA_ERR_WORKSPACE;
+    (void)hipGetLastError();
+    return hip_status(launch_sparse_partial(q, k, v, carve_sparse_ws(workspace, d), d, stream));
+}
+
+msa_status msa_sparse_attn_combine(const msa_shape* shape, const int32_t* block_idx, void* o, float* lse,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    Dims d;
+    const msa_status st = check_shape(shape, &d);
+    if (st != MSA_OK) return st;
+    if (!block_idx || !o || !lse) return MSA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < ws_bytes(d, MSA_OP_SPARSE_ATTN_FWD)) return MSA_ERR_WORKSPACE;
+    (void)hipGetLastError();
+    return hip_status(launch_sparse_combine(block_idx, o, lse, carve_sparse_ws(workspace, d), d, stream));
+}
+
+msa_status msa_fwd(const msa_shape* shape, const void* q_idx, const void* k_idx, const void* q, const void* k,
+                   const void* v, int32_t* block_idx, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+    Dims d;
+    const msa_status st = check_shape(shape, &d);
+    if (st != MSA_OK) return st;
+    if (!q_idx || !k_idx || !q || !k || !v || !block_idx || !o || !lse) return MSA_ERR_INVALID_ARG;
+    if (!topk_supported(d.nblk, d.top_k)) return MSA_ERR_UNSUPPORTED;
+    const size_t need = ws_bytes(d, MSA_OP_FWD);
+    if (!workspace || workspace_bytes < need) return MSA_ERR_WORKSPACE;
+    (void)hipGetLastError();
+    float* pooled = (float*)workspace;
+    void* rest = (char*)workspace + align_up(pooled_bytes(d), 256);
+    hipError_t e = launch_index_pool(q_idx, k_idx, pooled, d, false, stream);
+    if (e != hipSuccess) return MSA_ERR_HIP;
+    e = launch_block_topk(pooled, block_idx, d, stream);
+    if (e != hipSuccess) return MSA_ERR_HIP;
+    const SparseWs ws = carve_sparse_ws(rest, d);
+    e = launch_sparse_plan(block_idx, ws, d, stream);
+    if (e == hipSuccess) e = launch_sparse_partial(q, k, v, ws, d, stream);
+    if (e == hipSuccess) e = launch_sparse_combine(block_idx, o, lse, ws, d, stream);
+    return hip_status(e);
+}
+
+const char* msa_status_string(msa_status status) {
+    switch (status) {
+        case MSA_OK: return "MSA_OK: success";
+        case MSA_ERR_INVALID_ARG: return "MSA_ERR_INVALID_ARG: null pointer or inconsistent/invalid size";
+        case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED: valid shape this build does not handle";
+        case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE: workspace missing or too small";
+        case MSA_ERR_HIP: return "MSA_ERR_HIP: a HIP launch failed";
+    }
+    return "unknown msa_status";
+}
+
+}  // extern "C"

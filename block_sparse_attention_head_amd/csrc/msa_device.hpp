@@ -1,0 +1,58 @@
+// Device-side helpers shared by the libmsa kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "msa_internal.hpp"
+
+namespace msa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_32x32x16_bf16. Operand layouts (checked on the device):
+//   A (32 x 16): lane l holds A[l % 32][8 * (l / 32) + e], e = 0..7
+//   B (16 x 32): lane l holds B[8 * (l / 32) + e][l % 32]
+//   D (32 x 32): lane l, register i holds D[8 * (i / 4) + 4 * (l / 32) + i % 4][l % 32]
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row of the 32x32 MFMA result held by lane-half `h` in register `i`.
+__device__ __forceinline__ int mfma32_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+
+// A 128 x 128 bf16 tile in LDS, row-major with 256-byte rows cut into sixteen
+// 16-byte chunks. Chunk `ch` of row `r` is stored at chunk slot ch ^ (r & 15),
+// so the 32 rows read by one MFMA operand load fall into distinct banks.
+__device__ __forceinline__ int swz_chunk_offset(int row, int ch) {
+    return row * kDim + ((ch ^ (row & 15)) << 3);  // in bf16 elements
+}
+
+// Total order on fp32 scores as unsigned integers (larger float -> larger key),
+// with -0.0 folded onto +0.0 so that equal scores compare equal.
+__device__ __forceinline__ uint32_t order_key(float x) {
+    uint32_t u = __float_as_uint(x);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// 64-bit selection key: score first, then the LOWER block index wins ties.
+__device__ __forceinline__ uint64_t select_key(float score, int block) {
+    return ((uint64_t)order_key(score) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)block);
+}
+__device__ __forceinline__ int key_block(uint64_t key) {
+    return (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
+}
+
+__device__ __forceinline__ float wave_max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
+    uint32_t lo = __shfl_xor((uint32_t)x, m, 64);
+    uint32_t hi = __shfl_xor((uint32_t)(x >> 32), m, 64);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+}  // namespace msa

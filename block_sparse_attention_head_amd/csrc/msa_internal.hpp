@@ -1,0 +1,52 @@
+// Host-side declarations of the kernel launchers behind the libmsa C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msa {
+
+constexpr int kBlock = 128;  // key block size (tokens)
+constexpr int kDim = 128;    // head dim of Q/K/V and of the index heads
+
+// Problem sizes after validation (all derived from msa_shape).
+struct Dims {
+    int B, N, Hq, Hkv, G, gshift, nblk, top_k;
+    float scale;
+};
+
+// Index scores + causal block max-pool. Writes pooled[b,g,t,c] for c <= t/128;
+// when `fill_upper` also writes -inf for c > t/128.
+hipError_t launch_index_pool(const void* q_idx, const void* k_idx, float* pooled, const Dims& d,
+                             bool fill_upper, hipStream_t stream);
+
+// Largest top_k this build's selection kernel accepts for `nblk` key blocks.
+bool topk_supported(int nblk, int top_k);
+hipError_t launch_block_topk(const float* pooled, int32_t* block_idx, const Dims& d, hipStream_t stream);
+
+// Workspace of the sparse attention forward, carved from one caller buffer.
+struct SparseWs {
+    int32_t* cnt;       // [B*Hkv*nblk]    queries per (b, g, c) tile
+    int32_t* off;       // [B*Hkv*nblk+1]  exclusive prefix of cnt
+    int32_t* item_off;  // [B*Hkv*nblk+1]  exclusive prefix of work items per tile
+    int32_t* cursor;    // [B*Hkv*nblk]    scatter cursors
+    int32_t* entries;   // [B*Hkv*N*top_k] (t << 8 | slot), grouped by tile
+    void* part_o;       // bf16 [B, N, top_k, Hq, 128] normalised partial outputs (lane order)
+    float* part_lse;    // fp32 [B, N, top_k, Hq]      partial log-sum-exp
+};
+size_t sparse_ws_bytes(const Dims& d);
+SparseWs carve_sparse_ws(void* base, const Dims& d);
+
+hipError_t launch_sparse_plan(const int32_t* block_idx, const SparseWs& ws, const Dims& d, hipStream_t stream);
+hipError_t launch_sparse_partial(const void* q, const void* k, const void* v, const SparseWs& ws, const Dims& d,
+                                 hipStream_t stream);
+hipError_t launch_sparse_combine(const int32_t* block_idx, void* o, float* lse, const SparseWs& ws, const Dims& d,
+                                 hipStream_t stream);
+
+// Compute-unit count of the current device (cached per device).
+int device_cu_count();
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace msa

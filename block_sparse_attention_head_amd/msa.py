@@ -1,0 +1,231 @@
+"""Python binding of libmsa (ctypes). Argument marshalling only.
+
+Every computation runs in the HIP kernels of libmsa.so; this module checks
+tensor shapes, allocates outputs and workspace with torch on the tensors'
+device, and passes raw device pointers and torch's current HIP stream across
+the C ABI declared in include/msa.h. If libmsa.so is missing or cannot be
+loaded, every call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
+
+MSA_OK = 0
+MSA_CAUSAL = 1
+MSA_POOLED_VISIBLE_ONLY = 2
+OP_INDEX_SCORES, OP_BLOCK_TOPK, OP_SPARSE_ATTN_FWD, OP_FWD = 0, 1, 2, 3
+
+BLOCK_SIZE = 128
+HEAD_DIM = 128
+
+
+class MsaShape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("seqlen", ctypes.c_int32),
+        ("h_q", ctypes.c_int32),
+        ("h_kv", ctypes.c_int32),
+        ("h_idx", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("idx_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+class MsaError(RuntimeError):
+    def __init__(self, func: str, status: int, message: str):
+        super().__init__(f"{func} failed: {message} (status {status})")
+        self.status = status
+
+
+_P = ctypes.c_void_p
+_S = ctypes.POINTER(MsaShape)
+_SIGNATURES = {
+    "msa_workspace_size": [_S, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)],
+    "msa_index_scores": [_S, _P, _P, _P, _P],
+    "msa_block_topk": [_S, _P, _P, _P, ctypes.c_size_t, _P],
+    "msa_sparse_attn_fwd": [_S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "msa_sparse_attn_plan": [_S, _P, _P, ctypes.c_size_t, _P],
+    "msa_sparse_attn_partial": [_S, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "msa_sparse_attn_combine": [_S, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "msa_fwd": [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+}
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmsa.so once. torch is imported first so the library binds to torch's HIP runtime."""
+    global _lib
+    if _lib is None:
+        with _lib_lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(f"{LIB_PATH} is not built: run `python -m block_sparse_attention_head_amd.build`")
+                handle = ctypes.CDLL(LIB_PATH)
+                for name, args in _SIGNATURES.items():
+                    fn = getattr(handle, name)
+                    fn.argtypes = args
+                    fn.restype = ctypes.c_int
+                handle.msa_status_string.argtypes = [ctypes.c_int]
+                handle.msa_status_string.restype = ctypes.c_char_p
+                _lib = handle
+    return _lib
+
+
+def _check(name: str, status: int) -> None:
+    if status != MSA_OK:
+        msg = lib().msa_status_string(status).decode()
+        raise MsaError(name, status, msg)
+
+
+def make_shape(batch: int, seqlen: int, h_q: int, h_kv: int, top_k: int, softmax_scale: float,
+               h_idx: Optional[int] = None, flags: int = MSA_CAUSAL) -> MsaShape:
+    return MsaShape(batch, seqlen, h_q, h_kv, h_kv if h_idx is None else h_idx, HEAD_DIM, HEAD_DIM, BLOCK_SIZE,
+                    top_k, float(softmax_scale), flags)
+
+
+def workspace_size(shape: MsaShape, op: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("msa_workspace_size", lib().msa_workspace_size(ctypes.byref(shape), op, ctypes.byref(n)))
+    return int(n.value)
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: Tuple[int, ...]) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def alloc_workspace(shape: MsaShape, op: int, device: torch.device) -> torch.Tensor:
+    return torch.empty(max(workspace_size(shape, op), 1), dtype=torch.uint8, device=device)
+
+
+def _ws(workspace: Optional[torch.Tensor], shape: MsaShape, op: int, device) -> torch.Tensor:
+    if workspace is None:
+        return alloc_workspace(shape, op, device)
+    if workspace.device != torch.device(device) or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    return workspace
+
+
+# ---------------------------------------------------------------------------
+# Entry points
+# ---------------------------------------------------------------------------
+def index_scores(q_idx: torch.Tensor, k_idx: torch.Tensor, pooled: Optional[torch.Tensor] = None,
+                 visible_only: bool = False) -> torch.Tensor:
+    """Pooled index scores fp32 [B, H_idx, N, N/128] (see msa_index_scores)."""
+    B, N, H, D = q_idx.shape
+    _need(q_idx, "q_idx", torch.bfloat16, (B, N, H, D))
+    _need(k_idx, "k_idx", torch.bfloat16, (B, N, D))
+    nblk = -(-N // BLOCK_SIZE)
+    if pooled is None:
+        pooled = torch.empty((B, H, N, nblk), dtype=torch.float32, device=q_idx.device)
+    _need(pooled, "pooled", torch.float32, (B, H, N, nblk))
+    flags = MSA_CAUSAL | (MSA_POOLED_VISIBLE_ONLY if visible_only else 0)
+    shape = make_shape(B, N, H, H, 1, 1.0, flags=flags)
+    _check("msa_index_scores", lib().msa_index_scores(ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(pooled),
+                                                      _stream(q_idx.device)))
+    return pooled
+
+
+def block_topk(pooled: torch.Tensor, top_k: int, block_idx: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Selected blocks int32 [B, H_idx, N, top_k] from pooled scores (see msa_block_topk)."""
+    B, H, N, nblk = pooled.shape
+    _need(pooled, "pooled", torch.float32, (B, H, N, nblk))
+    if block_idx is None:
+        block_idx = torch.empty((B, H, N, top_k), dtype=torch.int32, device=pooled.device)
+    _need(block_idx, "block_idx", torch.int32, (B, H, N, top_k))
+    shape = make_shape(B, N, H, H, top_k, 1.0)
+    _check("msa_block_topk", lib().msa_block_topk(ctypes.byref(shape), _ptr(pooled), _ptr(block_idx), _P(0), 0,
+                                                  _stream(pooled.device)))
+    return block_idx
+
+
+def _attn_shape(q, k, v, block_idx, softmax_scale) -> MsaShape:
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    top_k = block_idx.shape[-1]
+    _need(q, "q", torch.bfloat16, (B, N, Hq, D))
+    _need(k, "k", torch.bfloat16, (B, N, Hkv, D))
+    _need(v, "v", torch.bfloat16, (B, N, Hkv, D))
+    _need(block_idx, "block_idx", torch.int32, (B, Hkv, N, top_k))
+    return make_shape(B, N, Hq, Hkv, top_k, softmax_scale)
+
+
+def sparse_attn_fwd(q, k, v, block_idx, softmax_scale: float, o=None, lse=None, workspace=None):
+    """(O bf16 [B,N,H_q,128], LSE fp32 [B,H_q,N]) over the selected blocks (see msa_sparse_attn_fwd)."""
+    shape = _attn_shape(q, k, v, block_idx, softmax_scale)
+    B, N, Hq, D = q.shape
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, "o", torch.bfloat16, (B, N, Hq, D))
+    _need(lse, "lse", torch.float32, (B, Hq, N))
+    ws = _ws(workspace, shape, OP_SPARSE_ATTN_FWD, q.device)
+    _check("msa_sparse_attn_fwd",
+           lib().msa_sparse_attn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(o),
+                                     _ptr(lse), _ptr(ws), ws.numel(), _stream(q.device)))
+    return o, lse
+
+
+def sparse_attn_plan(shape: MsaShape, block_idx: torch.Tensor, workspace: torch.Tensor) -> None:
+    _check("msa_sparse_attn_plan", lib().msa_sparse_attn_plan(ctypes.byref(shape), _ptr(block_idx), _ptr(workspace),
+                                                              workspace.numel(), _stream(block_idx.device)))
+
+
+def sparse_attn_partial(shape: MsaShape, q, k, v, workspace: torch.Tensor) -> None:
+    _check("msa_sparse_attn_partial",
+           lib().msa_sparse_attn_partial(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(workspace),
+                                         workspace.numel(), _stream(q.device)))
+
+
+def sparse_attn_combine(shape: MsaShape, block_idx, o, lse, workspace: torch.Tensor) -> None:
+    _check("msa_sparse_attn_combine",
+           lib().msa_sparse_attn_combine(ctypes.byref(shape), _ptr(block_idx), _ptr(o), _ptr(lse), _ptr(workspace),
+                                         workspace.numel(), _stream(o.device)))
+
+
+def msa_fwd(q_idx, k_idx, q, k, v, top_k: int, softmax_scale: float, block_idx=None, o=None, lse=None,
+            workspace=None):
+    """The whole forward; returns (block_idx int32 [B,H_kv,N,top_k], O, LSE) (see msa_fwd)."""
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    _need(q_idx, "q_idx", torch.bfloat16, (B, N, Hkv, D))
+    _need(k_idx, "k_idx", torch.bfloat16, (B, N, D))
+    if block_idx is None:
+        block_idx = torch.empty((B, Hkv, N, top_k), dtype=torch.int32, device=q.device)
+    shape = _attn_shape(q, k, v, block_idx, softmax_scale)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, "o", torch.bfloat16, (B, N, Hq, D))
+    _need(lse, "lse", torch.float32, (B, Hq, N))
+    ws = _ws(workspace, shape, OP_FWD, q.device)
+    _check("msa_fwd", lib().msa_fwd(ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(block_idx), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(q.device)))
+    return block_idx, o, lse

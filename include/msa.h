@@ -1,0 +1,162 @@
+/*
+ * libmsa -- MiniMax Sparse Attention (MSA) forward on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI. Every entry point takes plain device pointers, sizes in a shape
+ * struct, a caller-owned workspace and a HIP stream. The library never
+ * allocates, frees or synchronises: all work is enqueued on `stream` and runs
+ * asynchronously. Arguments are validated on the host before anything is
+ * enqueued; on any error nothing is enqueued and no output is touched.
+ * No C++ exception crosses this boundary. The library keeps no mutable global
+ * state; calls from several host threads on different streams are safe.
+ *
+ * The method (cited from the web pages that describe it, by title and section):
+ *   [MSA summary] "MiniMax Sparse Attention (MSA): Turning Theoretical Sparse
+ *       Attention Gains into Real GPU Speedups", section "Architecture:
+ *       two-stage block-sparse attention": an index branch (one index query
+ *       head per GQA group, one shared index key head) scores the visible key
+ *       tokens, aggregates the scores into 128-token blocks and keeps the top-k
+ *       blocks (the query's own block always kept); the main branch runs exact
+ *       softmax attention over the selected blocks only.
+ *   [Flash-MSA] "Flash-MSA: Accelerating Million-Token Training with Sparse
+ *       Attention Kernels", sections "About MSA" (blocks chosen by max-pooling
+ *       the index scores), "Forward" (index branch, then sparse main
+ *       attention; block indices and the main LSE are kept) and "Proxy
+ *       attention" (causal max inside the local block; local block forced).
+ *   [flash-msa pkg] "flash-msa 0.1.0", sections "Usage" (the call takes index
+ *       queries, index keys, Q, K, V, top_k and the softmax scale) and
+ *       "Caveats" (head dim 128 and block size 128 only; no quantised inputs;
+ *       no attention temperature or softmax bias; index heads tied to KV
+ *       groups).
+ *
+ * Tensor layouts (all dense, row-major, contiguous; bf16 = bfloat16 passed as void*):
+ *   q_idx    bf16  [B, N, H_idx, 128]   index queries
+ *   k_idx    bf16  [B, N, 128]          shared index key head
+ *   q        bf16  [B, N, H_q, 128]
+ *   k, v     bf16  [B, N, H_kv, 128]
+ *   pooled   fp32  [B, H_idx, N, nblk]  nblk = N / 128
+ *   block_idx int32 [B, H_idx, N, top_k] selected blocks, ascending, -1 padded
+ *   o        bf16  [B, N, H_q, 128]
+ *   lse      fp32  [B, H_q, N]          natural log
+ * Query head h belongs to group g = h / G (G = H_q / H_kv); group g uses KV
+ * head g and index head g.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum msa_status {
+    MSA_OK = 0,
+    MSA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, inconsistent heads, size overflow */
+    MSA_ERR_UNSUPPORTED = 2, /* a valid shape this build does not handle (see msa_shape) */
+    MSA_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than msa_workspace_size() */
+    MSA_ERR_HIP = 4          /* a HIP launch failed; work before it may have been enqueued */
+} msa_status;
+
+/* flags */
+#define MSA_CAUSAL 1u               /* required: the method is causal */
+#define MSA_POOLED_VISIBLE_ONLY 2u  /* msa_index_scores: leave pooled[.., c > t/128] unwritten */
+
+typedef struct msa_shape {
+    int32_t batch;       /* B >= 1 */
+    int32_t seqlen;      /* N >= 1, a multiple of block_size, N < 2^23 */
+    int32_t h_q;         /* query heads, a multiple of h_kv */
+    int32_t h_kv;        /* KV heads; G = h_q / h_kv must be a power of two <= 128 */
+    int32_t h_idx;       /* index query heads; must equal h_kv */
+    int32_t head_dim;    /* must be 128 */
+    int32_t idx_dim;     /* must be 128 */
+    int32_t block_size;  /* must be 128 */
+    int32_t top_k;       /* 1 <= top_k <= 256; counts the forced local block */
+    float softmax_scale; /* > 0 and finite, usually head_dim^-0.5 */
+    uint32_t flags;      /* MSA_CAUSAL must be set */
+} msa_shape;
+
+typedef enum msa_op {
+    MSA_OP_INDEX_SCORES = 0,
+    MSA_OP_BLOCK_TOPK = 1,
+    MSA_OP_SPARSE_ATTN_FWD = 2,
+    MSA_OP_FWD = 3
+} msa_op;
+
+/* Bytes of device workspace `op` needs for `shape` (0 is a valid answer).
+ * The workspace is scratch owned by the caller, needs no initialisation, and
+ * must not be used by anything else while the call's work runs. */
+msa_status msa_workspace_size(const msa_shape* shape, msa_op op, size_t* bytes);
+
+/* Index scores with causal block max-pool ([MSA summary] "Architecture";
+ * [Flash-MSA] "About MSA" item 1 and "Proxy attention"):
+ *   pooled[b,g,t,c] = max_{j in block c, j <= t} sum_e q_idx[b,t,g,e] * k_idx[b,j,e]
+ * for c <= t/128, and -inf for c > t/128. Raw dot products (no scale),
+ * bf16 products accumulated in fp32. Writes every element of `pooled`, or only
+ * the visible part (c <= t/128) when shape->flags has MSA_POOLED_VISIBLE_ONLY. */
+msa_status msa_index_scores(const msa_shape* shape, const void* q_idx, const void* k_idx,
+                            float* pooled, hipStream_t stream);
+
+/* Top-k block selection with the local block forced ([MSA summary]
+ * "Architecture" and "GPU kernel co-design": selection on raw scores;
+ * [Flash-MSA] "Proxy attention": local block forced). For query t with
+ * c_loc = t/128: if c_loc + 1 <= top_k every visible block is selected;
+ * otherwise c_loc plus the top_k - 1 largest pooled[.., c] over c < c_loc,
+ * larger score first, lower block first among equal scores (-0.0 == +0.0).
+ * Only the visible part (c <= c_loc) of `pooled` is read. Output ascending,
+ * padded with -1. Deterministic; no workspace is needed today (pass NULL, 0). */
+msa_status msa_block_topk(const msa_shape* shape, const float* pooled, int32_t* block_idx,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Exact causal softmax attention of every query head over the blocks its
+ * group selected ([MSA summary] "Architecture" main branch; [Flash-MSA]
+ * "Main attention" and "Forward": O and the main LSE are produced):
+ *   z_j = softmax_scale * q[b,t,h] . k[b,j,g]  for j in a selected block, j <= t
+ *   o[b,t,h] = sum_j softmax(z)_j v[b,j,g];   lse[b,h,t] = log sum_j exp(z_j)
+ * block_idx entries outside [0, t/128] are ignored (treated as padding);
+ * entries must not repeat within a row (a repeated block counts twice). A row
+ * with no valid entry gives o = 0 and lse = -inf. Runs KV-outer: each
+ * (key block, KV head) tile gathers the queries that selected it ([MSA summary]
+ * "GPU kernel co-design"), writes per-slot partial results into the workspace,
+ * and a combine pass merges them. Deterministic (no floating-point atomics). */
+msa_status msa_sparse_attn_fwd(const msa_shape* shape, const void* q, const void* k, const void* v,
+                               const int32_t* block_idx, void* o, float* lse,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The three phases of msa_sparse_attn_fwd, for callers that schedule or time
+ * them separately. All three take the workspace sized for
+ * MSA_OP_SPARSE_ATTN_FWD and must be enqueued in this order on one stream with
+ * the same shape and workspace:
+ *   plan:    reverse sparse index ([Flash-MSA] "Backward": the map from
+ *            (query, slot) to key block is inverted into key block -> queries;
+ *            [MSA summary] "GPU kernel co-design": reverse sparse indexing)
+ *            and the tile work list, from block_idx;
+ *   partial: per (key block, KV head) tile, softmax attention of the gathered
+ *            queries over that block, written to per-slot partial outputs;
+ *   combine: merge of the partials into o and lse ([MSA summary] "GPU kernel
+ *            co-design": two-phase forward with a global softmax combine). */
+msa_status msa_sparse_attn_plan(const msa_shape* shape, const int32_t* block_idx, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+msa_status msa_sparse_attn_partial(const msa_shape* shape, const void* q, const void* k, const void* v,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+msa_status msa_sparse_attn_combine(const msa_shape* shape, const int32_t* block_idx, void* o, float* lse,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The whole forward: msa_index_scores (pooled kept in the workspace, only its
+ * visible part computed), msa_block_topk into `block_idx`, then
+ * msa_sparse_attn_fwd into `o` and `lse` ([Flash-MSA] "Forward": index branch
+ * first, then sparse main attention; block indices and LSE are kept). */
+msa_status msa_fwd(const msa_shape* shape, const void* q_idx, const void* k_idx, const void* q,
+                   const void* k, const void* v, int32_t* block_idx, void* o, float* lse,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static, never-NULL description of a status code. */
+const char* msa_status_string(msa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

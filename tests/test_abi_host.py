@@ -1,0 +1,126 @@
+"""Host-only checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments before touching the GPU. No compute call is
+made here, so these run without a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "block_sparse_attention_head_amd", "libmsa.so")
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmsa.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def m():
+    import torch  # noqa: F401  (bind to torch's HIP runtime, as the binding does)
+    from block_sparse_attention_head_amd import msa
+
+    return msa
+
+
+def test_every_declared_function_is_exported():
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    declared = _declared()
+    assert "msa_fwd" in declared and "msa_block_topk" in declared
+    assert not set(declared) - exported, sorted(set(declared) - exported)
+
+
+def test_library_loads_and_resolves_every_symbol(m):
+    lib = m.lib()
+    for name in _declared():
+        assert getattr(lib, name) is not None
+
+
+def _ws(m, op=None, **kw):
+    base = dict(batch=1, seqlen=1024, h_q=4, h_kv=1, top_k=4, softmax_scale=128 ** -0.5)
+    base.update(kw)
+    s = m.make_shape(**base)
+    n = ctypes.c_size_t(123)
+    st = m.lib().msa_workspace_size(ctypes.byref(s), m.OP_FWD if op is None else op, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_valid(m):
+    st, n = _ws(m)
+    assert st == 0
+    # pooled [1,1,1024,8] fp32 + reverse index + partials [1,1024,4,4,128] bf16 + lse
+    assert n >= 1024 * 8 * 4 + 1024 * 4 * 4 * 128 * 2 + 1024 * 4 * 4 * 4
+    st, n = _ws(m, op=m.OP_INDEX_SCORES)
+    assert (st, n) == (0, 0)
+    st, n = _ws(m, op=m.OP_BLOCK_TOPK)
+    assert (st, n) == (0, 0)
+    st1, n1 = _ws(m, op=m.OP_SPARSE_ATTN_FWD)
+    st2, n2 = _ws(m, op=m.OP_FWD)
+    assert st1 == st2 == 0 and n2 > n1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), 1),
+    (dict(seqlen=0), 1),
+    (dict(h_q=6, h_kv=4), 1),           # not a multiple
+    (dict(top_k=0), 1),
+    (dict(softmax_scale=0.0), 1),
+    (dict(softmax_scale=float("inf")), 1),
+    (dict(seqlen=1000), 2),             # not a multiple of 128
+    (dict(h_q=12, h_kv=4), 2),          # G = 3 is not a power of two
+    (dict(h_q=256, h_kv=1), 2),         # G > 128
+    (dict(top_k=257), 2),
+])
+def test_workspace_size_rejects(m, kw, code):
+    st, _ = _ws(m, **kw)
+    assert st == code, (kw, st)
+
+
+def test_unsupported_dims_and_flags(m):
+    s = m.make_shape(1, 1024, 4, 1, 4, 0.1)
+    n = ctypes.c_size_t()
+    for field, val in (("head_dim", 64), ("idx_dim", 256), ("block_size", 64), ("h_idx", 2), ("flags", 0)):
+        t = m.make_shape(1, 1024, 4, 1, 4, 0.1)
+        setattr(t, field, val)
+        assert m.lib().msa_workspace_size(ctypes.byref(t), m.OP_FWD, ctypes.byref(n)) == 2, field
+    assert m.lib().msa_workspace_size(ctypes.byref(s), 9, ctypes.byref(n)) == 1
+    assert m.lib().msa_workspace_size(None, m.OP_FWD, ctypes.byref(n)) == 1
+    assert m.lib().msa_workspace_size(ctypes.byref(s), m.OP_FWD, None) == 1
+
+
+def test_null_pointers_rejected_before_any_launch(m):
+    lib = m.lib()
+    s = m.make_shape(1, 1024, 4, 1, 4, 0.1)
+    P = ctypes.c_void_p
+    one = P(16)  # never dereferenced: validation fails on the null argument first
+    assert lib.msa_index_scores(ctypes.byref(s), P(0), one, one, P(0)) == 1
+    assert lib.msa_block_topk(ctypes.byref(s), one, P(0), P(0), 0, P(0)) == 1
+    assert lib.msa_sparse_attn_fwd(ctypes.byref(s), one, one, one, one, one, P(0), one, 1 << 40, P(0)) == 1
+    # workspace too small / missing
+    assert lib.msa_sparse_attn_fwd(ctypes.byref(s), one, one, one, one, one, one, P(0), 0, P(0)) == 3
+    assert lib.msa_fwd(ctypes.byref(s), one, one, one, one, one, one, one, one, one, 10, P(0)) == 3
+    assert lib.msa_sparse_attn_plan(ctypes.byref(s), one, one, 10, P(0)) == 3
+    assert lib.msa_sparse_attn_partial(ctypes.byref(s), one, one, one, one, 10, P(0)) == 3
+    assert lib.msa_sparse_attn_combine(ctypes.byref(s), one, one, one, one, 10, P(0)) == 3
+    assert lib.msa_fwd(None, one, one, one, one, one, one, one, one, one, 10, P(0)) == 1
+
+
+def test_status_strings(m):
+    for code in range(5):
+        assert m.lib().msa_status_string(code).startswith(b"MSA_")
+    assert m.lib().msa_status_string(77) == b"unknown msa_status"
+
+
+def test_binding_rejects_cpu_tensors(m):
+    import torch
+
+    q = torch.zeros(1, 128, 1, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 128, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        m.index_scores(q, k)

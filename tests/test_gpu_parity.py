@@ -1,0 +1,256 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every test prints the case it is about to run before touching the GPU.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import msa_oracle as O
+from synth.msa_inputs import WORKLOADS, make_inputs, small_workload
+from tests._parity import (check_attn, check_pooled, check_topk, pooled_bound, sample_positions, to_np)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _say(*a):
+    print("[gpu-case]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def msa():
+    from block_sparse_attention_head_amd import msa as m
+
+    m.lib()
+    return m
+
+
+def _gpu(x):
+    return {k: v.to(DEV) for k, v in x.items()}
+
+
+def _run_stages(msa, w, xg):
+    """Index scores, top-k, then sparse attention, each through its own entry point."""
+    pooled = msa.index_scores(xg["q_idx"], xg["k_idx"])
+    bi = msa.block_topk(pooled, w.top_k)
+    o, lse = msa.sparse_attn_fwd(xg["q"], xg["k"], xg["v"], bi, w.softmax_scale)
+    torch.cuda.synchronize()
+    return pooled, bi, o, lse
+
+
+def _full_parity(msa, w, x):
+    xg = _gpu(x)
+    _say(w.name, "stages")
+    pooled, bi, o, lse = _run_stages(msa, w, xg)
+    _say(w.name, "msa_fwd")
+    bi2, o2, lse2 = msa.msa_fwd(xg["q_idx"], xg["k_idx"], xg["q"], xg["k"], xg["v"], w.top_k, w.softmax_scale)
+    torch.cuda.synchronize()
+    # msa_fwd runs the same kernels: identical bits
+    assert torch.equal(bi, bi2) and torch.equal(o, o2) and torch.equal(lse, lse2)
+
+    ref_pooled = O.index_scores(x["q_idx"], x["k_idx"])
+    gp = to_np(pooled)
+    check_pooled(gp, ref_pooled, pooled_bound(x["q_idx"], x["k_idx"]), w.name, check_upper=True)
+    gi = to_np(bi)
+    n_mis, n_tie = check_topk(gi, gp, ref_pooled, w.top_k, tag=w.name)
+    _say(w.name, f"index rows differing from the oracle: {n_mis} (all near-ties: {n_tie})")
+    for label, sel in (("oracle-indices", O.block_topk(ref_pooled, w.top_k)), ("gpu-indices", gi)):
+        if label == "oracle-indices":
+            og, lg = msa.sparse_attn_fwd(xg["q"], xg["k"], xg["v"], torch.from_numpy(sel).to(DEV), w.softmax_scale)
+            torch.cuda.synchronize()
+        else:
+            og, lg = o, lse
+        ro, rl = O.sparse_attention(x["q"], x["k"], x["v"], sel, w.softmax_scale)
+        do, dl = check_attn(to_np(og), to_np(lg), ro, rl, f"{w.name}/{label}")
+        _say(w.name, label, f"max|dO|={do:.2e} max|dLSE|={dl:.2e}")
+
+
+def test_mfma_full_parity_tiny(msa):
+    w = WORKLOADS["tiny_n1k"]
+    _full_parity(msa, w, make_inputs(w))
+
+
+def test_full_parity_n8k(msa):
+    w = WORKLOADS["n8k"]
+    _full_parity(msa, w, make_inputs(w))
+
+
+SHAPES = [
+    # (seqlen, h_q, h_kv, top_k, batch): ragged index tiles (3 heads), G = 1, 2, 32, 128,
+    # top_k = 1, top_k > blocks (dense), one block, batch 2
+    (640, 6, 3, 3, 1),
+    (1024, 4, 4, 2, 1),
+    (2048, 32, 1, 5, 2),
+    (512, 8, 2, 16, 1),
+    (1024, 8, 2, 1, 1),
+    (128, 4, 1, 4, 1),
+    (768, 128, 1, 3, 1),
+    (3072, 16, 2, 7, 1),
+]
+
+
+@pytest.mark.parametrize("N,hq,hkv,k,b", SHAPES)
+def test_shapes_parity(msa, N, hq, hkv, k, b):
+    w = small_workload(N, hq, hkv, k, seed=100 + N + hq + k, batch=b)
+    _full_parity(msa, w, make_inputs(w))
+
+
+def test_dense_reduction_on_gpu(msa):
+    # top_k covering every block: the GPU path must equal dense causal GQA attention
+    w = small_workload(1024, 8, 2, 8, seed=21)
+    x = make_inputs(w)
+    xg = _gpu(x)
+    _say(w.name, "dense")
+    bi, o, lse = msa.msa_fwd(xg["q_idx"], xg["k_idx"], xg["q"], xg["k"], xg["v"], w.top_k, w.softmax_scale)
+    torch.cuda.synchronize()
+    q = x["q"].double().permute(0, 2, 1, 3)
+    kk = x["k"].double().permute(0, 2, 1, 3).repeat_interleave(4, dim=1)
+    vv = x["v"].double().permute(0, 2, 1, 3).repeat_interleave(4, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, kk, vv, is_causal=True, scale=w.softmax_scale)
+    s = (q @ kk.transpose(-1, -2)) * w.softmax_scale
+    s = s.masked_fill(~torch.ones(w.seqlen, w.seqlen, dtype=torch.bool).tril(), float("-inf"))
+    check_attn(to_np(o), to_np(lse), ref.permute(0, 2, 1, 3).numpy(), torch.logsumexp(s, -1).numpy(), "dense")
+
+
+@pytest.mark.parametrize("name", ["n32k_b2", "n128k"])
+def test_full_size_sampled_rows(msa, name):
+    w = WORKLOADS[name]
+    _say(name, "generating inputs")
+    x = make_inputs(w)
+    xg = _gpu(x)
+    _say(name, "msa_fwd + index scores")
+    bi, o, lse = msa.msa_fwd(xg["q_idx"], xg["k_idx"], xg["q"], xg["k"], xg["v"], w.top_k, w.softmax_scale)
+    pooled = msa.index_scores(xg["q_idx"], xg["k_idx"], visible_only=True)
+    torch.cuda.synchronize()
+    pos = sample_positions(w.seqlen, 40, seed=w.seed)
+    _say(name, f"oracle on {len(pos)} sampled positions")
+    gp = to_np(pooled[:, :, pos])
+    ref_pooled = O.index_scores(x["q_idx"], x["k_idx"], positions=pos)
+    vis = np.isfinite(ref_pooled)
+    gp = np.where(vis, gp, -np.inf)
+    check_pooled(gp, ref_pooled, pooled_bound(x["q_idx"], x["k_idx"], positions=pos), name)
+    gi = to_np(bi[:, :, pos])
+    n_mis, n_tie = check_topk(gi, gp, ref_pooled, w.top_k, positions=pos, tag=name)
+    _say(name, f"sampled index rows differing from the oracle: {n_mis} (near-ties: {n_tie})")
+    ro, rl = O.sparse_attention(x["q"], x["k"], x["v"], gi, w.softmax_scale, positions=pos)
+    do, dl = check_attn(to_np(o[:, pos]), to_np(lse[:, :, pos]), ro, rl, name)
+    _say(name, f"max|dO|={do:.2e} max|dLSE|={dl:.2e}")
+    # properties that hold at every position: local block present, count, order
+    bic = to_np(bi).astype(np.int64)
+    t = np.arange(w.seqlen)
+    cl = t // 128
+    valid = bic >= 0
+    assert np.all(valid.sum(-1) == np.minimum(w.top_k, cl + 1)[None, None])
+    assert np.all(np.take_along_axis(bic, (valid.sum(-1, keepdims=True) - 1), -1)[..., 0] == cl[None, None])
+    assert np.all(np.where(valid[..., 1:], np.diff(bic, axis=-1) > 0, True))
+    assert np.all(np.isfinite(to_np(lse)))
+
+
+def test_zero_index_queries_tie_to_lowest_blocks(msa):
+    w = small_workload(2048, 4, 1, 5, seed=3)
+    x = make_inputs(w)
+    xg = _gpu(x)
+    xg["q_idx"].zero_()
+    _say(w.name, "zero q_idx")
+    pooled = msa.index_scores(xg["q_idx"], xg["k_idx"])
+    bi = msa.block_topk(pooled, w.top_k)
+    torch.cuda.synchronize()
+    gi = to_np(bi)[0, 0]
+    for t in range(w.seqlen):
+        cl = t // 128
+        want = list(range(cl + 1)) if cl + 1 <= w.top_k else list(range(w.top_k - 1)) + [cl]
+        assert list(gi[t][: len(want)]) == want
+
+
+def test_duplicate_block_exact_tie_lower_index_wins(msa):
+    w = small_workload(2048, 4, 1, 4, seed=4)
+    x = make_inputs(w)
+    x["k_idx"][:, 5 * 128:6 * 128] = x["k_idx"][:, 2 * 128:3 * 128]
+    xg = _gpu(x)
+    _say(w.name, "duplicate key block")
+    pooled = msa.index_scores(xg["q_idx"], xg["k_idx"])
+    bi = msa.block_topk(pooled, w.top_k)
+    torch.cuda.synchronize()
+    gp, gi = to_np(pooled), to_np(bi)
+    rows = np.arange(6 * 128, w.seqlen)
+    assert np.array_equal(gp[0, 0, rows, 5], gp[0, 0, rows, 2])  # identical inputs, identical sums
+    np.testing.assert_array_equal(gi, O.block_topk(gp.astype(np.float64), w.top_k))
+    assert any(2 in gi[0, 0, t] and 5 not in gi[0, 0, t] for t in rows)
+
+
+def test_one_hot_value_probe(msa):
+    w = WORKLOADS["tiny_n1k"]
+    x = make_inputs(w)
+    N = w.seqlen
+    v = torch.zeros(1, N, 1, 128, dtype=torch.bfloat16)
+    v[0, torch.arange(N), 0, torch.arange(N) // 128] = 1.0
+    xg = _gpu(x)
+    _say(w.name, "one-hot V")
+    bi = msa.block_topk(msa.index_scores(xg["q_idx"], xg["k_idx"]), w.top_k)
+    o, _ = msa.sparse_attn_fwd(xg["q"], xg["k"], v.to(DEV), bi, w.softmax_scale)
+    torch.cuda.synchronize()
+    og, gi = to_np(o)[0], to_np(bi)[0, 0]
+    for t in range(N):
+        sel = set(int(c) for c in gi[t] if c >= 0)
+        off = [c for c in range(128) if c not in sel]
+        assert np.all(og[t][:, off] == 0.0), t
+        np.testing.assert_allclose(og[t][:, :w.nblk].sum(-1), 1.0, atol=2e-2)
+
+
+def test_invalid_and_empty_selections(msa):
+    # entries < 0 or > t//128 are padding; repeats count twice; rows with no valid entry give O = 0, LSE = -inf
+    w = small_workload(1024, 8, 2, 4, seed=5)
+    x = make_inputs(w)
+    rng = np.random.default_rng(0)
+    sel = rng.integers(-3, 10, size=(1, 2, w.seqlen, 4)).astype(np.int32)
+    sel[0, 0, 300] = -1
+    sel[0, 1, 900] = [7, 100, -1, -5]
+    xg = _gpu(x)
+    _say(w.name, "invalid entries")
+    o, lse = msa.sparse_attn_fwd(xg["q"], xg["k"], xg["v"], torch.from_numpy(sel).to(DEV), w.softmax_scale)
+    torch.cuda.synchronize()
+    og, lg = to_np(o), to_np(lse)
+    assert np.all(og[0, 300, 0:4] == 0.0) and np.all(lg[0, 0:4, 300] == -np.inf)
+    ro, rl = O.sparse_attention(x["q"], x["k"], x["v"], sel, w.softmax_scale)
+    assert (rl == -np.inf).sum() > 100  # the case is exercised
+    assert np.array_equal(og[rl.transpose(0, 2, 1) == -np.inf], np.zeros_like(og[rl.transpose(0, 2, 1) == -np.inf]))
+    check_attn(og, lg, ro, rl, "invalid-entries")
+
+
+def test_deterministic_and_stage_calls_match(msa):
+    w = WORKLOADS["n8k"]
+    x = make_inputs(w)
+    xg = _gpu(x)
+    _say(w.name, "determinism")
+    r1 = msa.msa_fwd(xg["q_idx"], xg["k_idx"], xg["q"], xg["k"], xg["v"], w.top_k, w.softmax_scale)
+    r2 = msa.msa_fwd(xg["q_idx"], xg["k_idx"], xg["q"], xg["k"], xg["v"], w.top_k, w.softmax_scale)
+    shape = msa.make_shape(1, w.seqlen, w.h_q, w.h_kv, w.top_k, w.softmax_scale)
+    ws = msa.alloc_workspace(shape, msa.OP_SPARSE_ATTN_FWD, torch.device(DEV))
+    o3 = torch.empty_like(xg["q"])
+    lse3 = torch.empty_like(r1[2])
+    msa.sparse_attn_plan(shape, r1[0], ws)
+    msa.sparse_attn_partial(shape, xg["q"], xg["k"], xg["v"], ws)
+    msa.sparse_attn_combine(shape, r1[0], o3, lse3, ws)
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+    assert torch.equal(o3, r1[1]) and torch.equal(lse3, r1[2])
+
+
+def test_binding_rejects_bad_shapes(msa):
+    q = torch.zeros(1, 256, 4, 128, dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros(1, 256, 1, 128, dtype=torch.bfloat16, device=DEV)
+    bi = torch.zeros(1, 1, 256, 4, dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError):
+        msa.sparse_attn_fwd(q, k, k, bi[:, :, :128], 0.1)
+    with pytest.raises(TypeError):
+        msa.sparse_attn_fwd(q.float(), k, k, bi, 0.1)
+    q2 = torch.zeros(1, 200, 4, 128, dtype=torch.bfloat16, device=DEV)
+    k2 = torch.zeros(1, 200, 1, 128, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(msa.MsaError) as e:
+        msa.sparse_attn_fwd(q2, k2, k2, torch.zeros(1, 1, 200, 4, dtype=torch.int32, device=DEV), 0.1)
+    assert e.value.status == 2
