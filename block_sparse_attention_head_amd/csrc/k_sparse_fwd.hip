@@ -242,9 +242,11 @@ __global__ __launch_bounds__(256, 2) void k_sparse_partial(
                 for (int i = 0; i < 16; ++i) m = fmaxf(m, sacc[mt][i]);
             m = wave_max_xor32(m);
 
-            // P = exp(scale * (s - m)) rounded to bf16; l sums the rounded values
+            // P = exp(scale * (s - m)) rounded to bf16 for the PV product. The LSE
+            // uses the fp32 sum l; O is normalised by lb, the sum of the rounded
+            // values, so the partial O is a convex combination of V rows.
             bf16x8 pf[8];
-            float l = 0.0f;
+            float l = 0.0f, lb = 0.0f;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -253,10 +255,12 @@ __global__ __launch_bounds__(256, 2) void k_sparse_partial(
                     for (int e = 0; e < 8; ++e) {
                         const float p = exp2f((sacc[mt][half * 8 + e] - m) * scale_log2);
                         const __bf16 pb = (__bf16)p;
-                        l += (float)pb;
+                        l += p;
+                        lb += (float)pb;
                         pf[mt * 2 + half][e] = pb;
                     }
             l += __shfl_xor(l, 32, 64);
+            lb += __shfl_xor(lb, 32, 64);
 
             f32x16 oacc[4];
 #pragma unroll
@@ -272,7 +276,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_partial(
                 }
 
             if (valid) {
-                const float inv = 1.0f / l;
+                const float inv = 1.0f / lb;
                 const size_t rec = (((size_t)b * N + t) * top_k + slot) * Hq + head;
                 __bf16* dst = part_o + rec * kDim + h * 64;
 #pragma unroll

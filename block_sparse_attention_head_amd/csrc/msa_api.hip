@@ -39,6 +39,7 @@ msa_status check_shape(const msa_shape* s, Dims* d) {
     if (pairs >= 2147483647.0) return MSA_ERR_UNSUPPORTED;
     if ((double)s->seqlen * s->h_kv >= 2147483647.0) return MSA_ERR_UNSUPPORTED;
     if ((double)s->batch * s->seqlen >= 2147483647.0) return MSA_ERR_UNSUPPORTED;
+    if ((double)s->batch * s->h_kv > 65535.0) return MSA_ERR_UNSUPPORTED;  // grid y / z extents
     d->B = s->batch;
     d->N = s->seqlen;
     d->Hq = s->h_q;
