@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the MSA forward hot path on one MI355X.
+
+One step = one full forward over one batch of the workload: index scores
+(causal block max-pool), top-k selection, reverse index + tile plan, KV-outer
+partial attention, softmax combine. Inputs are seeded synthetic bf16 tensors
+already resident in HBM when the timed region starts; each stage is bracketed
+by HIP events on the stream the library launches on.
+
+Prints ONE JSON line (rank 0): the contract fields, the roofline of the
+dominant kernel, per-stage figures and the CPU oracle baseline.
+
+    python bench.py [--steps K] [--warmup W] [--workload n128k] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MSA fwd tokens/sec and TFLOP/s at N=131072, k=16, B_k=128 (% of MFMA peak)"
+PROFILES = os.path.join(ROOT, "profiles")
+
+# kernel behind each single-kernel stage, the source it is built from, and its roofline bound
+STAGE_KERNEL = {
+    "index_pool": ("k_index_pool", "k_index_pool.hip", "mfma"),
+    "topk": ("k_block_topk", "k_block_topk.hip", "hbm"),
+    "partial": ("k_sparse_partial", "k_sparse_fwd.hip", "hbm"),
+    "combine": ("k_combine", "k_sparse_fwd.hip", "hbm"),
+}
+
+
+def _source_sha(fname: str) -> str:
+    p = os.path.join(ROOT, "block_sparse_attention_head_amd", "csrc", fname)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def _traffic(kernel: str, workload: str, src: str):
+    """HBM bytes per launch from the committed counter runs, or None when the kernel changed since."""
+    p = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("source_sha") != _source_sha(src):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, budget_s: float, seed: int = 7):
+    """The CPU oracle, as it stands, on a bounded uniform sample of query positions."""
+    import numpy as np
+
+    from oracle import msa_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    x64 = {k: v.double().numpy() for k, v in x.items() if k in ("q", "k", "v", "q_idx", "k_idx")}
+    order = np.random.default_rng(seed).permutation(w.seqlen)
+    done, t_total, chunk = 0, 0.0, 16
+    while done < w.seqlen and t_total < budget_s:
+        pos = np.sort(order[done:done + chunk])
+        t0 = time.perf_counter()
+        O.msa_forward(x64["q_idx"], x64["k_idx"], x64["q"], x64["k"], x64["v"], w.top_k, w.softmax_scale,
+                      positions=pos)
+        t_total += time.perf_counter() - t0
+        done += len(pos)
+    del x64
+    return {
+        "value": w.batch * done / t_total,
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{done} query positions drawn uniformly (seed {seed}) from the {w.name} workload "
+                   f"(batch {w.batch}, all {w.h_idx} index heads and {w.h_q} query heads), full forward per "
+                   f"position (index scores over all visible keys, top-k, sparse attention); "
+                   f"{t_total:.1f} s of float64 NumPy on the host; tokens/s = positions x batch / seconds"),
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="n128k")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run one plain 1 GiB device-to-device copy (counter calibration)")
+    a = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the MSA forward here is a single-GPU build "
+              "(how it would shard across GPUs is described in DESIGN.md); use --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from block_sparse_attention_head_amd import msa
+    from block_sparse_attention_head_amd import perfmodel as P
+    from synth.msa_inputs import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 3
+    w = WORKLOADS[a.workload]
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    x = make_inputs(w)
+    xg = {k: v.to(dev) for k, v in x.items()}
+    B, N, Hq, Hkv, K = w.batch, w.seqlen, w.h_q, w.h_kv, w.top_k
+    shape = msa.make_shape(B, N, Hq, Hkv, K, w.softmax_scale)
+    pooled = torch.empty((B, Hkv, N, w.nblk), dtype=torch.float32, device=dev)
+    block_idx = torch.empty((B, Hkv, N, K), dtype=torch.int32, device=dev)
+    o = torch.empty_like(xg["q"])
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    ws = msa.alloc_workspace(shape, msa.OP_SPARSE_ATTN_FWD, dev)
+    stages = ["index_pool", "topk", "plan", "partial", "combine"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        msa.index_scores(xg["q_idx"], xg["k_idx"], pooled, visible_only=True)
+        if ev is not None:
+            ev[1].record()
+        msa.block_topk(pooled, K, block_idx)
+        if ev is not None:
+            ev[2].record()
+        msa.sparse_attn_plan(shape, block_idx, ws)
+        if ev is not None:
+            ev[3].record()
+        msa.sparse_attn_partial(shape, xg["q"], xg["k"], xg["v"], ws)
+        if ev is not None:
+            ev[4].record()
+        msa.sparse_attn_combine(shape, block_idx, o, lse, ws)
+        if ev is not None:
+            ev[5].record()
+
+    print(f"[bench] warmup {a.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(a.steps):
+        step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / a.steps
+    stage_ms = {s: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / a.steps for j, s in enumerate(stages)}
+
+    if a.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    s = P.Shape(B, N, Hq, Hkv, K)
+    idx_f, main_f = P.index_flops(s), P.main_flops(s)
+    work = {
+        "index_pool": ("TFLOP/s", idx_f / 1e12, P.PEAK_BF16_TFLOPS),
+        "topk": ("GB/s", P.topk_bytes(s) / 1e9, P.PEAK_HBM_GBS),
+        "partial": ("GB/s", P.partial_bytes(s) / 1e9, P.PEAK_HBM_GBS),
+        "combine": ("GB/s", P.combine_bytes(s) / 1e9, P.PEAK_HBM_GBS),
+    }
+    stage_report = {}
+    for name in stages:
+        ms = stage_ms[name]
+        r = {"ms": round(ms, 4)}
+        if name in work:
+            unit, amount, peak = work[name]
+            ach = amount / (ms / 1e3)
+            r.update({"achieved": round(ach, 2), "unit": unit, "peak": peak, "frac": round(ach / peak, 4),
+                      "kernel": STAGE_KERNEL[name][0]})
+        stage_report[name] = r
+    stage_report["partial"]["tflops"] = round(main_f / 1e12 / (stage_ms["partial"] / 1e3), 2)
+    main_ms = stage_ms["plan"] + stage_ms["partial"] + stage_ms["combine"]
+
+    dom = max(work, key=lambda n: stage_ms[n])
+    kname, src, bound = STAGE_KERNEL[dom]
+    unit, amount, peak = work[dom]
+    ach = amount / (stage_ms[dom] / 1e3)
+    traffic = _traffic(kname, w.name, src)
+    roofline = {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
+                "traffic": traffic, "kernel": kname,
+                "per_launch": (f"{amount:.4g} {'TFLOP' if unit == 'TFLOP/s' else 'GB'} algorithmic per launch "
+                               f"/ {stage_ms[dom]:.3f} ms mean launch time (HIP events)")}
+
+    tokens_s = B * N / (ms_step / 1e3)
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "seqlen": N, "h_q": Hq, "h_kv": Hkv, "h_idx": w.h_idx,
+                   "head_dim": w.head_dim, "block_size": w.block_size, "top_k": K, "seed": w.seed},
+        "tflops": round((idx_f + main_f) / 1e12 / (ms_step / 1e3), 2),
+        "tflops_frac_of_bf16_peak": round((idx_f + main_f) / 1e12 / (ms_step / 1e3) / P.PEAK_BF16_TFLOPS, 4),
+        "main_attention_tflops": round(main_f / 1e12 / (main_ms / 1e3), 2),
+        "index_tflops": round(idx_f / 1e12 / (stage_ms["index_pool"] / 1e3), 2),
+        "stages": stage_report,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    del xg, pooled, block_idx, o, lse, ws
+    torch.cuda.empty_cache()
+    if not a.no_cpu_baseline:
+        print(f"[bench] CPU oracle baseline (~{a.cpu_budget:.0f} s)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, x, a.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

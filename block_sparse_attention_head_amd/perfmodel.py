@@ -1,0 +1,139 @@
+"""Algorithmic FLOP and byte counts of the MSA forward stages (closed forms).
+
+These are the counts the benchmark divides by measured time. They count the
+work the method needs, not what a particular kernel happens to do:
+
+  index scores     2 * d_idx FLOP per (query, visible key, index head)
+                   ([MSA summary] "Architecture": every visible key is scored)
+  main attention   4 * d FLOP per (query head, attended key): QK^T and PV
+  top-k            reads the non-local visible pooled scores of every row that
+                   has more visible blocks than top_k, writes top_k int32
+  partial (KV-outer) per (query row, selected block): read the query row (bf16),
+                   write a bf16 partial O row and one fp32 LSE; per tile read
+                   K and V of the block once; read the reverse-index entries
+  combine          read every partial O row and LSE, read the selection rows,
+                   write O (bf16) and LSE (fp32)
+
+Pins (tests): with 64 query heads, 4 index heads, d = d_idx = 128, k = 16,
+B_k = 128 and N = 2^20, full attention needs 28.44x the per-token FLOP of
+MSA ([MSA summary] "Summary" / "Experimental results": 28.4x); KV-outer
+intensity is (2/3) B_k = 85.3 FLOP/B against G for query-outer
+([MSA summary] "GPU kernel co-design": 85 vs 16 for B_k = 128, G = 16).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+BLOCK = 128
+HEAD_DIM = 128
+BF16 = 2
+FP32 = 4
+INT32 = 4
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def valid_blocks(t: int, top_k: int, block: int = BLOCK) -> int:
+    """Blocks a query at position t attends to: min(top_k, t // block + 1)."""
+    return min(top_k, t // block + 1)
+
+
+def sum_valid_blocks(N: int, top_k: int, block: int = BLOCK) -> int:
+    """sum_t min(top_k, t//block + 1) over t < N (N a multiple of block)."""
+    nb = N // block
+    return block * sum(min(top_k, c + 1) for c in range(nb)) + (N % block) * min(top_k, nb + 1)
+
+
+def sum_attended_keys(N: int, top_k: int, block: int = BLOCK) -> int:
+    """sum_t n_t, n_t = keys attended by query t: block * (blocks - 1) + (t % block) + 1."""
+    total = 0
+    for c in range(-(-N // block)):
+        rows = min(block, N - c * block)
+        nb = min(top_k, c + 1)
+        total += rows * block * (nb - 1) + rows * (rows + 1) // 2
+    return total
+
+
+@dataclass(frozen=True)
+class Shape:
+    batch: int
+    seqlen: int
+    h_q: int
+    h_kv: int
+    top_k: int
+    h_idx: int = 0
+    head_dim: int = HEAD_DIM
+    idx_dim: int = HEAD_DIM
+    block: int = BLOCK
+
+    @property
+    def hidx(self) -> int:
+        return self.h_idx or self.h_kv
+
+    @property
+    def nblk(self) -> int:
+        return -(-self.seqlen // self.block)
+
+    @property
+    def group(self) -> int:
+        return self.h_q // self.h_kv
+
+
+def index_flops(s: Shape) -> float:
+    return 2.0 * s.idx_dim * s.hidx * s.batch * s.seqlen * (s.seqlen + 1) / 2
+
+
+def main_flops(s: Shape) -> float:
+    return 4.0 * s.head_dim * s.h_q * s.batch * sum_attended_keys(s.seqlen, s.top_k, s.block)
+
+
+def index_bytes(s: Shape) -> float:
+    visible = s.batch * s.hidx * sum(min(s.block, s.seqlen - c * s.block) * (c + 1) for c in range(s.nblk))
+    return (s.batch * s.seqlen * s.hidx * s.idx_dim * BF16 + s.batch * s.seqlen * s.idx_dim * BF16
+            + visible * FP32)
+
+
+def topk_bytes(s: Shape) -> float:
+    read = 0
+    for c in range(s.nblk):
+        if c + 1 > s.top_k:
+            read += min(s.block, s.seqlen - c * s.block) * c
+    rows = s.batch * s.hidx * s.seqlen
+    return s.batch * s.hidx * read * FP32 + rows * s.top_k * INT32
+
+
+def pair_rows(s: Shape) -> int:
+    """(query head, selected block) pairs = query rows the KV-outer tiles process."""
+    return s.batch * s.h_kv * sum_valid_blocks(s.seqlen, s.top_k, s.block) * s.group
+
+
+def partial_bytes(s: Shape) -> float:
+    rows = pair_rows(s)
+    tiles = s.batch * s.h_kv * s.nblk
+    entries = s.batch * s.h_kv * sum_valid_blocks(s.seqlen, s.top_k, s.block)
+    return (rows * (s.head_dim * BF16 + s.head_dim * BF16 + FP32)
+            + tiles * 2 * s.block * s.head_dim * BF16 + entries * INT32)
+
+
+def combine_bytes(s: Shape) -> float:
+    rows = pair_rows(s)
+    return (rows * (s.head_dim * BF16 + FP32) + s.batch * s.h_kv * s.seqlen * s.top_k * INT32
+            + s.batch * s.seqlen * s.h_q * s.head_dim * BF16 + s.batch * s.h_q * s.seqlen * FP32)
+
+
+def per_token_compute_ratio(N: int, h_q: int, h_idx: int, d: int, d_idx: int, top_k: int, block: int) -> float:
+    """Full causal attention FLOP per token over MSA FLOP per token (index branch + main branch)."""
+    full = h_q * 4 * d * (N + 1) / 2
+    msa = h_idx * 2 * d_idx * (N + 1) / 2 + h_q * 4 * d * top_k * block
+    return full / msa
+
+
+def kv_outer_intensity(block: int, d: int, partial_o_bytes: int = FP32) -> float:
+    """FLOP per HBM byte of one (query row, key block) pair: gather the bf16 query row, write its partial O."""
+    return 4.0 * block * d / (BF16 * d + partial_o_bytes * d)
+
+
+def q_outer_intensity(group: int) -> float:
+    """Query-outer: a K/V block is loaded for the G heads of one query, so FLOP/byte equals G."""
+    return float(group)

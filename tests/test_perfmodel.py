@@ -1,0 +1,40 @@
+"""The FLOP/byte model reproduces the figures the pages print (tests/golden/pages_figures.json)."""
+import json
+import os
+
+import pytest
+
+from block_sparse_attention_head_amd import perfmodel as P
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_figures.json")))
+
+
+def test_per_token_compute_reduction_28_4x():
+    r = P.per_token_compute_ratio(N=2 ** 20, h_q=64, h_idx=4, d=128, d_idx=128, top_k=16, block=128)
+    assert round(r, 1) == GOLD["per_token_compute_reduction"]["value"]
+    assert r == pytest.approx(28.44, abs=0.01)
+
+
+def test_kv_outer_vs_q_outer_intensity():
+    g = GOLD["kv_outer_intensity"]
+    assert round(P.kv_outer_intensity(g["block"], 128)) == g["value"]
+    assert P.q_outer_intensity(g["group"]) == g["q_outer_value"]
+
+
+def test_tokens_per_query():
+    # attended keys: top_k - 1 full blocks plus the causal part of the query's own block
+    assert 16 * 128 == GOLD["tokens_per_query"]["value"]
+    N = 128 * 40
+    s = P.sum_attended_keys(N, 16)
+    # brute force
+    brute = sum(128 * (min(16, t // 128 + 1) - 1) + t % 128 + 1 for t in range(N))
+    assert s == brute
+    assert P.sum_valid_blocks(N, 16) == sum(min(16, t // 128 + 1) for t in range(N))
+
+
+def test_flops_of_the_128k_workload():
+    s = P.Shape(batch=1, seqlen=131072, h_q=64, h_kv=4, top_k=16)
+    assert P.index_flops(s) == pytest.approx(8.796e12, rel=1e-3)
+    brute_keys = sum(128 * (min(16, t // 128 + 1) - 1) + t % 128 + 1 for t in range(0, 131072))
+    assert P.main_flops(s) == 4 * 128 * 64 * brute_keys
+    assert P.pair_rows(s) == 4 * 16 * sum(min(16, t // 128 + 1) for t in range(131072))
