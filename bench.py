@@ -31,14 +31,19 @@ PROFILES = os.path.join(ROOT, "profiles")
 STAGE_KERNEL = {
     "index_pool": ("k_index_pool", "k_index_pool.hip", "mfma"),
     "topk": ("k_block_topk", "k_block_topk.hip", "hbm"),
-    "partial": ("k_sparse_partial", "k_sparse_fwd.hip", "hbm"),
-    "combine": ("k_combine", "k_sparse_fwd.hip", "hbm"),
+    "partial": ("k_sparse_partial", "k_sparse_partial.hip", "hbm"),
+    "combine": ("k_combine", "k_combine.hip", "hbm"),
 }
+SHARED_HEADERS = ("msa_device.hpp", "msa_internal.hpp")
 
 
-def _source_sha(fname: str) -> str:
-    p = os.path.join(ROOT, "block_sparse_attention_head_amd", "csrc", fname)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+def source_sha(fname: str) -> str:
+    """Hash of a kernel's source file and the headers every kernel includes."""
+    h = hashlib.sha256()
+    for f in (fname, *SHARED_HEADERS):
+        p = os.path.join(ROOT, "block_sparse_attention_head_amd", "csrc", f)
+        h.update(open(p, "rb").read() if os.path.exists(p) else b"<missing>")
+    return h.hexdigest()[:16]
 
 
 def _traffic(kernel: str, workload: str, src: str):
@@ -47,7 +52,7 @@ def _traffic(kernel: str, workload: str, src: str):
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
-    if rec.get("source_sha") != _source_sha(src):
+    if rec.get("source_sha") != source_sha(src):
         return None
     return rec.get("hbm_bytes_per_launch")
 

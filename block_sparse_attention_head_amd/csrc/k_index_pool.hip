@@ -9,17 +9,33 @@
 // The index queries of all heads form one [N*H_idx, 128] matrix (their memory
 // layout already is), because every head is scored against the same keys.
 // A workgroup owns 256 of those rows (held in registers as the MFMA B operand)
-// and streams kIdxChunk key blocks through LDS. Each wave computes
-// S^T = K_blk * Q^T for its 64 rows, so one lane holds one query row and the
-// block max is an in-lane max plus one exchange between the wave's halves.
-// The per-block maxima are staged in LDS and written as contiguous runs.
+// and streams kIdxChunk key blocks through a double-buffered LDS tile filled by
+// direct global->LDS loads. Each wave computes S^T = K_blk * Q^T for its 64
+// rows, so a lane holds one query row and the block max is an in-lane max plus
+// one exchange between the wave's halves. Each lane keeps its row's maxima for
+// the chunk in registers and writes them as one 128-byte run.
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 
 namespace msa {
 
 constexpr int kIdxTileRows = 256;  // (position, index head) rows per workgroup
-constexpr int kIdxChunk = 16;      // key blocks per workgroup
+constexpr int kIdxChunk = 32;      // key blocks per workgroup: one 128-byte pooled run per row
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Stage key block c into LDS buffer `dst` with direct global->LDS loads.
+// Instruction i of wave w fills 16-byte slots p = (4i + w) * 64 + lane, i.e.
+// row p / 16, stored chunk p % 16, which holds logical chunk (p % 16) ^ (row % 16).
+__device__ __forceinline__ void stage_key_block(const __bf16* __restrict__ src, __bf16* dst, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int p = (i * 4 + wave) * 64 + lane;
+        const int row = p >> 4, logical = (p & 15) ^ (row & 15);
+        __builtin_amdgcn_global_load_lds((const void*)(src + row * kDim + logical * 8),
+                                         (lds_ptr)(dst + (i * 4 + wave) * 64 * 8), 16, 0, 0);
+    }
+}
 
 __global__ __launch_bounds__(256, 2) void k_index_pool(const __bf16* __restrict__ q_idx,
                                                        const __bf16* __restrict__ k_idx,
@@ -33,12 +49,13 @@ __global__ __launch_bounds__(256, 2) void k_index_pool(const __bf16* __restrict_
     if (c0 >= nkb) return;
     const int c1 = min(c0 + kIdxChunk, nkb);
 
-    __shared__ __attribute__((aligned(16))) __bf16 ks[kBlock * kDim];
-    __shared__ float stage[kIdxChunk * kIdxTileRows];
+    __shared__ __attribute__((aligned(16))) __bf16 ks[2][kBlock * kDim];  // double-buffered key block
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
     const __bf16* qb = q_idx + (size_t)b * R * kDim;
     const __bf16* kb = k_idx + (size_t)b * N * kDim;
+
+    stage_key_block(kb + (size_t)c0 * kBlock * kDim, ks[0], wave, lane);
 
     // B operand (Q^T): lane holds row (wave*64 + nt*32 + l32), dims kk*16 + 8h .. +7.
     bf16x8 qf[2][8];
@@ -58,66 +75,72 @@ __global__ __launch_bounds__(256, 2) void k_index_pool(const __bf16* __restrict_
         }
     }
 
+    // pv[j] ends up holding this lane's row max for key block c1 - kIdxChunk + j
+    float pv[kIdxChunk];
+#pragma unroll
+    for (int j = 0; j < kIdxChunk; ++j) pv[j] = -INFINITY;
+
     for (int c = c0; c < c1; ++c) {
-        __syncthreads();  // every wave is done reading the previous key block
-        const __bf16* src = kb + (size_t)c * kBlock * kDim;
+        const int buf = (c - c0) & 1;
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of block c have landed
+        __syncthreads();                // ... and everyone's; the other buffer is free again
+        if (c + 1 < c1) stage_key_block(kb + (size_t)(c + 1) * kBlock * kDim, ks[buf ^ 1], wave, lane);
+        const __bf16* kt = ks[buf];
+        const bool diag0 = (trow[0] >> 7) == c, diag1 = (trow[1] >> 7) == c;
+        const bool any_diag = __any(diag0 || diag1);
+        const int lim0 = diag0 ? trow[0] - c * kBlock : kBlock - 1;
+        const int lim1 = diag1 ? trow[1] - c * kBlock : kBlock - 1;
+        float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int idx = tid + i * 256, key = idx >> 4, ch = idx & 15;
-            const uint4 val = *(const uint4*)(src + key * kDim + ch * 8);
-            *(uint4*)(ks + swz_chunk_offset(key, ch)) = val;
-        }
-        __syncthreads();
-
-        f32x16 acc[4][2];
+        for (int mt = 0; mt < 4; ++mt) {  // one 32-key M tile at a time keeps the accumulators small
+            f32x16 acc0, acc1;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+            for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.0f;
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.0f;
-
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const bf16x8 a = *(const bf16x8*)(ks + swz_chunk_offset(mt * 32 + l32, 2 * kk + h));
-                acc[mt][0] = mfma32(a, qf[0][kk], acc[mt][0]);
-                acc[mt][1] = mfma32(a, qf[1][kk], acc[mt][1]);
+            for (int kk = 0; kk < 8; ++kk) {
+                const bf16x8 a = *(const bf16x8*)(kt + swz_chunk_offset(mt * 32 + l32, 2 * kk + h));
+                acc0 = mfma32(a, qf[0][kk], acc0);
+                acc1 = mfma32(a, qf[1][kk], acc1);
             }
-        }
-
+            if (any_diag) {  // the query's own block: keep keys j <= t only
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int t = trow[nt];
-            const bool diag = (t >> 7) == c;  // the query's own block: keep keys j <= t only
-            float m = -INFINITY;
-            if (__any(diag)) {
-                const int lim = diag ? t - c * kBlock : kBlock - 1;
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        if (mt * 32 + mfma32_row(i, h) <= lim) m = fmaxf(m, acc[mt][nt][i]);
+                for (int i = 0; i < 16; ++i) {
+                    const int key = mt * 32 + mfma32_row(i, h);
+                    if (key <= lim0) m0 = fmaxf(m0, acc0[i]);
+                    if (key <= lim1) m1 = fmaxf(m1, acc1[i]);
+                }
             } else {
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[mt][nt][i]);
+                for (int i = 0; i < 16; ++i) {
+                    m0 = fmaxf(m0, acc0[i]);
+                    m1 = fmaxf(m1, acc1[i]);
+                }
             }
-            m = wave_max_xor32(m);
-            if (h == nt) stage[(c - c0) * kIdxTileRows + wave * 64 + nt * 32 + l32] = m;
         }
+        m0 = wave_max_xor32(m0);
+        m1 = wave_max_xor32(m1);
+        // after the exchange lane-half h owns row tile h
+#pragma unroll
+        for (int j = 0; j + 1 < kIdxChunk; ++j) pv[j] = pv[j + 1];
+        pv[kIdxChunk - 1] = h ? m1 : m0;
     }
-    __syncthreads();
 
-    const int row = r0 + tid;
+    const int row = r0 + wave * 64 + h * 32 + l32;
     if (row < R) {
         const int t = row / H, g = row - t * H;
-        const int cl = t >> 7;
+        const int cend = min(c1, (t >> 7) + 1);
         float* dst = pooled + (((size_t)b * H + g) * N + t) * nblk;
-        const int cend = min(c1, cl + 1);
-        for (int c = c0; c < cend; ++c) dst[c] = stage[(c - c0) * kIdxTileRows + tid];
+        if (c1 - c0 == kIdxChunk && cend == c1 && (nblk & 3) == 0) {
+#pragma unroll
+            for (int q4 = 0; q4 < kIdxChunk / 4; ++q4)
+                *(f32x4*)(dst + c0 + 4 * q4) = (f32x4){pv[4 * q4], pv[4 * q4 + 1], pv[4 * q4 + 2], pv[4 * q4 + 3]};
+        } else {
+#pragma unroll
+            for (int j = 0; j < kIdxChunk; ++j) {
+                const int c = c1 - kIdxChunk + j;
+                if (c >= c0 && c < cend) dst[c] = pv[j];
+            }
+        }
     }
 }
 

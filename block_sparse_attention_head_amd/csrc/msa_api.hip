@@ -52,6 +52,37 @@ msa_status check_shape(const msa_shape* s, Dims* d) {
     return MSA_OK;
 }
 
+}  // namespace
+
+size_t sparse_ws_bytes(const Dims& d) {
+    const size_t n = (size_t)d.B * d.Hkv * d.nblk;
+    size_t s = 0;
+    s += align_up(n * 4, 256);                                      // cnt
+    s += align_up((n + 1) * 4, 256);                                // off
+    s += align_up((n + 1) * 4, 256);                                // item_off
+    s += align_up(n * 4, 256);                                      // cursor
+    s += align_up((size_t)d.B * d.Hkv * d.N * d.top_k * 4, 256);    // entries
+    s += align_up((size_t)d.B * d.N * d.top_k * d.Hq * kDim * 2, 256);  // part_o
+    s += align_up((size_t)d.B * d.N * d.top_k * d.Hq * 4, 256);     // part_lse
+    return s;
+}
+
+SparseWs carve_sparse_ws(void* base, const Dims& d) {
+    const size_t n = (size_t)d.B * d.Hkv * d.nblk;
+    char* p = (char*)base;
+    SparseWs w;
+    w.cnt = (int32_t*)p;      p += align_up(n * 4, 256);
+    w.off = (int32_t*)p;      p += align_up((n + 1) * 4, 256);
+    w.item_off = (int32_t*)p; p += align_up((n + 1) * 4, 256);
+    w.cursor = (int32_t*)p;   p += align_up(n * 4, 256);
+    w.entries = (int32_t*)p;  p += align_up((size_t)d.B * d.Hkv * d.N * d.top_k * 4, 256);
+    w.part_o = (void*)p;      p += align_up((size_t)d.B * d.N * d.top_k * d.Hq * kDim * 2, 256);
+    w.part_lse = (float*)p;
+    return w;
+}
+
+namespace {
+
 size_t pooled_bytes(const Dims& d) { return (size_t)d.B * d.Hkv * d.N * d.nblk * sizeof(float); }
 
 size_t ws_bytes(const Dims& d, msa_op op) {

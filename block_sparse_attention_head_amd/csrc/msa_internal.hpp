@@ -9,6 +9,7 @@ namespace msa {
 
 constexpr int kBlock = 128;  // key block size (tokens)
 constexpr int kDim = 128;    // head dim of Q/K/V and of the index heads
+constexpr int kRowTilesPerItem = 16;  // 128-row query tiles per sparse-attention work item
 
 // Problem sizes after validation (all derived from msa_shape).
 struct Dims {
