@@ -10,61 +10,110 @@
 
 namespace msa {
 
-// Partial record layout: element q = hf*64 + dt*16 + i of a record holds
-// dim 32*dt + 8*(i/4) + 4*hf + i%4 (the order the MFMA result registers are in).
+// Partial O layout: [(b*N + t)*top_k + slot][chunk c][head][8], where chunk
+// c = hf*8 + dt*2 + i0/8 holds dims 32*dt + 8*(i/4) + 4*hf + i%4 for
+// i = i0 .. i0+7 (the order the MFMA result registers are in).
+//
+// One workgroup per (b, t). The slot weights w_s = exp(lse_s - M) / L of every
+// head are computed once into LDS. Then each thread takes (chunk, head) pairs,
+// head fastest, so every load instruction reads a contiguous run, accumulates
+// the valid slots in fp32, and puts the result in an LDS copy of the position's
+// output row; the row (H_q x 128 bf16, contiguous in O) is written at the end.
+
 __global__ __launch_bounds__(256) void k_combine(const __bf16* __restrict__ part_o, const float* __restrict__ part_lse,
                                                  const int32_t* __restrict__ block_idx, __bf16* __restrict__ o,
                                                  float* __restrict__ lse, int N, int Hq, int Hkv, int gshift,
                                                  int top_k) {
+    // dynamic LDS: orow [Hq][128] bf16 | wts [top_k][Hq] fp32 | inv_l [Hq] fp32
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    __bf16* orow = (__bf16*)smem;
+    float* wts = (float*)(smem + (size_t)Hq * kDim * 2);  // 0 for invalid slots
+    float* inv_l = wts + (size_t)top_k * Hq;
     const int bt = blockIdx.x;
     const int b = bt / N, t = bt - b * N;
     const int cl = t >> 7;
-    for (int j = threadIdx.x; j < Hq * 16; j += 256) {
-        const int head = j >> 4, ch = j & 15;
+    const size_t rec0 = (size_t)bt * top_k;  // first record of this position: (b*N + t) * top_k
+
+    // 1. per head: M, L and the slot weights (one thread per head)
+    for (int head = threadIdx.x; head < Hq; head += 256) {
         const int g = head >> gshift;
         const int32_t* bi = block_idx + (((size_t)b * Hkv + g) * N + t) * top_k;
-        const size_t rec0 = ((size_t)b * N + t) * top_k;
         float M = -INFINITY;
         for (int s = 0; s < top_k; ++s) {
             const int c = bi[s];
             if (c >= 0 && c <= cl) M = fmaxf(M, part_lse[(rec0 + s) * Hq + head]);
         }
+        float L = 0.0f;
+        for (int s = 0; s < top_k; ++s) {
+            const int c = bi[s];
+            float w = 0.0f;
+            if (c >= 0 && c <= cl) w = expf(part_lse[(rec0 + s) * Hq + head] - M);
+            L += w;
+            wts[s * Hq + head] = w;
+        }
+        inv_l[head] = L > 0.0f ? 1.0f / L : 0.0f;
+        lse[((size_t)b * Hq + head) * N + t] = M + logf(L);
+    }
+    __syncthreads();
+
+    // 2. weighted sum of the slot records; j -> (chunk = j / Hq, head = j % Hq)
+    const int nchunk = Hq * 16;
+    const size_t slot_stride = (size_t)16 * Hq * 8;
+    for (int j = threadIdx.x; j < nchunk; j += 256) {
+        const int ch = j / Hq, head = j - ch * Hq;
         float acc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-        float L = 0.0f;
-        if (M != -INFINITY) {
-            for (int s = 0; s < top_k; ++s) {
-                const int c = bi[s];
-                if (c < 0 || c > cl) continue;
-                const size_t rec = (rec0 + s) * Hq + head;
-                const float w = expf(part_lse[rec] - M);
-                L += w;
-                const bf16x8 x = *(const bf16x8*)(part_o + rec * kDim + ch * 8);
+        const __bf16* src = part_o + rec0 * slot_stride + (size_t)j * 8;
+        int s = 0;
+        for (; s + 4 <= top_k; s += 4) {  // four slots in flight per step
+            bf16x8 x[4];
+            float w[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                w[u] = wts[(s + u) * Hq + head];
+                if (w[u] != 0.0f) x[u] = *(const bf16x8*)(src + (s + u) * slot_stride);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (w[u] != 0.0f)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[e] += w[u] * (float)x[u][e];
+        }
+        for (; s < top_k; ++s) {
+            const float w = wts[s * Hq + head];
+            if (w != 0.0f) {
+                const bf16x8 x = *(const bf16x8*)(src + s * slot_stride);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[e] += w * (float)x[e];
             }
         }
-        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        const float inv = inv_l[head];
         const int hf = ch >> 3, dt = (ch & 7) >> 1, i0 = (ch & 1) * 8;
         const int dim_a = 32 * dt + 2 * i0 + 4 * hf;  // elements 0..3 -> dim_a.., 4..7 -> dim_a+8..
-        __bf16* orow = o + (((size_t)b * N + t) * Hq + head) * kDim;
         bf16x4 wa, wb;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             wa[e] = (__bf16)(acc[e] * inv);
             wb[e] = (__bf16)(acc[4 + e] * inv);
         }
-        *(bf16x4*)(orow + dim_a) = wa;
-        *(bf16x4*)(orow + dim_a + 8) = wb;
-        if (ch == 0) lse[((size_t)b * Hq + head) * N + t] = M + logf(L);
+        *(bf16x4*)(orow + head * kDim + dim_a) = wa;
+        *(bf16x4*)(orow + head * kDim + dim_a + 8) = wb;
     }
+    __syncthreads();
+
+    // 3. the position's output row is contiguous in O: write it in 16-byte pieces
+    uint4* dst = (uint4*)(o + (size_t)bt * Hq * kDim);
+    const uint4* srcl = (const uint4*)orow;
+    for (int j = threadIdx.x; j < Hq * 16; j += 256) dst[j] = srcl[j];
 }
+
+size_t combine_lds_bytes(const Dims& d) { return (size_t)d.Hq * kDim * 2 + ((size_t)d.top_k + 1) * d.Hq * 4; }
 
 hipError_t launch_sparse_combine(const int32_t* block_idx, void* o, float* lse, const SparseWs& ws, const Dims& d,
                                  hipStream_t stream) {
-    hipLaunchKernelGGL(k_combine, dim3(d.B * d.N), dim3(256), 0, stream, (const __bf16*)ws.part_o, ws.part_lse,
-                       block_idx, (__bf16*)o, lse, d.N, d.Hq, d.Hkv, d.gshift, d.top_k);
+    hipLaunchKernelGGL(k_combine, dim3(d.B * d.N), dim3(256), combine_lds_bytes(d), stream, (const __bf16*)ws.part_o,
+                       ws.part_lse, block_idx, (__bf16*)o, lse, d.N, d.Hq, d.Hkv, d.gshift, d.top_k);
     return hipGetLastError();
 }
 

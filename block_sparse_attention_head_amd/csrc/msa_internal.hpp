@@ -42,6 +42,8 @@ SparseWs carve_sparse_ws(void* base, const Dims& d);
 hipError_t launch_sparse_plan(const int32_t* block_idx, const SparseWs& ws, const Dims& d, hipStream_t stream);
 hipError_t launch_sparse_partial(const void* q, const void* k, const void* v, const SparseWs& ws, const Dims& d,
                                  hipStream_t stream);
+// Dynamic LDS bytes of the combine kernel (must stay within 64 KB).
+size_t combine_lds_bytes(const Dims& d);
 hipError_t launch_sparse_combine(const int32_t* block_idx, void* o, float* lse, const SparseWs& ws, const Dims& d,
                                  hipStream_t stream);
 
