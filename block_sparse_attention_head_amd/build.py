@@ -41,9 +41,16 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+# Per-source extra flags. The index max-pool never needs NaN quieting, so its
+# fmaxf chains compile to plain v_max_f32 instead of canonicalise + max.
+EXTRA_FLAGS = {
+    "k_index_pool.hip": ["-fno-honor-nans"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CXXFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CXXFLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass warns that it does not know the packed-fp32 feature; that is expected.
     noise = re.compile(r"'-packed-fp32-ops' is not a recognized feature|warnings? generated when compiling for host")

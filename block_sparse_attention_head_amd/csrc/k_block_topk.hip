@@ -122,11 +122,126 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
     if (lane == 0) dst[need] = cl;
 }
 
+// Rows of at most 64 * kTopkRegVals non-local blocks: each wave walks a strided
+// sequence of rows, keeps the current row's scores in registers (one load per
+// score) and issues the next row's loads before ranking the current one.
+constexpr int kTopkRegVals = 16;
+
+__device__ __forceinline__ void topk_load_row(const float* __restrict__ src, int cl, int lane,
+                                              float (&v)[kTopkRegVals]) {
+#pragma unroll
+    for (int i = 0; i < kTopkRegVals; ++i) {
+        const int c = lane + 64 * i;
+        v[i] = c < cl ? src[c] : 0.0f;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_block_topk_reg(const float* __restrict__ pooled,
+                                                        int32_t* __restrict__ block_idx, int N, int nblk, int top_k,
+                                                        long long rows) {
+    __shared__ uint64_t cand[kTopkWaves][64 * kTopkRegVals];
+    __shared__ int32_t chosen[kTopkWaves][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const long long stride = (long long)gridDim.x * kTopkWaves;
+    const int need = top_k - 1;
+    uint64_t* list = cand[wave];
+
+    long long row = (long long)blockIdx.x * kTopkWaves + wave;
+    float v[kTopkRegVals];
+    if (row < rows) {
+        const int cl = (int)(row % N) >> 7;
+        if (cl + 1 > top_k) topk_load_row(pooled + row * nblk, cl, lane, v);
+    }
+    for (; row < rows; row += stride) {
+        const int t = (int)(row % N);
+        const int cl = t >> 7;
+        int32_t* dst = block_idx + row * top_k;
+        const bool rank_row = cl + 1 > top_k;
+        float cur[kTopkRegVals];
+#pragma unroll
+        for (int i = 0; i < kTopkRegVals; ++i) cur[i] = v[i];
+        const long long nrow = row + stride;  // prefetch the next row's scores
+        if (nrow < rows) {
+            const int ncl = (int)(nrow % N) >> 7;
+            if (ncl + 1 > top_k) topk_load_row(pooled + nrow * nblk, ncl, lane, v);
+        }
+        if (!rank_row) {  // every visible block
+            for (int s = lane; s < top_k; s += 64) dst[s] = s <= cl ? s : -1;
+            continue;
+        }
+        if (need == 0) {
+            if (lane == 0) dst[0] = cl;
+            continue;
+        }
+        uint64_t key[kTopkRegVals];
+        uint64_t lmax = 0;
+#pragma unroll
+        for (int i = 0; i < kTopkRegVals; ++i) {
+            const int c = lane + 64 * i;
+            key[i] = c < cl ? select_key(cur[i], c) : 0ull;
+            lmax = key[i] > lmax ? key[i] : lmax;
+        }
+        uint64_t x = lmax;
+#pragma unroll
+        for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                const uint64_t y = shfl_xor_u64(x, j);
+                const bool keep_big = ((lane & j) == 0) == ((lane & k) == 0);
+                const uint64_t big = x > y ? x : y, small = x > y ? y : x;
+                x = keep_big ? big : small;
+            }
+        }
+        const uint32_t thi = __shfl((uint32_t)(x >> 32), need - 1, 64);
+        const uint32_t tlo = __shfl((uint32_t)x, need - 1, 64);
+        const uint64_t T = ((uint64_t)thi << 32) | tlo;
+        int n = 0;
+#pragma unroll
+        for (int i = 0; i < kTopkRegVals; ++i) {
+            const bool take = key[i] != 0ull && key[i] >= T;
+            const uint64_t mask = __ballot(take);
+            if (take) list[n + __popcll(mask & ((1ull << lane) - 1ull))] = key[i];
+            n += __popcll(mask);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int i = lane; i < n; i += 64) {
+            const uint64_t mine = list[i];
+            int r = 0;
+            for (int j = 0; j < n; ++j) r += list[j] > mine ? 1 : 0;
+            if (r < need) chosen[wave][r] = key_block(mine);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane < need) {
+            const int mine = chosen[wave][lane];
+            int pos = 0;
+            for (int j = 0; j < need; ++j) pos += chosen[wave][j] < mine ? 1 : 0;
+            dst[pos] = mine;
+        }
+        if (lane == 0) dst[need] = cl;
+        // the next row reuses this wave's LDS lists
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
 hipError_t launch_block_topk(const float* pooled, int32_t* block_idx, const Dims& d, hipStream_t stream) {
     const long long rows = (long long)d.B * d.Hkv * d.N;
-    const long long blocks = (rows + kTopkWaves - 1) / kTopkWaves;
-    hipLaunchKernelGGL(k_block_topk, dim3((unsigned)blocks), dim3(256), 0, stream, pooled, block_idx, d.N, d.nblk,
-                       d.top_k, rows);
+    if (d.nblk - 1 <= 64 * kTopkRegVals && d.top_k <= 65) {
+        const long long want = (rows + kTopkWaves - 1) / kTopkWaves;
+        const long long cap = 8LL * device_cu_count();
+        const unsigned blocks = (unsigned)(want < cap ? want : cap);
+        hipLaunchKernelGGL(k_block_topk_reg, dim3(blocks), dim3(256), 0, stream, pooled, block_idx, d.N, d.nblk,
+                           d.top_k, rows);
+    } else {
+        const long long blocks = (rows + kTopkWaves - 1) / kTopkWaves;
+        hipLaunchKernelGGL(k_block_topk, dim3((unsigned)blocks), dim3(256), 0, stream, pooled, block_idx, d.N,
+                           d.nblk, d.top_k, rows);
+    }
     return hipGetLastError();
 }
 

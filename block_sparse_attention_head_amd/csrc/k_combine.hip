@@ -14,40 +14,53 @@ namespace msa {
 // c = hf*8 + dt*2 + i0/8 holds dims 32*dt + 8*(i/4) + 4*hf + i%4 for
 // i = i0 .. i0+7 (the order the MFMA result registers are in).
 //
-// One workgroup per (b, t). The slot weights w_s = exp(lse_s - M) / L of every
-// head are computed once into LDS. Then each thread takes (chunk, head) pairs,
-// head fastest, so every load instruction reads a contiguous run, accumulates
-// the valid slots in fp32, and puts the result in an LDS copy of the position's
-// output row; the row (H_q x 128 bf16, contiguous in O) is written at the end.
+// One workgroup per (b, t):
+//   0. the position's selection rows (H_kv x top_k) and slot LSEs (top_k x H_q,
+//      contiguous) are loaded cooperatively into LDS;
+//   1. one thread per head turns them into weights w_s / L and writes LSE;
+//   2. each thread takes (chunk, head) pairs, head fastest, so every load
+//      instruction reads a contiguous run; all slots of a pair are loaded
+//      before any is used (top_k <= 16), accumulated in fp32 and put in an LDS
+//      copy of the position's output row;
+//   3. the row (H_q x 128 bf16, contiguous in O) is written in 16-byte pieces.
+constexpr int kCombineFastSlots = 16;
 
 __global__ __launch_bounds__(256) void k_combine(const __bf16* __restrict__ part_o, const float* __restrict__ part_lse,
                                                  const int32_t* __restrict__ block_idx, __bf16* __restrict__ o,
                                                  float* __restrict__ lse, int N, int Hq, int Hkv, int gshift,
                                                  int top_k) {
-    // dynamic LDS: orow [Hq][128] bf16 | wts [top_k][Hq] fp32 | inv_l [Hq] fp32
+    // dynamic LDS: orow [Hq][128] bf16 | wts [top_k][Hq] fp32 | inv_l [Hq] fp32 | sel [Hkv][top_k] int32
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __bf16* orow = (__bf16*)smem;
-    float* wts = (float*)(smem + (size_t)Hq * kDim * 2);  // 0 for invalid slots
+    float* wts = (float*)(smem + (size_t)Hq * kDim * 2);
     float* inv_l = wts + (size_t)top_k * Hq;
+    int32_t* sel = (int32_t*)(inv_l + Hq);
+    const int tid = threadIdx.x;
     const int bt = blockIdx.x;
     const int b = bt / N, t = bt - b * N;
     const int cl = t >> 7;
     const size_t rec0 = (size_t)bt * top_k;  // first record of this position: (b*N + t) * top_k
 
-    // 1. per head: M, L and the slot weights (one thread per head)
-    for (int head = threadIdx.x; head < Hq; head += 256) {
-        const int g = head >> gshift;
-        const int32_t* bi = block_idx + (((size_t)b * Hkv + g) * N + t) * top_k;
+    // 0. selection rows and slot LSEs into LDS
+    for (int i = tid; i < Hkv * top_k; i += 256) {
+        const int g = i / top_k, s = i - g * top_k;
+        sel[i] = block_idx[(((size_t)b * Hkv + g) * N + t) * top_k + s];
+    }
+    for (int i = tid; i < top_k * Hq; i += 256) wts[i] = part_lse[rec0 * Hq + i];
+    __syncthreads();
+
+    // 1. per head: M = max lse_s, w_s = exp(lse_s - M), L = sum w_s over valid slots
+    for (int head = tid; head < Hq; head += 256) {
+        const int32_t* sg = sel + (head >> gshift) * top_k;
         float M = -INFINITY;
         for (int s = 0; s < top_k; ++s) {
-            const int c = bi[s];
-            if (c >= 0 && c <= cl) M = fmaxf(M, part_lse[(rec0 + s) * Hq + head]);
+            const int c = sg[s];
+            if (c >= 0 && c <= cl) M = fmaxf(M, wts[s * Hq + head]);
         }
         float L = 0.0f;
         for (int s = 0; s < top_k; ++s) {
-            const int c = bi[s];
-            float w = 0.0f;
-            if (c >= 0 && c <= cl) w = expf(part_lse[(rec0 + s) * Hq + head] - M);
+            const int c = sg[s];
+            const float w = (c >= 0 && c <= cl) ? expf(wts[s * Hq + head] - M) : 0.0f;
             L += w;
             wts[s * Hq + head] = w;
         }
@@ -57,35 +70,34 @@ __global__ __launch_bounds__(256) void k_combine(const __bf16* __restrict__ part
     __syncthreads();
 
     // 2. weighted sum of the slot records; j -> (chunk = j / Hq, head = j % Hq)
-    const int nchunk = Hq * 16;
     const size_t slot_stride = (size_t)16 * Hq * 8;
-    for (int j = threadIdx.x; j < nchunk; j += 256) {
+    for (int j = tid; j < Hq * 16; j += 256) {
         const int ch = j / Hq, head = j - ch * Hq;
+        const __bf16* src = part_o + rec0 * slot_stride + (size_t)j * 8;
         float acc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-        const __bf16* src = part_o + rec0 * slot_stride + (size_t)j * 8;
-        int s = 0;
-        for (; s + 4 <= top_k; s += 4) {  // four slots in flight per step
-            bf16x8 x[4];
-            float w[4];
+        if (top_k <= kCombineFastSlots) {
+            bf16x8 x[kCombineFastSlots];
+            float w[kCombineFastSlots];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                w[u] = wts[(s + u) * Hq + head];
-                if (w[u] != 0.0f) x[u] = *(const bf16x8*)(src + (s + u) * slot_stride);
+            for (int s = 0; s < kCombineFastSlots; ++s) {
+                w[s] = s < top_k ? wts[s * Hq + head] : 0.0f;
+                if (w[s] != 0.0f) x[s] = *(const bf16x8*)(src + s * slot_stride);
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (w[u] != 0.0f)
+            for (int s = 0; s < kCombineFastSlots; ++s)
+                if (w[s] != 0.0f)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[e] += w[u] * (float)x[u][e];
-        }
-        for (; s < top_k; ++s) {
-            const float w = wts[s * Hq + head];
-            if (w != 0.0f) {
-                const bf16x8 x = *(const bf16x8*)(src + s * slot_stride);
+                    for (int e = 0; e < 8; ++e) acc[e] += w[s] * (float)x[s][e];
+        } else {
+            for (int s = 0; s < top_k; ++s) {
+                const float w = wts[s * Hq + head];
+                if (w != 0.0f) {
+                    const bf16x8 x = *(const bf16x8*)(src + s * slot_stride);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] += w * (float)x[e];
+                    for (int e = 0; e < 8; ++e) acc[e] += w * (float)x[e];
+                }
             }
         }
         const float inv = inv_l[head];
@@ -105,10 +117,12 @@ __global__ __launch_bounds__(256) void k_combine(const __bf16* __restrict__ part
     // 3. the position's output row is contiguous in O: write it in 16-byte pieces
     uint4* dst = (uint4*)(o + (size_t)bt * Hq * kDim);
     const uint4* srcl = (const uint4*)orow;
-    for (int j = threadIdx.x; j < Hq * 16; j += 256) dst[j] = srcl[j];
+    for (int j = tid; j < Hq * 16; j += 256) dst[j] = srcl[j];
 }
 
-size_t combine_lds_bytes(const Dims& d) { return (size_t)d.Hq * kDim * 2 + ((size_t)d.top_k + 1) * d.Hq * 4; }
+size_t combine_lds_bytes(const Dims& d) {
+    return (size_t)d.Hq * kDim * 2 + ((size_t)d.top_k + 1) * d.Hq * 4 + (size_t)d.Hkv * d.top_k * 4;
+}
 
 hipError_t launch_sparse_combine(const int32_t* block_idx, void* o, float* lse, const SparseWs& ws, const Dims& d,
                                  hipStream_t stream) {
