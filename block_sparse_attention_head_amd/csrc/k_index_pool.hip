@@ -88,8 +88,10 @@ __global__ __launch_bounds__(256, 2) void k_index_pool(const __bf16* __restrict_
         const __bf16* kt = ks[buf];
         const bool diag0 = (trow[0] >> 7) == c, diag1 = (trow[1] >> 7) == c;
         const bool any_diag = __any(diag0 || diag1);
-        const int lim0 = diag0 ? trow[0] - c * kBlock : kBlock - 1;
-        const int lim1 = diag1 ? trow[1] - c * kBlock : kBlock - 1;
+        // key = mt*32 + 8*(i/4) + 4h + i%4 <= lim  <=>  mt*32 + 8*(i/4) + i%4 <= lim - 4h,
+        // so every comparison is against a compile-time constant
+        const int lim0 = (diag0 ? trow[0] - c * kBlock : kBlock - 1) - 4 * h;
+        const int lim1 = (diag1 ? trow[1] - c * kBlock : kBlock - 1) - 4 * h;
         float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {  // one 32-key M tile at a time keeps the accumulators small
@@ -105,9 +107,9 @@ __global__ __launch_bounds__(256, 2) void k_index_pool(const __bf16* __restrict_
             if (any_diag) {  // the query's own block: keep keys j <= t only
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int key = mt * 32 + mfma32_row(i, h);
-                    if (key <= lim0) m0 = fmaxf(m0, acc0[i]);
-                    if (key <= lim1) m1 = fmaxf(m1, acc1[i]);
+                    const int key_h0 = mt * 32 + mfma32_row(i, 0);
+                    if (key_h0 <= lim0) m0 = fmaxf(m0, acc0[i]);
+                    if (key_h0 <= lim1) m1 = fmaxf(m1, acc1[i]);
                 }
             } else {
 #pragma unroll

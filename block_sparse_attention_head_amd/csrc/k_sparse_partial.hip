@@ -140,12 +140,13 @@ __global__ __launch_bounds__(256, 2) void k_sparse_partial(
             // causal mask inside the query's own block
             const bool diag = (cur.t >> 7) == c;
             if (__any(diag)) {
-                const int lim = diag ? cur.t - c * kBlock : kBlock - 1;
+                // key = mt*32 + mfma32_row(i, h) > lim  <=>  mt*32 + mfma32_row(i, 0) > lim - 4h
+                const int lim = (diag ? cur.t - c * kBlock : kBlock - 1) - 4 * h;
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                     for (int i = 0; i < 16; ++i)
-                        if (mt * 32 + mfma32_row(i, h) > lim) sacc[mt][i] = -INFINITY;
+                        if (mt * 32 + mfma32_row(i, 0) > lim) sacc[mt][i] = -INFINITY;
             }
 
             float m = -INFINITY;

@@ -3,7 +3,7 @@
 
 #include <atomic>
 
-#include "../../include/msa.h"
+#include "msa.h"
 #include "msa_internal.hpp"
 
 namespace msa {
