@@ -19,13 +19,14 @@ namespace msa {
 //      contiguous) are loaded cooperatively into LDS;
 //   1. one thread per head turns them into weights w_s / L and writes LSE;
 //   2. each thread takes (chunk, head) pairs, head fastest, so every load
-//      instruction reads a contiguous run; all slots of a pair are loaded
+//      instruction reads a contiguous run; slots are loaded eight at a time
 //      before any is used (top_k <= 16), accumulated in fp32 and put in an LDS
-//      copy of the position's output row;
+//      copy of the position's output row (8 slots in flight at a time keeps
+//      the kernel small enough for 6 waves per SIMD);
 //   3. the row (H_q x 128 bf16, contiguous in O) is written in 16-byte pieces.
 constexpr int kCombineFastSlots = 16;
 
-__global__ __launch_bounds__(256) void k_combine(const __bf16* __restrict__ part_o, const float* __restrict__ part_lse,
+__global__ __launch_bounds__(256, 6) void k_combine(const __bf16* __restrict__ part_o, const float* __restrict__ part_lse,
                                                  const int32_t* __restrict__ block_idx, __bf16* __restrict__ o,
                                                  float* __restrict__ lse, int N, int Hq, int Hkv, int gshift,
                                                  int top_k) {
@@ -78,18 +79,21 @@ __global__ __launch_bounds__(256) void k_combine(const __bf16* __restrict__ part
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
         if (top_k <= kCombineFastSlots) {
-            bf16x8 x[kCombineFastSlots];
-            float w[kCombineFastSlots];
 #pragma unroll
-            for (int s = 0; s < kCombineFastSlots; ++s) {
-                w[s] = s < top_k ? wts[s * Hq + head] : 0.0f;
-                if (w[s] != 0.0f) x[s] = *(const bf16x8*)(src + s * slot_stride);
+            for (int s0 = 0; s0 < kCombineFastSlots; s0 += 8) {  // 8 slots in flight per batch
+                bf16x8 x[8];
+                float w[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    w[u] = s0 + u < top_k ? wts[(s0 + u) * Hq + head] : 0.0f;
+                    if (w[u] != 0.0f) x[u] = *(const bf16x8*)(src + (s0 + u) * slot_stride);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (w[u] != 0.0f)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[e] += w[u] * (float)x[u][e];
             }
-#pragma unroll
-            for (int s = 0; s < kCombineFastSlots; ++s)
-                if (w[s] != 0.0f)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[e] += w[s] * (float)x[s][e];
         } else {
             for (int s = 0; s < top_k; ++s) {
                 const float w = wts[s * Hq + head];

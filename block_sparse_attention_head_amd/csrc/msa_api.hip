@@ -34,8 +34,10 @@ msa_status check_shape(const msa_shape* s, Dims* d) {
     if (!is_pow2(G) || G > kBlock) return MSA_ERR_UNSUPPORTED;
     if (s->seqlen % kBlock != 0 || s->seqlen >= (1 << 23)) return MSA_ERR_UNSUPPORTED;
     if (s->top_k > 256) return MSA_ERR_UNSUPPORTED;
-    // the combine keeps a position's output row, slot weights and selection rows in LDS (<= 64 KB)
-    if ((double)s->h_q * (256.0 + 4.0 * (s->top_k + 1)) + 4.0 * s->h_kv * s->top_k > 65536.0)
+    // the combine keeps a position's output row, slot weights and selection rows in LDS (<= 64 KB);
+    // the bound below is the one msa.h states
+    if ((double)s->h_q * (256.0 + 4.0 * (s->top_k + 1)) + 8.0 * ((double)s->top_k * s->h_q + 4.0 * s->h_kv * s->top_k) >
+        65536.0)
         return MSA_ERR_UNSUPPORTED;
     // 32-bit index arithmetic bounds used inside the kernels
     const double pairs = (double)s->batch * s->h_kv * s->seqlen * s->top_k;

@@ -67,13 +67,17 @@ typedef enum msa_status {
 typedef struct msa_shape {
     int32_t batch;       /* B >= 1 */
     int32_t seqlen;      /* N >= 1, a multiple of block_size, N < 2^23 */
-    int32_t h_q;         /* query heads, a multiple of h_kv */
+    int32_t h_q;         /* query heads, a multiple of h_kv; the combine keeps one position's output row,
+                            slot weights and selection rows in 64 KB of LDS, which needs
+                            h_q*(256 + 4*(top_k+1)) + 8*(top_k*h_q + 4*h_kv*top_k) <= 65536 */
     int32_t h_kv;        /* KV heads; G = h_q / h_kv must be a power of two <= 128 */
     int32_t h_idx;       /* index query heads; must equal h_kv */
     int32_t head_dim;    /* must be 128 */
     int32_t idx_dim;     /* must be 128 */
     int32_t block_size;  /* must be 128 */
-    int32_t top_k;       /* 1 <= top_k <= 256; counts the forced local block */
+    int32_t top_k;       /* 1 <= top_k <= 256; counts the forced local block. msa_block_topk and
+                            msa_fwd also need top_k >= nblk, or top_k <= 65 with
+                            (top_k-1)*ceil((nblk-1)/64) <= 1024 */
     float softmax_scale; /* > 0 and finite, usually head_dim^-0.5 */
     uint32_t flags;      /* MSA_CAUSAL must be set */
 } msa_shape;
