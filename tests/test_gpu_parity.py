@@ -116,9 +116,12 @@ def test_dense_reduction_on_gpu(msa):
     check_attn(to_np(o), to_np(lse), ref.permute(0, 2, 1, 3).numpy(), torch.logsumexp(s, -1).numpy(), "dense")
 
 
-@pytest.mark.parametrize("name", ["n32k_b2", "n128k"])
+LONG_ROWS = small_workload(1040 * 128, 2, 1, 16, seed=31)  # 1040 blocks: the general (two-pass) top-k path
+
+
+@pytest.mark.parametrize("name", ["n32k_b2", "n128k", "n64k_train", "long_rows"])
 def test_full_size_sampled_rows(msa, name):
-    w = WORKLOADS[name]
+    w = LONG_ROWS if name == "long_rows" else WORKLOADS[name]
     _say(name, "generating inputs")
     x = make_inputs(w)
     xg = _gpu(x)
