@@ -242,6 +242,70 @@ def msa_forward(q_idx, k_idx, q, k, v, top_k: int, softmax_scale: float,
 
 
 # ---------------------------------------------------------------------------
+# Backward of the main branch over cached selections
+# ---------------------------------------------------------------------------
+def sparse_attention_bwd(q, k, v, block_idx, d_o, softmax_scale: float, block_size: int = DEFAULT_BLOCK,
+                         positions: Optional[Sequence[int]] = None):
+    """Gradients of the main-branch attention with the selection held fixed.
+
+    [Flash-MSA] "Kernel Design" and "Backward": the block indices kept from
+    the forward are reused, so the main branch's backward only touches the
+    selected blocks. The selection itself (a top-k) has no gradient. For query
+    head h at position t (group g) with attended keys K(t), P = softmax(z),
+    z_j = scale * q.k_j, O = sum_j P_j v_j, and an incoming gradient dO:
+        dV_j += P_j dO
+        dP_j  = dO . v_j
+        dS_j  = P_j (dP_j - sum_i P_i dP_i)
+        dQ    = scale * sum_j dS_j k_j
+        dK_j += scale * dS_j q
+    (the chain rule through the softmax; LSE receives no gradient).
+
+    block_idx: [B, H_kv, P, top_k] rows for the P query positions that
+    contribute (default: all N, one row per position). dQ rows are returned for
+    those positions; dK, dV hold the sum of their contributions over the whole
+    sequence. Returns dQ float64 [B, P, H_q, D], dK, dV float64 [B, N, H_kv, D].
+    """
+    qq, kk, vv, go = _f64(q), _f64(k), _f64(v), _f64(d_o)
+    bi = np.asarray(block_idx)
+    B, N, Hq, D = qq.shape
+    Hkv = kk.shape[2]
+    G = Hq // Hkv
+    pos = _positions(N, positions)
+    if bi.shape[:3] != (B, Hkv, pos.size):
+        raise ValueError("block_idx must be [B, H_kv, P, top_k] for the contributing positions")
+    dQ = np.zeros((B, pos.size, Hq, D))
+    dK = np.zeros_like(kk)
+    dV = np.zeros_like(vv)
+    for b in range(B):
+        for i, t in enumerate(pos):
+            t = int(t)
+            for g in range(Hkv):
+                keys = attended_keys(bi[b, g, i], t, block_size)
+                if keys.size == 0:  # R9: nothing attended, nothing to differentiate
+                    continue
+                hs = slice(g * G, (g + 1) * G)
+                qg, dog = qq[b, t, hs], go[b, t, hs]         # [G, D]
+                kg, vg = kk[b, keys, g], vv[b, keys, g]      # [n, D]
+                z = softmax_scale * (qg @ kg.T)              # [G, n]
+                p = np.exp(z - z.max(axis=-1, keepdims=True))
+                p /= p.sum(axis=-1, keepdims=True)
+                dp = dog @ vg.T                              # [G, n]
+                ds = p * (dp - (p * dp).sum(axis=-1, keepdims=True))
+                dQ[b, i, hs] = softmax_scale * (ds @ kg)
+                np.add.at(dK[b, :, g], keys, softmax_scale * (ds.T @ qg))
+                np.add.at(dV[b, :, g], keys, p.T @ dog)
+    return dQ, dK, dV
+
+
+def positions_attending(block_idx, block: int, block_size: int = DEFAULT_BLOCK):
+    """Query positions (per batch and KV head) whose selection row holds `block` (attendable: block <= t/B)."""
+    bi = np.asarray(block_idx)
+    t = np.arange(bi.shape[2])
+    hit = np.any(bi == block, axis=-1) & (block <= t // block_size)[None, None]
+    return hit  # [B, H_kv, N] boolean
+
+
+# ---------------------------------------------------------------------------
 # Parity helpers (comparison logic; no method arithmetic beyond the definitions above)
 # ---------------------------------------------------------------------------
 def near_tie_rows(pooled_ref, sel_a, sel_b, top_k: int, block_size: int = DEFAULT_BLOCK,
