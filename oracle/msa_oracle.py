@@ -292,8 +292,19 @@ def sparse_attention_bwd(q, k, v, block_idx, d_o, softmax_scale: float, block_si
                 dp = dog @ vg.T                              # [G, n]
                 ds = p * (dp - (p * dp).sum(axis=-1, keepdims=True))
                 dQ[b, i, hs] = softmax_scale * (ds @ kg)
-                np.add.at(dK[b, :, g], keys, softmax_scale * (ds.T @ qg))
-                np.add.at(dV[b, :, g], keys, p.T @ dog)
+                gk = softmax_scale * (ds.T @ qg)             # [n, D], rows in the order of `keys`
+                gv = p.T @ dog
+                # keys is the concatenation of one contiguous run per valid selected
+                # block (attended_keys); add each run back to its block, so a block
+                # listed twice receives both contributions
+                o = 0
+                for c in bi[b, g, i]:
+                    lo, hi = int(c) * block_size, min((int(c) + 1) * block_size, t + 1)
+                    if c < 0 or hi <= lo:  # padding, or a block after the query: no keys
+                        continue
+                    dK[b, lo:hi, g] += gk[o:o + hi - lo]
+                    dV[b, lo:hi, g] += gv[o:o + hi - lo]
+                    o += hi - lo
     return dQ, dK, dV
 
 

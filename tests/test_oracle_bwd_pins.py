@@ -113,3 +113,38 @@ def test_bwd_empty_rows_contribute_nothing():
     sel = np.full((1, 1, 256, 2), -1, dtype=np.int32)
     dq, dk, dv = O.sparse_attention_bwd(q, k, v, sel, d_o, 1.0)
     assert not dq.any() and not dk.any() and not dv.any()
+
+
+def test_bwd_repeated_and_out_of_range_entries_match_log_multiplicity_bias():
+    # A block listed m times enters the softmax m times, which is the same as one
+    # copy with log(m) added to its logits; entries < 0 or after the query's own
+    # block add nothing. Reference: float64 autograd through SDPA with that bias.
+    rng = np.random.default_rng(7)
+    B, N, Hq, Hkv, D, blk = 1, 512, 4, 2, 8, 128
+    q, k, v, d_o = _inputs(rng, B, N, Hq, Hkv, D)
+    G = Hq // Hkv
+    sel = rng.integers(-2, 6, size=(B, Hkv, N, 4)).astype(np.int32)
+    sel[0, 0, 400] = [2, 2, 3, -1]   # block 2 twice
+    sel[0, 1, 100] = [0, 0, 0, 9]    # block 0 three times, then past the end
+    mult = np.zeros((B, Hq, N, N))
+    for g in range(Hkv):
+        for t in range(N):
+            for c in sel[0, g, t]:
+                if 0 <= c <= t // blk:
+                    mult[0, g * G:(g + 1) * G, t, c * blk:(c + 1) * blk] += 1
+    mult *= np.tril(np.ones((N, N)))[None, None]
+    live = mult.sum(-1) > 0                      # rows with at least one attended key
+    assert live[0, 0, 400] and not live.all()
+    bias = np.where(mult > 0, np.log(np.maximum(mult, 1)), -np.inf)
+    bias[~live] = 0.0                            # keep dead rows finite; their output is masked below
+    qt = torch.tensor(q).permute(0, 2, 1, 3).contiguous().requires_grad_(True)
+    kt = torch.tensor(k).permute(0, 2, 1, 3).contiguous().requires_grad_(True)
+    vt = torch.tensor(v).permute(0, 2, 1, 3).contiguous().requires_grad_(True)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt.repeat_interleave(G, dim=1), vt.repeat_interleave(G, dim=1), attn_mask=torch.tensor(bias), scale=0.5)
+    w = torch.tensor(d_o).permute(0, 2, 1, 3) * torch.tensor(live[..., None].astype(np.float64))
+    (out * w).sum().backward()
+    dq, dk, dv = O.sparse_attention_bwd(q, k, v, sel, d_o, 0.5)
+    np.testing.assert_allclose(dq, qt.grad.permute(0, 2, 1, 3).numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(dk, kt.grad.permute(0, 2, 1, 3).numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(dv, vt.grad.permute(0, 2, 1, 3).numpy(), rtol=1e-10, atol=1e-11)
