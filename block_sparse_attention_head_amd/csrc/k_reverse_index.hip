@@ -5,62 +5,73 @@
 // [MSA summary] "GPU kernel co-design": reverse sparse indexing of queries and
 // pre-scheduled tile chunks for the persistent grid.
 //
-// count: queries per (b, g, c) tile (LDS histogram per workgroup);
-// scan:  exclusive prefix of the counts and of the work items per tile
-//        (a tile of n queries is ceil(n / (128/G)) row tiles of 128 rows, cut
-//        into items of up to kRowTilesPerItem row tiles);
-// scatter: (t << 8 | slot) entries grouped by tile. Each workgroup reserves one
-//        range per tile it touches with a single global atomic and fills it
-//        from LDS counters. The order inside a tile is not fixed, and nothing
-//        downstream depends on it: every query row is computed on its own.
+// The query positions of each (b, g) are cut into nwg consecutive ranges, one
+// workgroup each. Entries (t << 8 | slot) are grouped by tile in a fixed order
+// (position range, then position chunk of 256, then slot, then position), so
+// the plan is a pure function of block_idx: the backward sums over a tile's
+// rows in this order and is bitwise reproducible.
+//   count:   per range, entries per tile (LDS histogram) -> wgcnt[bg][w][c];
+//            the tile totals cnt[bg][c] by integer atomics;
+//   scan:    exclusive prefix of the counts and of the work items per tile
+//            (a tile of n queries is ceil(n / (128/G)) row tiles of 128 rows,
+//            cut into items of up to kRowTilesPerItem row tiles);
+//   wgoff:   in place, wgcnt[bg][w][c] -> off[tile] + sum over w' < w;
+//   scatter: each range writes its entries from its own offsets, ranking equal
+//            tiles inside a chunk by thread index (no atomics decide a slot).
+// Bins beyond the LDS capacity are handled in chunks of kRevLdsBins tiles.
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 
 namespace msa {
 
 constexpr int kRevThreads = 256;
-constexpr int kRevLdsBins = 8192;  // LDS histogram bins; larger nblk counts straight into global memory
+constexpr int kRevLdsBins = 8192;  // tiles per LDS pass
+constexpr int kRevMaxGroups = 256;  // position ranges per (b, g) at most
 
 __global__ __launch_bounds__(256) void k_fill_i32(int32_t* __restrict__ p, int32_t v, long long n) {
     for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) p[i] = v;
 }
 
-constexpr int kRevPosPerGroup = 1024;  // query positions per workgroup (4 per thread)
-
 __device__ __forceinline__ bool valid_entry(int c, int t) { return c >= 0 && c <= (t >> 7); }
 
-// cnt[(b*Hkv + g)*nblk + c] += number of queries t whose row selects block c (valid entries only).
+int rev_positions_per_group(int N) {
+    const int units = (N + 1023) / 1024;  // 1024 positions per range, or more so that ranges <= 256
+    return 1024 * ((units + kRevMaxGroups - 1) / kRevMaxGroups);
+}
+int rev_groups(int N) { return (N + rev_positions_per_group(N) - 1) / rev_positions_per_group(N); }
+
+// wgcnt[(bg*nwg + w)*nblk + c] = entries of range w selecting tile c; cnt[bg*nblk + c] += the same.
 __global__ __launch_bounds__(kRevThreads) void k_rev_count(const int32_t* __restrict__ block_idx,
-                                                           int32_t* __restrict__ cnt, int N, int nblk, int top_k) {
+                                                           int32_t* __restrict__ cnt, int32_t* __restrict__ wgcnt,
+                                                           int N, int nblk, int top_k, int ppw) {
     __shared__ int32_t hist[kRevLdsBins];
-    const bool use_lds = nblk <= kRevLdsBins;
-    const int bg = blockIdx.y;
-    if (use_lds) {
-        for (int i = threadIdx.x; i < nblk; i += kRevThreads) hist[i] = 0;
+    const int bg = blockIdx.y, w = blockIdx.x, nwg = gridDim.x;
+    const int t0 = w * ppw, t1 = min(N, t0 + ppw);
+    int32_t* mine = wgcnt + ((size_t)bg * nwg + w) * nblk;
+    for (int c0 = 0; c0 < nblk; c0 += kRevLdsBins) {
+        const int nb = min(kRevLdsBins, nblk - c0);
+        for (int i = threadIdx.x; i < nb; i += kRevThreads) hist[i] = 0;
         __syncthreads();
-    }
-    for (int q = 0; q < kRevPosPerGroup / kRevThreads; ++q) {
-        const int t = blockIdx.x * kRevPosPerGroup + q * kRevThreads + threadIdx.x;
-        if (t >= N) break;
-        const int32_t* row = block_idx + ((size_t)bg * N + t) * top_k;
-        for (int s = 0; s < top_k; ++s) {
-            const int c = row[s];
-            if (!valid_entry(c, t)) continue;
-            if (use_lds) atomicAdd(&hist[c], 1);
-            else atomicAdd(&cnt[(size_t)bg * nblk + c], 1);
+        for (int t = t0 + threadIdx.x; t < t1; t += kRevThreads) {
+            const int32_t* row = block_idx + ((size_t)bg * N + t) * top_k;
+            for (int s = 0; s < top_k; ++s) {
+                const int c = row[s];
+                if (valid_entry(c, t) && c >= c0 && c < c0 + nb) atomicAdd(&hist[c - c0], 1);
+            }
         }
-    }
-    if (use_lds) {
         __syncthreads();
-        for (int i = threadIdx.x; i < nblk; i += kRevThreads)
-            if (hist[i]) atomicAdd(&cnt[(size_t)bg * nblk + i], hist[i]);
+        for (int i = threadIdx.x; i < nb; i += kRevThreads) {
+            const int n = hist[i];
+            mine[c0 + i] = n;
+            if (n) atomicAdd(&cnt[(size_t)bg * nblk + c0 + i], n);
+        }
+        __syncthreads();
     }
 }
 
 // One workgroup: exclusive scans of the tile counts and of the work items per tile.
 __global__ __launch_bounds__(1024) void k_rev_scan(const int32_t* __restrict__ cnt, int32_t* __restrict__ off,
-                                                   int32_t* __restrict__ item_off, int32_t* __restrict__ cursor,
-                                                   int n, int pos_per_tile) {
+                                                   int32_t* __restrict__ item_off, int n, int pos_per_tile) {
     __shared__ int32_t s_a[1024];
     __shared__ int32_t s_b[1024];
     const int tid = threadIdx.x;
@@ -89,7 +100,6 @@ __global__ __launch_bounds__(1024) void k_rev_scan(const int32_t* __restrict__ c
         const int c = cnt[i];
         const int rt = (c + pos_per_tile - 1) / pos_per_tile;
         off[i] = ra;
-        cursor[i] = ra;
         item_off[i] = rb;
         ra += c;
         rb += (rt + kRowTilesPerItem - 1) / kRowTilesPerItem;
@@ -100,58 +110,77 @@ __global__ __launch_bounds__(1024) void k_rev_scan(const int32_t* __restrict__ c
     }
 }
 
-// Each workgroup counts its entries per tile in LDS, reserves one contiguous
-// range per touched tile with a single global atomic, then hands out slots in
-// that range from LDS counters.
-__global__ __launch_bounds__(kRevThreads) void k_rev_scatter(const int32_t* __restrict__ block_idx,
-                                                             int32_t* __restrict__ cursor,
-                                                             int32_t* __restrict__ entries, int N, int nblk,
-                                                             int top_k) {
-    __shared__ int32_t bins[kRevLdsBins];
-    const bool use_lds = nblk <= kRevLdsBins;
-    const int bg = blockIdx.y;
-    int32_t* cur = cursor + (size_t)bg * nblk;
-    if (use_lds) {
-        for (int i = threadIdx.x; i < nblk; i += kRevThreads) bins[i] = 0;
-        __syncthreads();
-        for (int q = 0; q < kRevPosPerGroup / kRevThreads; ++q) {
-            const int t = blockIdx.x * kRevPosPerGroup + q * kRevThreads + threadIdx.x;
-            if (t >= N) break;
-            const int32_t* row = block_idx + ((size_t)bg * N + t) * top_k;
-            for (int s = 0; s < top_k; ++s) {
-                const int c = row[s];
-                if (valid_entry(c, t)) atomicAdd(&bins[c], 1);
-            }
-        }
-        __syncthreads();
-        for (int i = threadIdx.x; i < nblk; i += kRevThreads) {
-            const int n = bins[i];
-            bins[i] = n ? atomicAdd(&cur[i], n) : 0;
-        }
-        __syncthreads();
+// In place: wgcnt[bg][w][c] becomes the first entry index of range w in tile (bg, c).
+__global__ __launch_bounds__(256) void k_rev_wgoff(const int32_t* __restrict__ off, int32_t* __restrict__ wgcnt,
+                                                   int n_tiles, int nblk, int nwg) {
+    const int tile = blockIdx.x * 256 + threadIdx.x;
+    if (tile >= n_tiles) return;
+    const int bg = tile / nblk, c = tile - bg * nblk;
+    int run = off[tile];
+    for (int w = 0; w < nwg; ++w) {
+        int32_t* p = wgcnt + ((size_t)bg * nwg + w) * nblk + c;
+        const int k = *p;
+        *p = run;
+        run += k;
     }
-    for (int q = 0; q < kRevPosPerGroup / kRevThreads; ++q) {
-        const int t = blockIdx.x * kRevPosPerGroup + q * kRevThreads + threadIdx.x;
-        if (t >= N) break;
-        const int32_t* row = block_idx + ((size_t)bg * N + t) * top_k;
-        for (int s = 0; s < top_k; ++s) {
-            const int c = row[s];
-            if (!valid_entry(c, t)) continue;
-            const int p = use_lds ? atomicAdd(&bins[c], 1) : atomicAdd(&cur[c], 1);
-            entries[p] = (t << 8) | s;
+}
+
+// Range w of (b, g) writes its entries. Chunks of 256 positions are taken in
+// order, slots in order inside a chunk; an entry's place in its tile is the
+// tile's running offset plus the number of lower threads of the same chunk
+// and slot that selected the same tile.
+__global__ __launch_bounds__(kRevThreads) void k_rev_scatter(const int32_t* __restrict__ block_idx,
+                                                             const int32_t* __restrict__ wgoff,
+                                                             int32_t* __restrict__ entries, int N, int nblk,
+                                                             int top_k, int ppw) {
+    __shared__ int32_t bins[kRevLdsBins];
+    __shared__ __attribute__((aligned(16))) int32_t keys[kRevThreads];
+    const int tid = threadIdx.x;
+    const int bg = blockIdx.y, w = blockIdx.x, nwg = gridDim.x;
+    const int t0 = w * ppw, t1 = min(N, t0 + ppw);
+    const int32_t* base_off = wgoff + ((size_t)bg * nwg + w) * nblk;
+    for (int c0 = 0; c0 < nblk; c0 += kRevLdsBins) {
+        const int nb = min(kRevLdsBins, nblk - c0);
+        __syncthreads();  // the previous bin chunk is done
+        for (int i = tid; i < nb; i += kRevThreads) bins[i] = base_off[c0 + i];
+        __syncthreads();
+        for (int cb = t0; cb < t1; cb += kRevThreads) {  // uniform trip count
+            const int t = cb + tid;
+            const bool in = t < t1;
+            const int32_t* row = block_idx + ((size_t)bg * N + (in ? t : t0)) * top_k;
+            for (int s = 0; s < top_k; ++s) {
+                const int c = in ? row[s] : -1;
+                const bool ok = in && valid_entry(c, t) && c >= c0 && c < c0 + nb;
+                keys[tid] = ok ? c : -1;
+                __syncthreads();
+                if (ok) {
+                    int r = 0;
+                    for (int j = 0; j < (tid & ~3); j += 4) {
+                        const int4 kv = *(const int4*)(keys + j);
+                        r += (kv.x == c) + (kv.y == c) + (kv.z == c) + (kv.w == c);
+                    }
+                    for (int j = tid & ~3; j < tid; ++j) r += keys[j] == c;
+                    entries[bins[c - c0] + r] = (t << 8) | s;
+                }
+                __syncthreads();  // every place of this slot is taken from the old offsets
+                if (ok) atomicAdd(&bins[c - c0], 1);
+            }
         }
     }
 }
 
 hipError_t launch_sparse_plan(const int32_t* block_idx, const SparseWs& ws, const Dims& d, hipStream_t stream) {
     const int n = d.B * d.Hkv * d.nblk;
+    const int ppw = rev_positions_per_group(d.N), nwg = rev_groups(d.N);
     hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, stream, ws.cnt, 0, (long long)n);
-    const dim3 rgrid((d.N + kRevPosPerGroup - 1) / kRevPosPerGroup, d.B * d.Hkv);
-    hipLaunchKernelGGL(k_rev_count, rgrid, dim3(kRevThreads), 0, stream, block_idx, ws.cnt, d.N, d.nblk, d.top_k);
-    hipLaunchKernelGGL(k_rev_scan, dim3(1), dim3(1024), 0, stream, ws.cnt, ws.off, ws.item_off, ws.cursor, n,
+    const dim3 rgrid(nwg, d.B * d.Hkv);
+    hipLaunchKernelGGL(k_rev_count, rgrid, dim3(kRevThreads), 0, stream, block_idx, ws.cnt, ws.wgoff, d.N, d.nblk,
+                       d.top_k, ppw);
+    hipLaunchKernelGGL(k_rev_scan, dim3(1), dim3(1024), 0, stream, ws.cnt, ws.off, ws.item_off, n,
                        kBlock >> d.gshift);
-    hipLaunchKernelGGL(k_rev_scatter, rgrid, dim3(kRevThreads), 0, stream, block_idx, ws.cursor, ws.entries, d.N,
-                       d.nblk, d.top_k);
+    hipLaunchKernelGGL(k_rev_wgoff, dim3((n + 255) / 256), dim3(256), 0, stream, ws.off, ws.wgoff, n, d.nblk, nwg);
+    hipLaunchKernelGGL(k_rev_scatter, rgrid, dim3(kRevThreads), 0, stream, block_idx, ws.wgoff, ws.entries, d.N,
+                       d.nblk, d.top_k, ppw);
     return hipGetLastError();
 }
 

@@ -59,30 +59,70 @@ msa_status check_shape(const msa_shape* s, Dims* d) {
 
 }  // namespace
 
-size_t sparse_ws_bytes(const Dims& d) {
+namespace {
+
+// Reverse index and work list (cnt, off, item_off, wgoff, entries): the common
+// prefix of the forward and backward workspaces.
+size_t plan_ws_bytes(const Dims& d) {
     const size_t n = (size_t)d.B * d.Hkv * d.nblk;
     size_t s = 0;
-    s += align_up(n * 4, 256);                                      // cnt
-    s += align_up((n + 1) * 4, 256);                                // off
-    s += align_up((n + 1) * 4, 256);                                // item_off
-    s += align_up(n * 4, 256);                                      // cursor
-    s += align_up((size_t)d.B * d.Hkv * d.N * d.top_k * 4, 256);    // entries
-    s += align_up((size_t)d.B * d.N * d.top_k * d.Hq * kDim * 2, 256);  // part_o
-    s += align_up((size_t)d.B * d.N * d.top_k * d.Hq * 4, 256);     // part_lse
+    s += align_up(n * 4, 256);                                    // cnt
+    s += align_up((n + 1) * 4, 256);                              // off
+    s += align_up((n + 1) * 4, 256);                              // item_off
+    s += align_up(n * rev_groups(d.N) * 4, 256);                  // wgoff
+    s += align_up((size_t)d.B * d.Hkv * d.N * d.top_k * 4, 256);  // entries
     return s;
 }
 
-SparseWs carve_sparse_ws(void* base, const Dims& d) {
+SparseWs carve_plan_ws(void* base, const Dims& d) {
     const size_t n = (size_t)d.B * d.Hkv * d.nblk;
     char* p = (char*)base;
     SparseWs w;
     w.cnt = (int32_t*)p;      p += align_up(n * 4, 256);
     w.off = (int32_t*)p;      p += align_up((n + 1) * 4, 256);
     w.item_off = (int32_t*)p; p += align_up((n + 1) * 4, 256);
-    w.cursor = (int32_t*)p;   p += align_up(n * 4, 256);
-    w.entries = (int32_t*)p;  p += align_up((size_t)d.B * d.Hkv * d.N * d.top_k * 4, 256);
-    w.part_o = (void*)p;      p += align_up((size_t)d.B * d.N * d.top_k * d.Hq * kDim * 2, 256);
+    w.wgoff = (int32_t*)p;    p += align_up(n * rev_groups(d.N) * 4, 256);
+    w.entries = (int32_t*)p;
+    w.part_o = nullptr;
+    w.part_lse = nullptr;
+    return w;
+}
+
+}  // namespace
+
+size_t sparse_ws_bytes(const Dims& d) {
+    size_t s = plan_ws_bytes(d);
+    s += align_up((size_t)d.B * d.N * d.top_k * d.Hq * kDim * 2, 256);  // part_o
+    s += align_up((size_t)d.B * d.N * d.top_k * d.Hq * 4, 256);         // part_lse
+    return s;
+}
+
+SparseWs carve_sparse_ws(void* base, const Dims& d) {
+    SparseWs w = carve_plan_ws(base, d);
+    char* p = (char*)base + plan_ws_bytes(d);
+    w.part_o = (void*)p;
+    p += align_up((size_t)d.B * d.N * d.top_k * d.Hq * kDim * 2, 256);
     w.part_lse = (float*)p;
+    return w;
+}
+
+size_t bwd_ws_bytes(const Dims& d) {
+    size_t s = plan_ws_bytes(d);
+    s += align_up((size_t)d.B * d.N * d.Hq * 4, 256);                  // delta
+    s += align_up((size_t)d.B * d.N * d.top_k * d.Hq * kDim * 4, 256);  // dq_part
+    s += align_up(bwd_max_items(d) * 2 * kBlock * kDim * 4, 256);       // dkv_part
+    return s;
+}
+
+BwdWs carve_bwd_ws(void* base, const Dims& d) {
+    BwdWs w;
+    w.plan = carve_plan_ws(base, d);
+    char* p = (char*)base + plan_ws_bytes(d);
+    w.delta = (float*)p;
+    p += align_up((size_t)d.B * d.N * d.Hq * 4, 256);
+    w.dq_part = (float*)p;
+    p += align_up((size_t)d.B * d.N * d.top_k * d.Hq * kDim * 4, 256);
+    w.dkv_part = (float*)p;
     return w;
 }
 
@@ -96,6 +136,7 @@ size_t ws_bytes(const Dims& d, msa_op op) {
         case MSA_OP_BLOCK_TOPK: return 0;
         case MSA_OP_SPARSE_ATTN_FWD: return sparse_ws_bytes(d);
         case MSA_OP_FWD: return align_up(pooled_bytes(d), 256) + sparse_ws_bytes(d);
+        case MSA_OP_SPARSE_ATTN_BWD: return bwd_ws_bytes(d);
     }
     return 0;
 }
@@ -125,7 +166,7 @@ extern "C" {
 
 msa_status msa_workspace_size(const msa_shape* shape, msa_op op, size_t* bytes) {
     if (!bytes) return MSA_ERR_INVALID_ARG;
-    if (op < MSA_OP_INDEX_SCORES || op > MSA_OP_FWD) return MSA_ERR_INVALID_ARG;
+    if (op < MSA_OP_INDEX_SCORES || op > MSA_OP_SPARSE_ATTN_BWD) return MSA_ERR_INVALID_ARG;
     Dims d;
     const msa_status st = check_shape(shape, &d);
     if (st != MSA_OK) return st;
@@ -228,6 +269,24 @@ msa_status msa_fwd(const msa_shape* shape, const void* q_idx, const void* k_idx,
     e = launch_sparse_plan(block_idx, ws, d, stream);
     if (e == hipSuccess) e = launch_sparse_partial(q, k, v, ws, d, stream);
     if (e == hipSuccess) e = launch_sparse_combine(block_idx, o, lse, ws, d, stream);
+    return hip_status(e);
+}
+
+msa_status msa_sparse_attn_bwd(const msa_shape* shape, const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* d_o, const int32_t* block_idx, void* dq, void* dk,
+                               void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    Dims d;
+    const msa_status st = check_shape(shape, &d);
+    if (st != MSA_OK) return st;
+    if (!q || !k || !v || !o || !lse || !d_o || !block_idx || !dq || !dk || !dv) return MSA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < ws_bytes(d, MSA_OP_SPARSE_ATTN_BWD)) return MSA_ERR_WORKSPACE;
+    (void)hipGetLastError();
+    const BwdWs ws = carve_bwd_ws(workspace, d);
+    hipError_t e = launch_sparse_plan(block_idx, ws.plan, d, stream);
+    if (e == hipSuccess) e = launch_bwd_delta(o, d_o, ws.delta, d, stream);
+    if (e == hipSuccess) e = launch_bwd_main(q, k, v, d_o, lse, ws, d, stream);
+    if (e == hipSuccess) e = launch_bwd_dq_sum(block_idx, dq, ws, d, stream);
+    if (e == hipSuccess) e = launch_bwd_dkdv_reduce(dk, dv, ws, d, stream);
     return hip_status(e);
 }
 

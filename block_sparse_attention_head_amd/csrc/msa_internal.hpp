@@ -31,11 +31,13 @@ struct SparseWs {
     int32_t* cnt;       // [B*Hkv*nblk]    queries per (b, g, c) tile
     int32_t* off;       // [B*Hkv*nblk+1]  exclusive prefix of cnt
     int32_t* item_off;  // [B*Hkv*nblk+1]  exclusive prefix of work items per tile
-    int32_t* cursor;    // [B*Hkv*nblk]    scatter cursors
+    int32_t* wgoff;     // [B*Hkv, rev_groups(N), nblk] per position range: entries, then first entry
     int32_t* entries;   // [B*Hkv*N*top_k] (t << 8 | slot), grouped by tile
     void* part_o;       // bf16 [B, N, top_k, Hq, 128] normalised partial outputs (lane order)
     float* part_lse;    // fp32 [B, N, top_k, Hq]      partial log-sum-exp
 };
+// Position ranges (workgroups) per (b, g) of the reverse-index scatter.
+int rev_groups(int N);
 size_t sparse_ws_bytes(const Dims& d);
 SparseWs carve_sparse_ws(void* base, const Dims& d);
 
@@ -46,6 +48,25 @@ hipError_t launch_sparse_partial(const void* q, const void* k, const void* v, co
 size_t combine_lds_bytes(const Dims& d);
 hipError_t launch_sparse_combine(const int32_t* block_idx, void* o, float* lse, const SparseWs& ws, const Dims& d,
                                  hipStream_t stream);
+
+// Workspace of the sparse attention backward: the forward's plan (reverse index
+// and work items, part_o / part_lse unused) followed by the backward's buffers.
+struct BwdWs {
+    SparseWs plan;
+    float* delta;     // fp32 [B, N, Hq]               rowsum(dO * O)
+    float* dq_part;   // fp32 [B, N, top_k, Hq, 128]   unscaled dQ per (t, slot, head)
+    float* dkv_part;  // fp32 [items, 2, 128, 128]     dK (scaled), dV per work item
+};
+size_t bwd_max_items(const Dims& d);
+size_t bwd_ws_bytes(const Dims& d);
+BwdWs carve_bwd_ws(void* base, const Dims& d);
+
+hipError_t launch_bwd_delta(const void* o, const void* d_o, float* delta, const Dims& d, hipStream_t stream);
+hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* d_o, const float* lse,
+                           const BwdWs& ws, const Dims& d, hipStream_t stream);
+hipError_t launch_bwd_dq_sum(const int32_t* block_idx, void* dq, const BwdWs& ws, const Dims& d,
+                             hipStream_t stream);
+hipError_t launch_bwd_dkdv_reduce(void* dk, void* dv, const BwdWs& ws, const Dims& d, hipStream_t stream);
 
 // Compute-unit count of the current device (cached per device).
 int device_cu_count();

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
 MSA_OK = 0
 MSA_CAUSAL = 1
 MSA_POOLED_VISIBLE_ONLY = 2
-OP_INDEX_SCORES, OP_BLOCK_TOPK, OP_SPARSE_ATTN_FWD, OP_FWD = 0, 1, 2, 3
+OP_INDEX_SCORES, OP_BLOCK_TOPK, OP_SPARSE_ATTN_FWD, OP_FWD, OP_SPARSE_ATTN_BWD = 0, 1, 2, 3, 4
 
 BLOCK_SIZE = 128
 HEAD_DIM = 128
@@ -59,6 +59,7 @@ _SIGNATURES = {
     "msa_sparse_attn_partial": [_S, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "msa_sparse_attn_combine": [_S, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "msa_fwd": [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "msa_sparse_attn_bwd": [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
 }
 
 _lib = None
@@ -192,6 +193,29 @@ def sparse_attn_fwd(q, k, v, block_idx, softmax_scale: float, o=None, lse=None, 
            lib().msa_sparse_attn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(o),
                                      _ptr(lse), _ptr(ws), ws.numel(), _stream(q.device)))
     return o, lse
+
+
+def sparse_attn_bwd(q, k, v, o, lse, d_o, block_idx, softmax_scale: float, dq=None, dk=None, dv=None,
+                    workspace=None):
+    """(dQ, dK, dV) in bf16 over the cached selection (see msa_sparse_attn_bwd)."""
+    shape = _attn_shape(q, k, v, block_idx, softmax_scale)
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    _need(o, "o", torch.bfloat16, (B, N, Hq, D))
+    _need(lse, "lse", torch.float32, (B, Hq, N))
+    _need(d_o, "d_o", torch.bfloat16, (B, N, Hq, D))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", torch.bfloat16, (B, N, Hq, D))
+    _need(dk, "dk", torch.bfloat16, (B, N, Hkv, D))
+    _need(dv, "dv", torch.bfloat16, (B, N, Hkv, D))
+    ws = _ws(workspace, shape, OP_SPARSE_ATTN_BWD, q.device)
+    _check("msa_sparse_attn_bwd",
+           lib().msa_sparse_attn_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o),
+                                     _ptr(block_idx), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
+                                     _stream(q.device)))
+    return dq, dk, dv
 
 
 def sparse_attn_plan(shape: MsaShape, block_idx: torch.Tensor, workspace: torch.Tensor) -> None:

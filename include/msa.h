@@ -86,7 +86,8 @@ typedef enum msa_op {
     MSA_OP_INDEX_SCORES = 0,
     MSA_OP_BLOCK_TOPK = 1,
     MSA_OP_SPARSE_ATTN_FWD = 2,
-    MSA_OP_FWD = 3
+    MSA_OP_FWD = 3,
+    MSA_OP_SPARSE_ATTN_BWD = 4
 } msa_op;
 
 /* Bytes of device workspace `op` needs for `shape` (0 is a valid answer).
@@ -155,6 +156,31 @@ msa_status msa_sparse_attn_combine(const msa_shape* shape, const int32_t* block_
 msa_status msa_fwd(const msa_shape* shape, const void* q_idx, const void* k_idx, const void* q,
                    const void* k, const void* v, int32_t* block_idx, void* o, float* lse,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward of msa_sparse_attn_fwd over the cached block indices ([Flash-MSA]
+ * "Kernel Design": the block indices are kept until the backward so that the
+ * whole step after the index branch is linear in N; "Backward": the map from
+ * (query, slot) to key block is inverted into key block -> queries, tasks are
+ * scheduled per key block and each streams chunks of gathered query rows
+ * against the resident K/V block, computing dQ, dK and dV). With z_j and the
+ * attended set as in msa_sparse_attn_fwd, P_j = exp(z_j - lse[b,h,t]) and
+ * D = sum_d d_o[b,t,h,d] * o[b,t,h,d]:
+ *   dq[b,t,h] = softmax_scale * sum_j P_j (d_o[b,t,h] . v[b,j,g] - D) k[b,j,g]
+ *   dk[b,j,g] = softmax_scale * sum_{(t,h) attending j} P_j (d_o . v_j - D) q[b,t,h]
+ *   dv[b,j,g] = sum_{(t,h) attending j} P_j d_o[b,t,h]
+ * Inputs: q, k, v, block_idx as given to the forward; o and lse as the forward
+ * returned them; d_o bf16 [B, N, H_q, 128] (the gradient of o). Outputs (bf16,
+ * every element written): dq [B, N, H_q, 128], dk and dv [B, N, H_kv, 128]
+ * (zero for keys no query attends). The index branch has no gradient here.
+ * Products are bf16 with fp32 accumulation (P and dS are rounded to bf16 before
+ * their products, as in the forward). Per-slot dQ partials and per-task dK/dV
+ * partials in the workspace (MSA_OP_SPARSE_ATTN_BWD) are summed by separate
+ * passes: deterministic, no floating-point atomics. Rows with no valid entry
+ * get dq = 0. */
+msa_status msa_sparse_attn_bwd(const msa_shape* shape, const void* q, const void* k, const void* v,
+                               const void* o, const float* lse, const void* d_o,
+                               const int32_t* block_idx, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, never-NULL description of a status code. */
 const char* msa_status_string(msa_status status);

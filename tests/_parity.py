@@ -9,6 +9,13 @@ Tolerances:
     own pooled scores; against the oracle's float64 pooled scores, mismatching
     rows must be near-ties (reported, not failed).
   * O: max |GPU - oracle| <= 2e-2; LSE: max |GPU - oracle| <= 1e-3.
+  * gradients (dQ, dK, dV of the main branch): per tensor, the largest
+    elementwise error <= 1e-2 * max |oracle| and 1 - cosine similarity <= 1e-4.
+    The GPU rounds P and dS to bf16 before their products (relative 2^-9 per
+    term), takes D = rowsum(dO * O) from the bf16 O, and rounds each gradient
+    to bf16 (2^-9): errors of a few 2^-9 of the tensor's scale, so 1e-2 leaves
+    a margin of about 3. [Flash-MSA] "Correctness" compares gradients by cosine
+    similarity with 0.01 as the usual bf16 tolerance; 1e-4 is far inside it.
 """
 from __future__ import annotations
 
@@ -63,6 +70,33 @@ def check_attn(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_re
     assert do <= O_TOL, f"{tag}: O max abs error {do:.3e} > {O_TOL}"
     assert dl <= LSE_TOL, f"{tag}: LSE max abs error {dl:.3e} > {LSE_TOL}"
     return do, dl
+
+
+GRAD_REL_TOL = 1e-2
+GRAD_COS_TOL = 1e-4
+
+
+def check_grads(gpu, ref, tag=""):
+    """Compare tuples of gradient tensors; returns a printable summary."""
+    out = []
+    for i, (g, r) in enumerate(zip(gpu, ref)):
+        g = np.asarray(g, dtype=np.float64)
+        r = np.asarray(r, dtype=np.float64)
+        assert g.shape == r.shape, f"{tag}[{i}]: shape {g.shape} vs {r.shape}"
+        assert np.all(np.isfinite(g)), f"{tag}[{i}]: non-finite gradient"
+        scale = float(np.abs(r).max())
+        err = float(np.abs(g - r).max())
+        if scale == 0.0:
+            assert err == 0.0, f"{tag}[{i}]: nonzero gradient where the oracle's is zero"
+            out.append(f"[{i}] zero")
+            continue
+        nr, ng = float(np.linalg.norm(r)), float(np.linalg.norm(g))
+        cos = float((g * r).sum() / (nr * ng)) if ng > 0 else 0.0
+        rel = err / scale
+        assert rel <= GRAD_REL_TOL, f"{tag}[{i}]: max error {err:.3e} = {rel:.2e} of max|ref| {scale:.3e}"
+        assert 1.0 - cos <= GRAD_COS_TOL, f"{tag}[{i}]: cosine similarity {cos:.8f}"
+        out.append(f"[{i}] rel {rel:.2e} 1-cos {1.0 - cos:.1e}")
+    return " ".join(out)
 
 
 def to_np(t: torch.Tensor) -> np.ndarray:

@@ -63,6 +63,9 @@ def test_workspace_size_valid(m):
     st1, n1 = _ws(m, op=m.OP_SPARSE_ATTN_FWD)
     st2, n2 = _ws(m, op=m.OP_FWD)
     assert st1 == st2 == 0 and n2 > n1
+    # backward: reverse index + D [1,1024,4] + dQ partials [1,1024,4,4,128] fp32 + dK/dV item partials
+    st3, n3 = _ws(m, op=m.OP_SPARSE_ATTN_BWD)
+    assert st3 == 0 and n3 >= 1024 * 4 * 4 + 1024 * 4 * 4 * 128 * 4 + 2 * 128 * 128 * 4
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -109,6 +112,14 @@ def test_null_pointers_rejected_before_any_launch(m):
     assert lib.msa_sparse_attn_partial(ctypes.byref(s), one, one, one, one, 10, P(0)) == 3
     assert lib.msa_sparse_attn_combine(ctypes.byref(s), one, one, one, one, 10, P(0)) == 3
     assert lib.msa_fwd(None, one, one, one, one, one, one, one, one, one, 10, P(0)) == 1
+    bwd = lib.msa_sparse_attn_bwd
+    args = [one] * 10
+    for i in range(10):  # each of q, k, v, o, lse, d_o, block_idx, dq, dk, dv
+        a = list(args)
+        a[i] = P(0)
+        assert bwd(ctypes.byref(s), *a, one, 1 << 40, P(0)) == 1, i
+    assert bwd(ctypes.byref(s), *args, P(0), 1 << 40, P(0)) == 3
+    assert bwd(ctypes.byref(s), *args, one, 10, P(0)) == 3
 
 
 def test_status_strings(m):
