@@ -16,17 +16,19 @@
 //   k_bwd_main        one persistent workgroup per work item (a chunk of the
 //                     rows gathered for one (key block, KV head) tile). Wave w
 //                     owns keys 32w .. 32w+31 of the block and keeps their K, V
-//                     (and the K^T slice for dims 32w .. 32w+31) as MFMA
-//                     operands in registers. Per 32 gathered rows:
+//                     as MFMA operands in registers. Per 32 gathered rows:
 //                       S = Q K^T, dP = dO V^T    (rows x own keys, one lane per key)
 //                       P, dS                      (bf16, dS also into LDS)
 //                       dV += P^T dO, dK += dS^T Q (Q, dO staged transposed in LDS)
-//                       dQ_rows = dS K             (all 128 keys, own 32 dims)
-//                     dQ rows go to fp32 per-(t, slot, head) partials; dK, dV
-//                     to one fp32 partial per work item.
+//                       dQ^T = K^T dS^T            (all 128 keys, own 32 dims)
+//                     dQ rows go to bf16 per-(t, slot, head) partials (the
+//                     forward's chunk-major record layout); dK, dV to one fp32
+//                     partial per work item.
 //   k_bwd_dq_sum      dQ = scale * sum of the valid slots' partials, to bf16.
 //   k_bwd_dkdv_reduce dK, dV of each key block = sum of its items' partials, to
 //                     bf16 (zero for blocks no query selected).
+#include <utility>
+
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 
@@ -58,49 +60,108 @@ __global__ __launch_bounds__(256) void k_bwd_delta(const __bf16* __restrict__ o,
 
 // ---------------------------------------------------------------------------
 // Fused main backward.
+//
+// Per work item: the lane's own K and V rows go to registers; the block's K
+// tile is staged row-major in LDS once and the lane's K^T fragments (A
+// operands of dQ^T) are read from it with transposing LDS loads. Gathered
+// rows go 32 at a time ("steps") through a ring of kBwdRing row-major LDS
+// stages filled by direct global->LDS loads issued kBwdRing - 1 steps ahead
+// (no registers held while they fly). The transposed Q^T / dO^T operands of
+// dK, dV come from the same row-major stage through ds_read_b64_tr_b16. Step s:
+//   (a) issue the loads of step s+3
+//   (c) S = Q K^T, dP = dO V^T; P, dS (dS -> LDS)
+//   (d) dV += P^T dO, dK += dS^T Q
+//   (e) wait for step s+1's loads; barrier
+//   (f) dQ^T rows = K^T dS^T -> bf16 partials
 // ---------------------------------------------------------------------------
 constexpr int kBwdRows = 32;                                   // gathered rows per step
+constexpr int kBwdRing = 4;                                    // row-major stages
 constexpr int kBwdMaxItemEntries = kRowTilesPerItem * kBlock;  // entries of one item when G = 1
 
-// 64-byte lines of 32 bf16 (4 chunks); chunk ch of line r sits at ch ^ ((r >> 1) & 3).
-__device__ __forceinline__ int tline_offset(int r, int ch) { return r * kBwdRows + ((ch ^ ((r >> 1) & 3)) << 3); }
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(3))) bf16x4* lds_bf16x4_ptr;
 
-struct BwdStage {
-    __bf16 qr[kBwdRows * kDim];  // Q rows [row][dim] (swz_chunk_offset)
-    __bf16 dr[kBwdRows * kDim];  // dO rows
-    __bf16 qt[kDim * kBwdRows];  // Q^T [dim][tpos(row)] (tline_offset)
-    __bf16 dt[kDim * kBwdRows];  // dO^T
-    float lse2[kBwdRows];        // LSE * log2(e)
-    float dlt[kBwdRows];         // D
-    int lim[kBwdRows];           // last key offset of the block the row attends (127 off its own block, -1 padding)
-    int rec[kBwdRows];           // (b*N + t)*top_k + slot of the row, -1 padding
+// Row-major tiles with 128-element rows filled by global->LDS loads: chunk ch
+// (8 elements) of row r sits at chunk slot ch ^ (r & 7). Eight consecutive rows
+// read at one chunk fall into distinct banks, and most of the per-lane address
+// stays independent of the chunk, so unrolled reads share base registers.
+__device__ __forceinline__ int ring_off(int row, int ch) { return row * kDim + ((ch ^ (row & 7)) << 3); }
+
+// dS rows [32][128] padded to 136 elements (272 bytes): consecutive rows shift by
+// four banks, and every offset is a per-lane base plus a constant.
+constexpr int kDsRow = kBlock + 8;
+
+struct BwdRowStage {             // written by global->LDS loads
+    __bf16 q[kBwdRows * kDim];   // Q rows [row][dim] (ring_off)
+    __bf16 d[kBwdRows * kDim];   // dO rows
+    float lse[kBwdRows];         // LSE of the row (natural log)
+    float dlt[kBwdRows];         // D of the row; must follow lse
 };
 
-// One step's rows held in registers between their global loads and their LDS stores.
-struct BwdPrefetch {
-    uint4 qv[2], dv[2];  // row-major chunks
-    bf16x8 tr[4];        // 4 rows x 8 dims of Q or dO, for the transposed copy
-    float lse2, dlt;
-    int lim, rec;
-};
+// ds_read_b64_tr_b16 on a row-major tile with 128-element rows (ring_off):
+// inside each 16-lane group, lane li addresses row r0 + li/4, columns
+// c0 + 4(li%4) .. +3, and receives column c0 + li of rows r0 .. r0+3 (checked
+// on the device). c0 is a multiple of 16.
+__device__ __forceinline__ bf16x4 tr_rows4(const __bf16* tile, int r0, int c0, int li) {
+    const int row = r0 + (li >> 2), col = c0 + 4 * (li & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4_ptr)(tile + ring_off(row, col >> 3) + (col & 7)));
+}
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+    return (bf16x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// s_waitcnt with vmcnt <= n (n < 16) and no wait on the other counters (gfx9 encoding)
+#define MSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8))
+// s_waitcnt lgkmcnt(0) only
+#define MSA_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14))
+
+// Workgroup barrier for LDS data the caller has already waited for (lgkmcnt
+// for its own LDS stores, vmcnt for its own global->LDS loads). A fenced
+// barrier (__syncthreads, or a fence on LDS alone) waits for every outstanding
+// vector-memory operation, because global->LDS loads write LDS; that would
+// drain the row loads issued steps ahead. The memory clobber keeps the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// A 16-bit LDS store the compiler's wait insertion does not see. A plain LDS
+// store made after global->LDS loads are issued makes the compiler wait for all
+// of them (it cannot tell the destinations apart), which would drain the row
+// prefetch every step. These stores go to a buffer no such load writes; the
+// caller waits on lgkmcnt(0) before the barrier that publishes them.
+template <int OFF>
+__device__ __forceinline__ void lds_store_b16(uint32_t addr, uint32_t bits) {
+    asm volatile("ds_write_b16 %0, %1 offset:%2" ::"v"(addr), "v"(bits), "i"(OFF) : "memory");
+}
+// The 16 dS values of a lane (score register i holds row mfma32_row(i, h)) into
+// padded dS rows: byte address base + row(i, 0) * 2 * kDsRow, base covering the
+// lane's key and its 4h row offset.
+template <int... I>
+__device__ __forceinline__ void store_ds16(uint32_t base, const uint32_t (&bits)[16], std::integer_sequence<int, I...>) {
+    (lds_store_b16<(8 * (I >> 2) + (I & 3)) * 2 * kDsRow>(base, bits[I]), ...);
+}
 
 __global__ __launch_bounds__(256, 1) void k_bwd_main(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ off, const int32_t* __restrict__ item_off, const int32_t* __restrict__ entries,
-    float* __restrict__ dq_part, float* __restrict__ dkv_part, int N, int Hq, int Hkv, int gshift, int nblk,
+    __bf16* __restrict__ dq_part, float* __restrict__ dkv_part, int N, int Hq, int Hkv, int gshift, int nblk,
     int top_k, int n_tiles, float scale, float scale_log2) {
-    __shared__ __attribute__((aligned(16))) BwdStage st;
-    __shared__ __attribute__((aligned(16))) __bf16 dsl[kBwdRows * kBlock];  // dS [row][key] (swz_chunk_offset)
-    __shared__ __attribute__((aligned(16))) __bf16 kts[kDim * kBlock];       // K^T [dim][key] (swz_chunk_offset)
-    __shared__ int32_t ent[kBwdMaxItemEntries];                              // this item's (t << 8 | slot)
+    __shared__ __attribute__((aligned(16))) BwdRowStage ring[kBwdRing];         // also holds the K tile at item start
+    __shared__ __attribute__((aligned(16))) __bf16 dsl[2][kBwdRows * kDsRow];  // dS [row][key], padded rows
+    __shared__ int32_t ent[kBwdMaxItemEntries];                                 // this item's (t << 8 | slot)
+    __shared__ __attribute__((aligned(16))) int32_t lims[2][kBwdRows];          // per step: last attended key per row
+    static_assert(2 * sizeof(BwdRowStage) >= kBlock * kDim * sizeof(__bf16), "K tile must fit in two stages");
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
+    const int li = lane & 15, dhalf = (lane >> 4) & 1;  // 16-lane group: lane in group, which 16 columns
     const int G = 1 << gshift;
     const int P = kBlock >> gshift;
     const int my_key = wave * 32 + l32;  // key of this lane inside the block
     const int total_items = item_off[n_tiles];
     const float log2e = 1.4426950408889634f;
+    __bf16* ktile = ring[0].q;           // K [key][dim] during the item prologue
 
     for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
         int lo = 0, hi = n_tiles;  // tile = last index with item_off[tile] <= item
@@ -123,21 +184,13 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
 
         __syncthreads();  // the previous item's LDS reads are done
         for (int i = tid; i < ne; i += 256) ent[i] = entries[e0 + rt0 * P + i];
-        // K^T of the block: 4 keys x 8 dims per unit, 512 units
+        // K tile -> LDS (row-major, swizzled through the source chunk): 8 x 4 rows per wave
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int unit = tid + 256 * u, kg = unit >> 4, dc = unit & 15;
-            bf16x8 rows[4];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                rows[rr] = *(const bf16x8*)(k + tile_off + (size_t)(kg * 4 + rr) * kstride + dc * 8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                bf16x4 w;
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) w[rr] = rows[rr][e];
-                *(bf16x4*)(kts + swz_chunk_offset(dc * 8 + e, kg >> 1) + ((kg & 1) << 2)) = w;
-            }
+        for (int i = 0; i < 8; ++i) {
+            const int row = 16 * i + 4 * wave + (lane >> 4);  // 128 rows over 8 x 4 waves x 4 rows
+            const int ch = (lane & 15) ^ (row & 7);
+            __builtin_amdgcn_global_load_lds((const void*)(k + tile_off + (size_t)row * kstride + ch * 8),
+                                             (lds_ptr)(ktile + (16 * i + 4 * wave) * kDim), 16, 0, 0);
         }
         // own keys as B operands: lane holds K[my_key][16 kk + 8 h + e], same for V
         bf16x8 kf[8], vf[8];
@@ -148,19 +201,27 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
                 kf[kk] = *(const bf16x8*)(k + krow + kk * 16);
                 vf[kk] = *(const bf16x8*)(v + krow + kk * 16);
             }
+            // keep these loop-invariant MFMA operands in accumulation registers (MFMA reads them
+            // from there directly), leaving the vector registers to the step loop
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) asm volatile("" : "+a"(kf[kk]), "+a"(vf[kk]));
         }
         f32x16 dk[4], dv[4];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) dk[nt][i] = dv[nt][i] = 0.0f;
-        __syncthreads();  // ent, kts
-        // K^T slice as the B operand of dQ: lane holds K[16 kk + 8 h + e][32 wave + l32]
+        MSA_WAIT_VMCNT(0);
+        __syncthreads();  // ent, K tile
+        // K^T fragments, A operands of dQ^T: lane holds K[16 kk + 8 h + e][32 wave + l32]
         bf16x8 ktf[8];
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) ktf[kk] = *(const bf16x8*)(kts + swz_chunk_offset(32 * wave + l32, 2 * kk + h));
+        for (int kk = 0; kk < 8; ++kk)
+            ktf[kk] = cat8(tr_rows4(ktile, 16 * kk + 8 * h, 32 * wave + 16 * dhalf, li),
+                           tr_rows4(ktile, 16 * kk + 8 * h + 4, 32 * wave + 16 * dhalf, li));
+        __syncthreads();  // the K tile is read; the ring may be refilled
 
-        // entry and head of gathered row r of this item
+        // entry and head of gathered row r of this item (rows past the end read entry 0)
         auto row_src = [&](int r, bool& ok, int& t, int& slot, int& head) {
             ok = r < nrows;
             const int en = ent[ok ? (r >> gshift) : 0];
@@ -168,136 +229,160 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
             slot = en & 255;
             head = g * G + (ok ? (r & (G - 1)) : 0);
         };
-        auto load_step = [&](int s, BwdPrefetch& pf) {
+        // Step j's rows into ring[j % kBwdRing]: wave w loads rows 16u + 4w .. 16u + 4w + 3
+        // of Q (u = 0, 1) and of dO, one 16-byte chunk per lane, the swizzle applied
+        // through the source chunk; wave 0 then loads the rows' LSE and D.
+        // Every wave issues exactly 4 vector-memory operations here, wave 0 one more.
+        auto issue_step = [&](int j) {
+            BwdRowStage& R = ring[j % kBwdRing];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int idx = tid + 256 * u, rr = idx >> 4, ch = idx & 15;
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 16 * (i & 1) + 4 * wave + (lane >> 4);
                 bool ok;
                 int t, slot, head;
-                row_src(s * kBwdRows + rr, ok, t, slot, head);
-                const size_t a = (((size_t)b * N + t) * Hq + head) * kDim + ch * 8;
-                pf.qv[u] = *(const uint4*)(q + a);
-                pf.dv[u] = *(const uint4*)(d_o + a);
-                if (!ok) pf.qv[u] = pf.dv[u] = make_uint4(0, 0, 0, 0);
+                row_src(j * kBwdRows + rr, ok, t, slot, head);
+                const int ch = (lane & 15) ^ (rr & 7);
+                const __bf16* src = (i >> 1 ? d_o : q) + (((size_t)b * N + t) * Hq + head) * kDim + ch * 8;
+                __bf16* dst = (i >> 1 ? R.d : R.q) + (16 * (i & 1) + 4 * wave) * kDim;
+                __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)dst, 16, 0, 0);
             }
-            {
-                const int which = tid >> 7, u = tid & 127, rg = u >> 4, dc = u & 15;
-                const __bf16* src = which ? d_o : q;
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    bool ok;
-                    int t, slot, head;
-                    row_src(s * kBwdRows + rg * 4 + rr, ok, t, slot, head);
-                    pf.tr[rr] = *(const bf16x8*)(src + (((size_t)b * N + t) * Hq + head) * kDim + dc * 8);
-                    if (!ok)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) pf.tr[rr][e] = (__bf16)0.0f;
-                }
-            }
-            if (tid < kBwdRows) {
+            if (wave == 0) {
                 bool ok;
                 int t, slot, head;
-                row_src(s * kBwdRows + tid, ok, t, slot, head);
-                pf.lse2 = ok ? lse[((size_t)b * Hq + head) * N + t] * log2e : 0.0f;
-                pf.dlt = ok ? delta[((size_t)b * N + t) * Hq + head] : 0.0f;
-                pf.lim = !ok ? -1 : ((t >> 7) == c ? t - c * kBlock : kBlock - 1);
-                pf.rec = ok ? ((b * N + t) * top_k + slot) : -1;
-            }
-        };
-        auto store_step = [&](const BwdPrefetch& pf) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int idx = tid + 256 * u, rr = idx >> 4, ch = idx & 15;
-                *(uint4*)(st.qr + swz_chunk_offset(rr, ch)) = pf.qv[u];
-                *(uint4*)(st.dr + swz_chunk_offset(rr, ch)) = pf.dv[u];
-            }
-            {
-                const int which = tid >> 7, u = tid & 127, rg = u >> 4, dc = u & 15;
-                __bf16* dstT = which ? st.dt : st.qt;
-                const int p0 = tpos(rg * 4);  // rows 4rg .. 4rg+3 sit at p0 .. p0+3
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    bf16x4 w;
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) w[rr] = pf.tr[rr][e];
-                    *(bf16x4*)(dstT + tline_offset(dc * 8 + e, p0 >> 3) + (p0 & 7)) = w;
-                }
-            }
-            if (tid < kBwdRows) {
-                st.lse2[tid] = pf.lse2;
-                st.dlt[tid] = pf.dlt;
-                st.lim[tid] = pf.lim;
-                st.rec[tid] = pf.rec;
+                row_src(j * kBwdRows + l32, ok, t, slot, head);
+                const float* src = h == 0 ? lse + ((size_t)b * Hq + head) * N + t
+                                          : delta + ((size_t)b * N + t) * Hq + head;
+                __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)R.lse, 4, 0, 0);
             }
         };
 
-        BwdPrefetch pf;
-        load_step(0, pf);
-        store_step(pf);
+        // last key offset of the block that row j*32 + tid attends: its own position in its
+        // own block, 127 elsewhere, -1 for rows past the end
+        auto fill_lims = [&](int j) {
+            if (tid < kBwdRows) {
+                bool ok;
+                int t, slot, head;
+                row_src(j * kBwdRows + tid, ok, t, slot, head);
+                lims[j & 1][tid] = !ok ? -1 : ((t >> 7) == c ? t - c * kBlock : kBlock - 1);
+            }
+        };
+
+        const int ahead = min(kBwdRing - 1, nsteps);
+        for (int j = 0; j < ahead; ++j) issue_step(j);
+        fill_lims(0);
+        MSA_WAIT_VMCNT(0);
         __syncthreads();
 
         for (int s = 0; s < nsteps; ++s) {
-            if (s + 1 < nsteps) load_step(s + 1, pf);
+            const bool more = s + kBwdRing - 1 < nsteps;
+            if (more) issue_step(s + kBwdRing - 1);  // (a)
+            if (s + 1 < nsteps) fill_lims(s + 1);
 
-            // S = Q K^T, dP = dO V^T: 32 rows x this wave's 32 keys; register i holds row mfma32_row(i, h)
+            // (c) S = Q K^T, dP = dO V^T: 32 rows x this wave's 32 keys; register i holds row mfma32_row(i, h)
+            const BwdRowStage& R = ring[s % kBwdRing];
+            __bf16* ds_s = dsl[s & 1];
             f32x16 sa, pa;
 #pragma unroll
             for (int i = 0; i < 16; ++i) sa[i] = pa[i] = 0.0f;
+            {
+                // all 16 operand loads in flight before the MFMA chain starts
+                bf16x8 aq[8], ad[8];
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const int o2 = swz_chunk_offset(l32, 2 * kk + h);
-                sa = mfma32(*(const bf16x8*)(st.qr + o2), kf[kk], sa);
-                pa = mfma32(*(const bf16x8*)(st.dr + o2), vf[kk], pa);
+                for (int kk = 0; kk < 8; ++kk) {
+                    const int o2 = ring_off(l32, 2 * kk + h);
+                    aq[kk] = *(const bf16x8*)(R.q + o2);
+                    ad[kk] = *(const bf16x8*)(R.d + o2);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    sa = mfma32(aq[kk], kf[kk], sa);
+                    pa = mfma32(ad[kk], vf[kk], pa);
+                }
             }
-            // P and dS; the rows this lane holds are 8j + 4h + u
             bf16x8 pb[2], db[2];
-            int rec[16];
+            uint32_t dsbits[16];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f32x4 l4 = *(const f32x4*)(st.lse2 + 8 * j + 4 * h);
-                const f32x4 d4 = *(const f32x4*)(st.dlt + 8 * j + 4 * h);
-                const int4 m4 = *(const int4*)(st.lim + 8 * j + 4 * h);
-                const int4 r4 = *(const int4*)(st.rec + 8 * j + 4 * h);
+            for (int j = 0; j < 4; ++j) {  // rows 8j + 4h + u
+                const f32x4 l4 = *(const f32x4*)(R.lse + 8 * j + 4 * h);
+                const f32x4 d4 = *(const f32x4*)(R.dlt + 8 * j + 4 * h);
+                const int4 m4 = *(const int4*)(lims[s & 1] + 8 * j + 4 * h);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int i = 4 * j + u;
                     const int lim = u == 0 ? m4.x : u == 1 ? m4.y : u == 2 ? m4.z : m4.w;
-                    rec[i] = u == 0 ? r4.x : u == 1 ? r4.y : u == 2 ? r4.z : r4.w;
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], scale_log2, -l4[u]));
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], scale_log2, -l4[u] * log2e));
                     if (my_key > lim) p = 0.0f;
                     const __bf16 dsv = (__bf16)(p * (pa[i] - d4[u]));
                     pb[i >> 3][i & 7] = (__bf16)p;
                     db[i >> 3][i & 7] = dsv;
-                    dsl[swz_chunk_offset(mfma32_row(i, h), my_key >> 3) + (my_key & 7)] = dsv;
+                    dsbits[i] = (uint32_t)__builtin_bit_cast(uint16_t, dsv);
                 }
             }
-            // dV += P^T dO, dK += dS^T Q: own keys x 128 dims, k = the 32 rows (in tpos order)
+            store_ds16((uint32_t)(uintptr_t)(lds_ptr)(ds_s + 4 * h * kDsRow + my_key), dsbits,
+                       std::make_integer_sequence<int, 16>{});
+            // (d) dV += P^T dO, dK += dS^T Q: own keys x 128 dims, k = the 32 rows in the order
+            // tpos(16 hs + 8 h + e) of the score registers, i.e. rows 16 hs + 4 h + {0..3} and
+            // 16 hs + 8 + 4 h + {0..3}, read transposed from the row-major stage
 #pragma unroll
-            for (int hs = 0; hs < 2; ++hs)
+            for (int hs = 0; hs < 2; ++hs) {
+                bf16x8 bd[4], bq[4];
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) {
-                    const int o3 = tline_offset(nt * 32 + l32, 2 * hs + h);
-                    dv[nt] = mfma32(pb[hs], *(const bf16x8*)(st.dt + o3), dv[nt]);
-                    dk[nt] = mfma32(db[hs], *(const bf16x8*)(st.qt + o3), dk[nt]);
+                    const int c0 = nt * 32 + 16 * dhalf;
+                    bd[nt] = cat8(tr_rows4(R.d, 16 * hs + 4 * h, c0, li), tr_rows4(R.d, 16 * hs + 8 + 4 * h, c0, li));
+                    bq[nt] = cat8(tr_rows4(R.q, 16 * hs + 4 * h, c0, li), tr_rows4(R.q, 16 * hs + 8 + 4 * h, c0, li));
                 }
-            __syncthreads();  // dS of all keys is in LDS; this step's stage is no longer read
-            if (s + 1 < nsteps) store_step(pf);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    dv[nt] = mfma32(pb[hs], bd[nt], dv[nt]);
+                    dk[nt] = mfma32(db[hs], bq[nt], dk[nt]);
+                }
+            }
+            // (e) step s+1's rows have landed: every memory operation before the loads of steps
+            // s+2 and s+3 (issued in the last two (a) phases) is complete; then the barrier makes
+            // all waves' LDS writes visible
+            {
+                const int per = wave == 0 ? 5 : 4;
+                const int after = (s + kBwdRing - 2 < nsteps && s >= 1 ? per : 0) + (more ? per : 0);
+                if (after == 0) MSA_WAIT_VMCNT(0);
+                else if (after == 4) MSA_WAIT_VMCNT(4);
+                else if (after == 5) MSA_WAIT_VMCNT(5);
+                else if (after == 8) MSA_WAIT_VMCNT(8);
+                else MSA_WAIT_VMCNT(10);
+            }
+            MSA_WAIT_LGKM0();  // this lane's dS stores (not tracked by the compiler) are done
+            lds_barrier();
 
-            // dQ rows (unscaled) for dims 32 wave .. 32 wave + 31: sum over the block's 128 keys
+            // (f) dQ^T rows (unscaled) = K^T dS^T for dims 32 wave .. +31; lane l32 holds row l32
             f32x16 qa;
 #pragma unroll
             for (int i = 0; i < 16; ++i) qa[i] = 0.0f;
+            {
+                bf16x8 bs[8];
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk)
-                qa = mfma32(*(const bf16x8*)(dsl + swz_chunk_offset(l32, 2 * kk + h)), ktf[kk], qa);
-            const int r0 = s * kBwdRows;
+                for (int kk = 0; kk < 8; ++kk) bs[kk] = *(const bf16x8*)(ds_s + l32 * kDsRow + (2 * kk + h) * 8);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (rec[i] < 0) continue;
-                const int head = g * G + ((r0 + mfma32_row(i, h)) & (G - 1));
-                dq_part[((size_t)rec[i] * Hq + head) * kDim + 32 * wave + l32] = qa[i];
+                for (int kk = 0; kk < 8; ++kk) qa = mfma32(ktf[kk], bs[kk], qa);
             }
-            __syncthreads();  // next step's stage is in LDS; dS reads are done
+            {
+                bool ok;
+                int t, slot, head;
+                row_src(s * kBwdRows + l32, ok, t, slot, head);
+                if (ok) {
+                    // chunk-major partial record: [(b*N + t)*top_k + slot][16 chunks][Hq][8 dims]
+                    __bf16* dst = dq_part + ((((size_t)b * N + t) * top_k + slot) * 16 * Hq + head) * 8 + 4 * h;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {  // dims 32 wave + 8 j + 4 h + u = chunk 4 wave + j
+                        bf16x4 w;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) w[u] = (__bf16)qa[4 * j + u];
+                        *(bf16x4*)(dst + (size_t)(4 * wave + j) * Hq * 8) = w;
+                    }
+                }
+            }
         }
 
         // item partials [item][dK, dV][key][dim], fp32; dK carries the softmax scale
@@ -316,8 +401,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
 
 // ---------------------------------------------------------------------------
 // dQ[b, t, h] = scale * sum over the valid slots of the partials; one workgroup per (b, t).
+// A thread takes (chunk, head) pairs, so the reads of one slot's record are contiguous.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_bwd_dq_sum(const float* __restrict__ dq_part,
+__global__ __launch_bounds__(256) void k_bwd_dq_sum(const __bf16* __restrict__ dq_part,
                                                     const int32_t* __restrict__ block_idx, __bf16* __restrict__ dq,
                                                     int N, int Hq, int Hkv, int gshift, int top_k, float scale) {
     extern __shared__ int32_t sel[];  // [Hkv][top_k]
@@ -328,21 +414,25 @@ __global__ __launch_bounds__(256) void k_bwd_dq_sum(const float* __restrict__ dq
         sel[i] = block_idx[(((size_t)b * Hkv + g) * N + t) * top_k + s];
     }
     __syncthreads();
-    const size_t slot_stride = (size_t)Hq * kDim;
-    const float* base = dq_part + (size_t)bt * top_k * slot_stride;
-    for (int u = tid; u < Hq * (kDim / 4); u += 256) {  // 4 dims per unit
-        const int head = u / (kDim / 4), d4 = (u % (kDim / 4)) * 4;
+    const size_t slot_stride = (size_t)16 * Hq * 8;
+    const __bf16* base = dq_part + (size_t)bt * top_k * slot_stride;
+    for (int j = tid; j < Hq * 16; j += 256) {
+        const int chunk = j / Hq, head = j - chunk * Hq;
         const int32_t* sg = sel + (head >> gshift) * top_k;
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
         for (int s = 0; s < top_k; ++s) {
             const int cc = sg[s];
             if (cc < 0 || cc > cl) continue;
-            acc += *(const f32x4*)(base + s * slot_stride + (size_t)head * kDim + d4);
-        }
-        bf16x4 w;
+            const bf16x8 a = *(const bf16x8*)(base + s * slot_stride + (size_t)j * 8);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[e] * scale);
-        *(bf16x4*)(dq + ((size_t)bt * Hq + head) * kDim + d4) = w;
+            for (int e = 0; e < 8; ++e) acc[e] += (float)a[e];
+        }
+        bf16x8 w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = (__bf16)(acc[e] * scale);
+        *(bf16x8*)(dq + ((size_t)bt * Hq + head) * kDim + chunk * 8) = w;
     }
 }
 
@@ -401,7 +491,7 @@ hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const vo
     const float log2e = 1.4426950408889634f;
     hipLaunchKernelGGL(k_bwd_main, dim3(grid), dim3(256), 0, stream, (const __bf16*)q, (const __bf16*)k,
                        (const __bf16*)v, (const __bf16*)d_o, lse, ws.delta, ws.plan.off, ws.plan.item_off,
-                       ws.plan.entries, ws.dq_part, ws.dkv_part, d.N, d.Hq, d.Hkv, d.gshift, d.nblk, d.top_k, n,
+                       ws.plan.entries, (__bf16*)ws.dq_part, ws.dkv_part, d.N, d.Hq, d.Hkv, d.gshift, d.nblk, d.top_k, n,
                        d.scale, d.scale * log2e);
     return hipGetLastError();
 }
@@ -409,7 +499,7 @@ hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const vo
 hipError_t launch_bwd_dq_sum(const int32_t* block_idx, void* dq, const BwdWs& ws, const Dims& d,
                              hipStream_t stream) {
     const size_t lds = (size_t)d.Hkv * d.top_k * sizeof(int32_t);
-    hipLaunchKernelGGL(k_bwd_dq_sum, dim3((unsigned)(d.B * d.N)), dim3(256), lds, stream, ws.dq_part, block_idx,
+    hipLaunchKernelGGL(k_bwd_dq_sum, dim3((unsigned)(d.B * d.N)), dim3(256), lds, stream, (const __bf16*)ws.dq_part, block_idx,
                        (__bf16*)dq, d.N, d.Hq, d.Hkv, d.gshift, d.top_k, d.scale);
     return hipGetLastError();
 }

@@ -109,7 +109,7 @@ SparseWs carve_sparse_ws(void* base, const Dims& d) {
 size_t bwd_ws_bytes(const Dims& d) {
     size_t s = plan_ws_bytes(d);
     s += align_up((size_t)d.B * d.N * d.Hq * 4, 256);                  // delta
-    s += align_up((size_t)d.B * d.N * d.top_k * d.Hq * kDim * 4, 256);  // dq_part
+    s += align_up((size_t)d.B * d.N * d.top_k * d.Hq * kDim * 2, 256);  // dq_part
     s += align_up(bwd_max_items(d) * 2 * kBlock * kDim * 4, 256);       // dkv_part
     return s;
 }
@@ -120,8 +120,8 @@ BwdWs carve_bwd_ws(void* base, const Dims& d) {
     char* p = (char*)base + plan_ws_bytes(d);
     w.delta = (float*)p;
     p += align_up((size_t)d.B * d.N * d.Hq * 4, 256);
-    w.dq_part = (float*)p;
-    p += align_up((size_t)d.B * d.N * d.top_k * d.Hq * kDim * 4, 256);
+    w.dq_part = (void*)p;
+    p += align_up((size_t)d.B * d.N * d.top_k * d.Hq * kDim * 2, 256);
     w.dkv_part = (float*)p;
     return w;
 }

@@ -54,7 +54,7 @@ hipError_t launch_sparse_combine(const int32_t* block_idx, void* o, float* lse, 
 struct BwdWs {
     SparseWs plan;
     float* delta;     // fp32 [B, N, Hq]               rowsum(dO * O)
-    float* dq_part;   // fp32 [B, N, top_k, Hq, 128]   unscaled dQ per (t, slot, head)
+    void* dq_part;    // bf16 [B, N, top_k, 16, Hq, 8] unscaled dQ per (t, slot, head), chunk-major
     float* dkv_part;  // fp32 [items, 2, 128, 128]     dK (scaled), dV per work item
 };
 size_t bwd_max_items(const Dims& d);
