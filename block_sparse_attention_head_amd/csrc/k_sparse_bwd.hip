@@ -12,7 +12,7 @@
 //   dP = dO . v,  dS = P (dP - D),  dV = sum P dO,  dK = scale sum dS q,  dQ = scale sum dS k.
 //
 // Kernels:
-//   k_bwd_delta       D for every (b, t, h) row.
+//   k_bwd_delta       per (b, t, h) row: D and LSE * log2(e).
 //   k_bwd_main        one persistent workgroup per work item (a chunk of the
 //                     rows gathered for one (key block, KV head) tile). Wave w
 //                     owns keys 32w .. 32w+31 of the block and keeps their K, V
@@ -40,10 +40,15 @@ namespace msa {
 __device__ __forceinline__ int tpos(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
 // ---------------------------------------------------------------------------
-// D[row] = sum_d dO[row, d] * O[row, d], row = (b*N + t)*Hq + h; 16 lanes per row.
+// Per-row terms of the main kernel, row = (b*N + t)*Hq + h, two planes of
+// rows + 1 floats: plane 0 holds LSE * log2(e) (the LSE read from its [B, Hq, N]
+// layout), plane 1 holds D = sum_d dO * O. Index `rows` of each plane is a pad
+// row (+inf, 0) that padded step rows load: their P = exp2(-inf) = 0 exactly.
+// 16 lanes per row.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_bwd_delta(const __bf16* __restrict__ o, const __bf16* __restrict__ d_o,
-                                                   float* __restrict__ delta, long long rows) {
+                                                   const float* __restrict__ lse, float* __restrict__ rowterm,
+                                                   int N, int Hq, long long rows) {
     const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
     const int part = threadIdx.x & 15;
     float s = 0.0f;
@@ -55,37 +60,53 @@ __global__ __launch_bounds__(256) void k_bwd_delta(const __bf16* __restrict__ o,
     }
 #pragma unroll
     for (int m = 8; m > 0; m >>= 1) s += __shfl_xor(s, m, 16);
-    if (row < rows && part == 0) delta[row] = s;
+    if (row < rows && part == 0) {
+        const long long bt = row / Hq;
+        const int h = (int)(row - bt * Hq);
+        const long long b = bt / N;
+        const int t = (int)(bt - b * N);
+        rowterm[row] = lse[(b * Hq + h) * N + t] * 1.4426950408889634f;
+        rowterm[rows + 1 + row] = s;
+    }
+    if (row == 0 && part == 0) {
+        rowterm[rows] = __builtin_inff();
+        rowterm[rows + 1 + rows] = 0.0f;
+    }
 }
 
 // ---------------------------------------------------------------------------
 // Fused main backward.
 //
-// Per work item: the lane's own K and V rows go to registers; the block's K
-// tile is staged row-major in LDS once and the lane's K^T fragments (A
-// operands of dQ^T) are read from it with transposing LDS loads. Gathered
-// rows go 32 at a time ("steps") through a ring of kBwdRing row-major LDS
-// stages filled by direct global->LDS loads issued kBwdRing - 1 steps ahead
-// (no registers held while they fly). The transposed Q^T / dO^T operands of
-// dK, dV come from the same row-major stage through ds_read_b64_tr_b16. Step s:
+// One workgroup of 8 waves (two per SIMD) per work item; wave w owns keys
+// 16w .. 16w+15 of the block, keeps their K and V rows as MFMA operands in
+// registers, and accumulates their dK, dV. The block's K tile is staged
+// row-major in LDS once per item and each wave reads its K^T fragments (A
+// operands of dQ^T for dims 16w .. 16w+15) from it with transposing LDS loads.
+// Gathered rows go 32 at a time ("steps") through a ring of kBwdRing row-major
+// LDS stages filled by direct global->LDS loads issued kBwdRing - 1 steps
+// ahead (no registers held while they fly). Step s:
 //   (a) issue the loads of step s+3
-//   (c) S = Q K^T, dP = dO V^T; P, dS (dS -> LDS)
-//   (d) dV += P^T dO, dK += dS^T Q
+//   (c) S = Q K^T, dP = dO V^T (32 rows x 16 keys); P, dS (dS -> LDS)
+//   (d) dV += P^T dO, dK += dS^T Q, with dO^T, Q^T read transposed from the stage
 //   (e) wait for step s+1's loads; barrier
-//   (f) dQ^T rows = K^T dS^T -> bf16 partials
+//   (f) dQ^T (16 dims x 32 rows) = K^T dS^T over the block's 128 keys -> partials
+// All MFMAs are 16x16x32.
 // ---------------------------------------------------------------------------
 constexpr int kBwdRows = 32;                                   // gathered rows per step
 constexpr int kBwdRing = 4;                                    // row-major stages
+constexpr int kBwdWaves = 8;
 constexpr int kBwdMaxItemEntries = kRowTilesPerItem * kBlock;  // entries of one item when G = 1
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(3))) bf16x4* lds_bf16x4_ptr;
 
 // Row-major tiles with 128-element rows filled by global->LDS loads: chunk ch
-// (8 elements) of row r sits at chunk slot ch ^ (r & 7). Eight consecutive rows
-// read at one chunk fall into distinct banks, and most of the per-lane address
-// stays independent of the chunk, so unrolled reads share base registers.
-__device__ __forceinline__ int ring_off(int row, int ch) { return row * kDim + ((ch ^ (row & 7)) << 3); }
+// (8 elements) of row r sits at chunk slot ch ^ rsw(r), rsw(r) = the two 2-bit
+// halves of r & 15 swapped. Sixteen consecutive rows read at one chunk fall on
+// sixteen distinct slots, and the rows x chunks one transposing load covers
+// spread over all sixteen slots.
+__device__ __forceinline__ int rsw(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int ring_off(int row, int ch) { return row * kDim + ((ch ^ rsw(row)) << 3); }
 
 // dS rows [32][128] padded to 136 elements (272 bytes): consecutive rows shift by
 // four banks, and every offset is a per-lane base plus a constant.
@@ -94,7 +115,7 @@ constexpr int kDsRow = kBlock + 8;
 struct BwdRowStage {             // written by global->LDS loads
     __bf16 q[kBwdRows * kDim];   // Q rows [row][dim] (ring_off)
     __bf16 d[kBwdRows * kDim];   // dO rows
-    float lse[kBwdRows];         // LSE of the row (natural log)
+    float lse[kBwdRows];         // LSE * log2(e) of the row (+inf for padding rows)
     float dlt[kBwdRows];         // D of the row; must follow lse
 };
 
@@ -133,35 +154,37 @@ template <int OFF>
 __device__ __forceinline__ void lds_store_b16(uint32_t addr, uint32_t bits) {
     asm volatile("ds_write_b16 %0, %1 offset:%2" ::"v"(addr), "v"(bits), "i"(OFF) : "memory");
 }
-// The 16 dS values of a lane (score register i holds row mfma32_row(i, h)) into
-// padded dS rows: byte address base + row(i, 0) * 2 * kDsRow, base covering the
-// lane's key and its 4h row offset.
+// The 8 dS values of a lane (register 4mt + i holds row 16mt + 4g + i) into
+// padded dS rows: byte address base + (16mt + i) * 2 * kDsRow, base covering the
+// lane's key and its 4g row offset.
 template <int... I>
-__device__ __forceinline__ void store_ds16(uint32_t base, const uint32_t (&bits)[16], std::integer_sequence<int, I...>) {
-    (lds_store_b16<(8 * (I >> 2) + (I & 3)) * 2 * kDsRow>(base, bits[I]), ...);
+__device__ __forceinline__ void store_ds8(uint32_t base, const uint32_t (&bits)[8], std::integer_sequence<int, I...>) {
+    (lds_store_b16<(16 * (I >> 2) + (I & 3)) * 2 * kDsRow>(base, bits[I]), ...);
 }
 
-__global__ __launch_bounds__(256, 1) void k_bwd_main(
+__global__ __launch_bounds__(512, 1) void k_bwd_main(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const __bf16* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
+    const __bf16* __restrict__ d_o, const float* __restrict__ rowterm, long long rows,
     const int32_t* __restrict__ off, const int32_t* __restrict__ item_off, const int32_t* __restrict__ entries,
-    __bf16* __restrict__ dq_part, float* __restrict__ dkv_part, int N, int Hq, int Hkv, int gshift, int nblk,
-    int top_k, int n_tiles, float scale, float scale_log2) {
+    __bf16* __restrict__ dq_part, __bf16* __restrict__ dq_sink, float* __restrict__ dkv_part, int N, int Hq,
+    int Hkv, int gshift, int nblk, int top_k, int n_tiles, float scale, float scale_log2) {
     __shared__ __attribute__((aligned(16))) BwdRowStage ring[kBwdRing];         // also holds the K tile at item start
     __shared__ __attribute__((aligned(16))) __bf16 dsl[2][kBwdRows * kDsRow];  // dS [row][key], padded rows
-    __shared__ int32_t ent[kBwdMaxItemEntries];                                 // this item's (t << 8 | slot)
+    __shared__ int32_t ent_row[kBwdMaxItemEntries];  // per entry: (b*N + t)*Hq + g*G, the row of its first head
+    __shared__ int32_t ent_rec[kBwdMaxItemEntries];  // per entry: (b*N + t)*top_k + slot, its dQ partial record
     __shared__ __attribute__((aligned(16))) int32_t lims[2][kBwdRows];          // per step: last attended key per row
+    __shared__ int32_t diagf[2];                                                // per step: some row is on the diagonal
     static_assert(2 * sizeof(BwdRowStage) >= kBlock * kDim * sizeof(__bf16), "K tile must fit in two stages");
 
-    const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
-    const int li = lane & 15, dhalf = (lane >> 4) & 1;  // 16-lane group: lane in group, which 16 columns
+    const int l16 = lane & 15, g4 = lane >> 4;                   // MFMA lane in its 16-lane group, group
     const int G = 1 << gshift;
     const int P = kBlock >> gshift;
-    const int my_key = wave * 32 + l32;  // key of this lane inside the block
+    const int kw0 = 16 * wave;       // this wave's first key (and first dQ dim)
+    const int my_key = kw0 + l16;    // key of this lane's S column
     const int total_items = item_off[n_tiles];
-    const float log2e = 1.4426950408889634f;
-    __bf16* ktile = ring[0].q;           // K [key][dim] during the item prologue
+    __bf16* ktile = ring[0].q;       // K [key][dim] during the item prologue
 
     for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
         int lo = 0, hi = n_tiles;  // tile = last index with item_off[tile] <= item
@@ -183,87 +206,85 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
         const int kstride = Hkv * kDim;
 
         __syncthreads();  // the previous item's LDS reads are done
-        for (int i = tid; i < ne; i += 256) ent[i] = entries[e0 + rt0 * P + i];
-        // K tile -> LDS (row-major, swizzled through the source chunk): 8 x 4 rows per wave
+        for (int i = tid; i < ne; i += 512) {
+            const int en = entries[e0 + rt0 * P + i], t = en >> 8;
+            ent_row[i] = (b * N + t) * Hq + g * G;
+            ent_rec[i] = (b * N + t) * top_k + (en & 255);
+        }
+        // K tile -> LDS (row-major, swizzled through the source chunk): 4 x 4 rows per wave
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = 16 * i + 4 * wave + (lane >> 4);  // 128 rows over 8 x 4 waves x 4 rows
-            const int ch = (lane & 15) ^ (row & 7);
+        for (int i = 0; i < 4; ++i) {
+            const int row = 32 * i + 4 * wave + (lane >> 4);
+            const int ch = (lane & 15) ^ rsw(row);
             __builtin_amdgcn_global_load_lds((const void*)(k + tile_off + (size_t)row * kstride + ch * 8),
-                                             (lds_ptr)(ktile + (16 * i + 4 * wave) * kDim), 16, 0, 0);
+                                             (lds_ptr)(ktile + (32 * i + 4 * wave) * kDim), 16, 0, 0);
         }
-        // own keys as B operands: lane holds K[my_key][16 kk + 8 h + e], same for V
-        bf16x8 kf[8], vf[8];
+        // own keys as B operands of S, dP: lane holds K[my_key][32 kk + 8 g4 + e], same for V
+        bf16x8 kf[4], vf[4];
         {
-            const size_t krow = tile_off + (size_t)my_key * kstride + 8 * h;
+            const size_t krow = tile_off + (size_t)my_key * kstride + 8 * g4;
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                kf[kk] = *(const bf16x8*)(k + krow + kk * 16);
-                vf[kk] = *(const bf16x8*)(v + krow + kk * 16);
+            for (int kk = 0; kk < 4; ++kk) {
+                kf[kk] = *(const bf16x8*)(k + krow + kk * 32);
+                vf[kk] = *(const bf16x8*)(v + krow + kk * 32);
             }
-            // keep these loop-invariant MFMA operands in accumulation registers (MFMA reads them
-            // from there directly), leaving the vector registers to the step loop
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) asm volatile("" : "+a"(kf[kk]), "+a"(vf[kk]));
         }
-        f32x16 dk[4], dv[4];
+        f32x4 dk[8], dv[8];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) dk[nt][i] = dv[nt][i] = 0.0f;
+            for (int i = 0; i < 4; ++i) dk[nt][i] = dv[nt][i] = 0.0f;
         MSA_WAIT_VMCNT(0);
         __syncthreads();  // ent, K tile
-        // K^T fragments, A operands of dQ^T: lane holds K[16 kk + 8 h + e][32 wave + l32]
-        bf16x8 ktf[8];
+        // K^T fragments, A operands of dQ^T: lane holds K[32 kk + 8 g4 + e][16 wave + l16]
+        bf16x8 ktf[4];
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-            ktf[kk] = cat8(tr_rows4(ktile, 16 * kk + 8 * h, 32 * wave + 16 * dhalf, li),
-                           tr_rows4(ktile, 16 * kk + 8 * h + 4, 32 * wave + 16 * dhalf, li));
+        for (int kk = 0; kk < 4; ++kk)
+            ktf[kk] = cat8(tr_rows4(ktile, 32 * kk + 8 * g4, kw0, l16), tr_rows4(ktile, 32 * kk + 8 * g4 + 4, kw0, l16));
         __syncthreads();  // the K tile is read; the ring may be refilled
 
-        // entry and head of gathered row r of this item (rows past the end read entry 0)
-        auto row_src = [&](int r, bool& ok, int& t, int& slot, int& head) {
+        // Gathered row r of this item: its (b, t, head) row index into Q, dO and the row terms
+        // (rows past the end read entry 0's first row), and its entry
+        auto row_index = [&](int r, bool& ok) -> int {
             ok = r < nrows;
-            const int en = ent[ok ? (r >> gshift) : 0];
-            t = en >> 8;
-            slot = en & 255;
-            head = g * G + (ok ? (r & (G - 1)) : 0);
+            return ok ? ent_row[r >> gshift] + (r & (G - 1)) : ent_row[0];
         };
-        // Step j's rows into ring[j % kBwdRing]: wave w loads rows 16u + 4w .. 16u + 4w + 3
-        // of Q (u = 0, 1) and of dO, one 16-byte chunk per lane, the swizzle applied
-        // through the source chunk; wave 0 then loads the rows' LSE and D.
-        // Every wave issues exactly 4 vector-memory operations here, wave 0 one more.
+        // Step j's rows into ring[j % kBwdRing]: wave w loads rows 4w .. 4w+3 of Q and of
+        // dO, one 16-byte chunk per lane, the swizzle applied through the source chunk;
+        // wave 0 then loads the rows' LSE * log2(e) and D. Every wave issues exactly 2
+        // vector-memory operations here, wave 0 one more.
         auto issue_step = [&](int j) {
             BwdRowStage& R = ring[j % kBwdRing];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rr = 16 * (i & 1) + 4 * wave + (lane >> 4);
-                bool ok;
-                int t, slot, head;
-                row_src(j * kBwdRows + rr, ok, t, slot, head);
-                const int ch = (lane & 15) ^ (rr & 7);
-                const __bf16* src = (i >> 1 ? d_o : q) + (((size_t)b * N + t) * Hq + head) * kDim + ch * 8;
-                __bf16* dst = (i >> 1 ? R.d : R.q) + (16 * (i & 1) + 4 * wave) * kDim;
-                __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)dst, 16, 0, 0);
-            }
+            const int rr = 4 * wave + (lane >> 4);
+            bool ok;
+            const int ri = row_index(j * kBwdRows + rr, ok);
+            const int ch = (lane & 15) ^ rsw(rr);
+            const size_t src = ((size_t)(uint32_t)ri << 7) + ch * 8;
+            __builtin_amdgcn_global_load_lds((const void*)(q + src), (lds_ptr)(R.q + 4 * wave * kDim), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(d_o + src), (lds_ptr)(R.d + 4 * wave * kDim), 16, 0, 0);
             if (wave == 0) {
-                bool ok;
-                int t, slot, head;
-                row_src(j * kBwdRows + l32, ok, t, slot, head);
-                const float* src = h == 0 ? lse + ((size_t)b * Hq + head) * N + t
-                                          : delta + ((size_t)b * N + t) * Hq + head;
-                __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)R.lse, 4, 0, 0);
+                const int ri2 = row_index(j * kBwdRows + (lane & 31), ok);
+                const long long rt2 = ok ? (long long)ri2 : rows;  // padded rows: the pad row
+                __builtin_amdgcn_global_load_lds((const void*)(rowterm + (lane >> 5) * (rows + 1) + rt2),
+                                                 (lds_ptr)R.lse, 4, 0, 0);
             }
         };
-
-        // last key offset of the block that row j*32 + tid attends: its own position in its
-        // own block, 127 elsewhere, -1 for rows past the end
+        // Last key offset of the block that row j*32 + lane attends: its own position when the
+        // row's query lies in this block (the causal diagonal), 127 otherwise (padding rows
+        // need no limit: their P is 0). diagf[j & 1] says whether any row of step j is diagonal.
         auto fill_lims = [&](int j) {
-            if (tid < kBwdRows) {
-                bool ok;
-                int t, slot, head;
-                row_src(j * kBwdRows + tid, ok, t, slot, head);
-                lims[j & 1][tid] = !ok ? -1 : ((t >> 7) == c ? t - c * kBlock : kBlock - 1);
+            if (wave == 0) {
+                int lim = kBlock - 1;
+                if (lane < kBwdRows) {
+                    const int r = j * kBwdRows + lane;
+                    if (r < nrows) {
+                        const int t = ent_row[r >> gshift] / Hq - b * N;
+                        if ((t >> 7) == c) lim = t - c * kBlock;
+                    }
+                    lims[j & 1][lane] = lim;
+                }
+                const uint64_t m = __ballot(lim < kBlock - 1);
+                if (lane == 0) diagf[j & 1] = m != 0ull;
             }
         };
 
@@ -278,123 +299,147 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
             if (more) issue_step(s + kBwdRing - 1);  // (a)
             if (s + 1 < nsteps) fill_lims(s + 1);
 
-            // (c) S = Q K^T, dP = dO V^T: 32 rows x this wave's 32 keys; register i holds row mfma32_row(i, h)
+            // (c) S = Q K^T, dP = dO V^T: 32 rows x this wave's 16 keys;
+            // register 4 mt + i holds row 16 mt + 4 g4 + i, column key my_key
             const BwdRowStage& R = ring[s % kBwdRing];
             __bf16* ds_s = dsl[s & 1];
-            f32x16 sa, pa;
+            f32x4 sa[2], pa[2];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sa[i] = pa[i] = 0.0f;
-            {
-                // all 16 operand loads in flight before the MFMA chain starts
-                bf16x8 aq[8], ad[8];
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    const int o2 = ring_off(l32, 2 * kk + h);
+                for (int i = 0; i < 4; ++i) sa[mt][i] = pa[mt][i] = 0.0f;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                bf16x8 aq[4], ad[4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int o2 = ring_off(16 * mt + l16, 4 * kk + g4);
                     aq[kk] = *(const bf16x8*)(R.q + o2);
                     ad[kk] = *(const bf16x8*)(R.d + o2);
                 }
-                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_sched_barrier(0);  // all operand loads in flight before the MFMAs
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    sa = mfma32(aq[kk], kf[kk], sa);
-                    pa = mfma32(ad[kk], vf[kk], pa);
+                for (int kk = 0; kk < 4; ++kk) {
+                    sa[mt] = mfma16(aq[kk], kf[kk], sa[mt]);
+                    pa[mt] = mfma16(ad[kk], vf[kk], pa[mt]);
                 }
             }
-            bf16x8 pb[2], db[2];
-            uint32_t dsbits[16];
+            float pv[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {  // rows 8j + 4h + u
-                const f32x4 l4 = *(const f32x4*)(R.lse + 8 * j + 4 * h);
-                const f32x4 d4 = *(const f32x4*)(R.dlt + 8 * j + 4 * h);
-                const int4 m4 = *(const int4*)(lims[s & 1] + 8 * j + 4 * h);
+            for (int mt = 0; mt < 2; ++mt) {
+                const f32x4 l4 = *(const f32x4*)(R.lse + 16 * mt + 4 * g4);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int i = 4 * j + u;
-                    const int lim = u == 0 ? m4.x : u == 1 ? m4.y : u == 2 ? m4.z : m4.w;
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], scale_log2, -l4[u] * log2e));
-                    if (my_key > lim) p = 0.0f;
-                    const __bf16 dsv = (__bf16)(p * (pa[i] - d4[u]));
-                    pb[i >> 3][i & 7] = (__bf16)p;
-                    db[i >> 3][i & 7] = dsv;
-                    dsbits[i] = (uint32_t)__builtin_bit_cast(uint16_t, dsv);
+                for (int i = 0; i < 4; ++i)
+                    pv[4 * mt + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[mt][i], scale_log2, -l4[i]));
+            }
+            if (__builtin_amdgcn_readfirstlane(diagf[s & 1])) {  // causal mask on the diagonal rows
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    const int4 m4 = *(const int4*)(lims[s & 1] + 16 * mt + 4 * g4);
+                    if (my_key > m4.x) pv[4 * mt + 0] = 0.0f;
+                    if (my_key > m4.y) pv[4 * mt + 1] = 0.0f;
+                    if (my_key > m4.z) pv[4 * mt + 2] = 0.0f;
+                    if (my_key > m4.w) pv[4 * mt + 3] = 0.0f;
                 }
             }
-            store_ds16((uint32_t)(uintptr_t)(lds_ptr)(ds_s + 4 * h * kDsRow + my_key), dsbits,
-                       std::make_integer_sequence<int, 16>{});
-            // (d) dV += P^T dO, dK += dS^T Q: own keys x 128 dims, k = the 32 rows in the order
-            // tpos(16 hs + 8 h + e) of the score registers, i.e. rows 16 hs + 4 h + {0..3} and
-            // 16 hs + 8 + 4 h + {0..3}, read transposed from the row-major stage
+            // P^T, dS^T as A operands of dV, dK: k index 8 g4 + e is row 4 g4 + e (e < 4)
+            // and row 16 + 4 g4 + e - 4 (e >= 4), exactly the rows this lane holds
+            bf16x8 pb, db;
+            uint32_t dsbits[8];
 #pragma unroll
-            for (int hs = 0; hs < 2; ++hs) {
+            for (int mt = 0; mt < 2; ++mt) {
+                const f32x4 d4 = *(const f32x4*)(R.dlt + 16 * mt + 4 * g4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const __bf16 dsv = (__bf16)(pv[4 * mt + i] * (pa[mt][i] - d4[i]));
+                    pb[4 * mt + i] = (__bf16)pv[4 * mt + i];
+                    db[4 * mt + i] = dsv;
+                    dsbits[4 * mt + i] = (uint32_t)__builtin_bit_cast(uint16_t, dsv);
+                }
+            }
+            store_ds8((uint32_t)(uintptr_t)(lds_ptr)(ds_s + 4 * g4 * kDsRow + my_key), dsbits,
+                      std::make_integer_sequence<int, 8>{});
+            // (d) dV += P^T dO, dK += dS^T Q: own 16 keys x 128 dims; B operands are the rows
+            // 4 g4 .. +3 and 16 + 4 g4 .. +3 of dO / Q at dim 16 nt + l16, read transposed
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
                 bf16x8 bd[4], bq[4];
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
-                    const int c0 = nt * 32 + 16 * dhalf;
-                    bd[nt] = cat8(tr_rows4(R.d, 16 * hs + 4 * h, c0, li), tr_rows4(R.d, 16 * hs + 8 + 4 * h, c0, li));
-                    bq[nt] = cat8(tr_rows4(R.q, 16 * hs + 4 * h, c0, li), tr_rows4(R.q, 16 * hs + 8 + 4 * h, c0, li));
+                for (int n4 = 0; n4 < 4; ++n4) {
+                    const int c0 = 16 * (4 * half + n4);
+                    bd[n4] = cat8(tr_rows4(R.d, 4 * g4, c0, l16), tr_rows4(R.d, 16 + 4 * g4, c0, l16));
+                    bq[n4] = cat8(tr_rows4(R.q, 4 * g4, c0, l16), tr_rows4(R.q, 16 + 4 * g4, c0, l16));
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
-                    dv[nt] = mfma32(pb[hs], bd[nt], dv[nt]);
-                    dk[nt] = mfma32(db[hs], bq[nt], dk[nt]);
+                for (int n4 = 0; n4 < 4; ++n4) {
+                    dv[4 * half + n4] = mfma16(pb, bd[n4], dv[4 * half + n4]);
+                    dk[4 * half + n4] = mfma16(db, bq[n4], dk[4 * half + n4]);
                 }
             }
             // (e) step s+1's rows have landed: every memory operation before the loads of steps
             // s+2 and s+3 (issued in the last two (a) phases) is complete; then the barrier makes
             // all waves' LDS writes visible
+            // Issued after those loads: the loads of (a) of step s-1, the two dQ stores of (f) of
+            // step s-1, the loads of (a) of step s; they may stay in flight. The empty asm keeps the
+            // compiler from sinking any of them below the wait.
+            asm volatile("" ::: "memory");
             {
-                const int per = wave == 0 ? 5 : 4;
-                const int after = (s + kBwdRing - 2 < nsteps && s >= 1 ? per : 0) + (more ? per : 0);
-                if (after == 0) MSA_WAIT_VMCNT(0);
-                else if (after == 4) MSA_WAIT_VMCNT(4);
-                else if (after == 5) MSA_WAIT_VMCNT(5);
-                else if (after == 8) MSA_WAIT_VMCNT(8);
-                else MSA_WAIT_VMCNT(10);
+                const int per = wave == 0 ? 3 : 2;
+                const int after = (s >= 1 && s + kBwdRing - 2 < nsteps ? per : 0) + (s >= 1 ? 2 : 0) + (more ? per : 0);
+                switch (after) {
+                    case 0: MSA_WAIT_VMCNT(0); break;
+                    case 2: MSA_WAIT_VMCNT(2); break;
+                    case 3: MSA_WAIT_VMCNT(3); break;
+                    case 4: MSA_WAIT_VMCNT(4); break;
+                    case 5: MSA_WAIT_VMCNT(5); break;
+                    case 6: MSA_WAIT_VMCNT(6); break;
+                    case 7: MSA_WAIT_VMCNT(7); break;
+                    default: MSA_WAIT_VMCNT(8); break;
+                }
             }
             MSA_WAIT_LGKM0();  // this lane's dS stores (not tracked by the compiler) are done
             lds_barrier();
 
-            // (f) dQ^T rows (unscaled) = K^T dS^T for dims 32 wave .. +31; lane l32 holds row l32
-            f32x16 qa;
+            // (f) dQ^T (unscaled) = K^T dS^T for dims 16 wave .. +15 and the 32 rows;
+            // register i holds dim 16 wave + 4 g4 + i of row 16 rt + l16
 #pragma unroll
-            for (int i = 0; i < 16; ++i) qa[i] = 0.0f;
-            {
-                bf16x8 bs[8];
+            for (int rt = 0; rt < 2; ++rt) {
+                f32x4 qa = {0.0f, 0.0f, 0.0f, 0.0f};
+                bf16x8 bs[4];
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) bs[kk] = *(const bf16x8*)(ds_s + l32 * kDsRow + (2 * kk + h) * 8);
+                for (int kk = 0; kk < 4; ++kk)
+                    bs[kk] = *(const bf16x8*)(ds_s + (16 * rt + l16) * kDsRow + 32 * kk + 8 * g4);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) qa = mfma32(ktf[kk], bs[kk], qa);
-            }
-            {
-                bool ok;
-                int t, slot, head;
-                row_src(s * kBwdRows + l32, ok, t, slot, head);
-                if (ok) {
-                    // chunk-major partial record: [(b*N + t)*top_k + slot][16 chunks][Hq][8 dims]
-                    __bf16* dst = dq_part + ((((size_t)b * N + t) * top_k + slot) * 16 * Hq + head) * 8 + 4 * h;
+                for (int kk = 0; kk < 4; ++kk) qa = mfma16(ktf[kk], bs[kk], qa);
+                // chunk-major partial record: [(b*N + t)*top_k + slot][16 chunks][Hq][8 dims]. Rows
+                // past the end store to the sink, so every step issues exactly two stores per lane
+                // and the vmcnt accounting above stays exact.
+                const int r = s * kBwdRows + 16 * rt + l16;
+                const int dim = kw0 + 4 * g4;
+                const int head = g * G + (r & (G - 1));
+                __bf16* dst = r < nrows ? dq_part + ((size_t)ent_rec[r >> gshift] * 16 + (dim >> 3)) * Hq * 8 +
+                                              head * 8 + (dim & 7)
+                                        : dq_sink;
+                bf16x4 w4;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {  // dims 32 wave + 8 j + 4 h + u = chunk 4 wave + j
-                        bf16x4 w;
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) w[u] = (__bf16)qa[4 * j + u];
-                        *(bf16x4*)(dst + (size_t)(4 * wave + j) * Hq * 8) = w;
-                    }
-                }
+                for (int i = 0; i < 4; ++i) w4[i] = (__bf16)qa[i];
+                *(bf16x4*)dst = w4;
             }
         }
 
-        // item partials [item][dK, dV][key][dim], fp32; dK carries the softmax scale
+        // item partials [item][dK, dV][key][dim], fp32; dK carries the softmax scale;
+        // register i of tile nt holds key kw0 + 4 g4 + i, dim 16 nt + l16
         float* pk = dkv_part + (size_t)item * 2 * kBlock * kDim;
-        float* pv = pk + (size_t)kBlock * kDim;
+        float* pv2 = pk + (size_t)kBlock * kDim;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = wave * 32 + mfma32_row(i, h), dim = nt * 32 + l32;
+            for (int i = 0; i < 4; ++i) {
+                const int key = kw0 + 4 * g4 + i, dim = 16 * nt + l16;
                 pk[key * kDim + dim] = dk[nt][i] * scale;
-                pv[key * kDim + dim] = dv[nt][i];
+                pv2[key * kDim + dim] = dv[nt][i];
             }
     }
 }
@@ -477,21 +522,24 @@ size_t bwd_max_items(const Dims& d) {
     return (entries + per_item - 1) / per_item + (size_t)d.B * d.Hkv * d.nblk;
 }
 
-hipError_t launch_bwd_delta(const void* o, const void* d_o, float* delta, const Dims& d, hipStream_t stream) {
+hipError_t launch_bwd_delta(const void* o, const void* d_o, const float* lse, float* rowterm, const Dims& d,
+                            hipStream_t stream) {
     const long long rows = (long long)d.B * d.N * d.Hq;
     hipLaunchKernelGGL(k_bwd_delta, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, (const __bf16*)o,
-                       (const __bf16*)d_o, delta, rows);
+                       (const __bf16*)d_o, lse, rowterm, d.N, d.Hq, rows);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* d_o, const float* lse,
-                           const BwdWs& ws, const Dims& d, hipStream_t stream) {
+hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* d_o, const BwdWs& ws,
+                           const Dims& d, hipStream_t stream) {
     const int n = d.B * d.Hkv * d.nblk;
     const int grid = device_cu_count();
     const float log2e = 1.4426950408889634f;
-    hipLaunchKernelGGL(k_bwd_main, dim3(grid), dim3(256), 0, stream, (const __bf16*)q, (const __bf16*)k,
-                       (const __bf16*)v, (const __bf16*)d_o, lse, ws.delta, ws.plan.off, ws.plan.item_off,
-                       ws.plan.entries, (__bf16*)ws.dq_part, ws.dkv_part, d.N, d.Hq, d.Hkv, d.gshift, d.nblk, d.top_k, n,
+    hipLaunchKernelGGL(k_bwd_main, dim3(grid), dim3(512), 0, stream, (const __bf16*)q, (const __bf16*)k,
+                       (const __bf16*)v, (const __bf16*)d_o, ws.rowterm, (long long)d.B * d.N * d.Hq, ws.plan.off,
+                       ws.plan.item_off,
+                       ws.plan.entries, (__bf16*)ws.dq_part,
+                       (__bf16*)ws.dq_part + (size_t)d.B * d.N * d.top_k * d.Hq * kDim, ws.dkv_part, d.N, d.Hq, d.Hkv, d.gshift, d.nblk, d.top_k, n,
                        d.scale, d.scale * log2e);
     return hipGetLastError();
 }

@@ -108,8 +108,8 @@ SparseWs carve_sparse_ws(void* base, const Dims& d) {
 
 size_t bwd_ws_bytes(const Dims& d) {
     size_t s = plan_ws_bytes(d);
-    s += align_up((size_t)d.B * d.N * d.Hq * 4, 256);                  // delta
-    s += align_up((size_t)d.B * d.N * d.top_k * d.Hq * kDim * 2, 256);  // dq_part
+    s += align_up(((size_t)d.B * d.N * d.Hq + 1) * 2 * 4, 256);        // rowterm
+    s += align_up((size_t)d.B * d.N * d.top_k * d.Hq * kDim * 2 + 256, 256);  // dq_part + store sink
     s += align_up(bwd_max_items(d) * 2 * kBlock * kDim * 4, 256);       // dkv_part
     return s;
 }
@@ -118,10 +118,10 @@ BwdWs carve_bwd_ws(void* base, const Dims& d) {
     BwdWs w;
     w.plan = carve_plan_ws(base, d);
     char* p = (char*)base + plan_ws_bytes(d);
-    w.delta = (float*)p;
-    p += align_up((size_t)d.B * d.N * d.Hq * 4, 256);
+    w.rowterm = (float*)p;
+    p += align_up(((size_t)d.B * d.N * d.Hq + 1) * 2 * 4, 256);
     w.dq_part = (void*)p;
-    p += align_up((size_t)d.B * d.N * d.top_k * d.Hq * kDim * 2, 256);
+    p += align_up((size_t)d.B * d.N * d.top_k * d.Hq * kDim * 2 + 256, 256);
     w.dkv_part = (float*)p;
     return w;
 }
@@ -279,12 +279,14 @@ msa_status msa_sparse_attn_bwd(const msa_shape* shape, const void* q, const void
     const msa_status st = check_shape(shape, &d);
     if (st != MSA_OK) return st;
     if (!q || !k || !v || !o || !lse || !d_o || !block_idx || !dq || !dk || !dv) return MSA_ERR_INVALID_ARG;
+    // the backward indexes query rows (b, t, h) with 32-bit integers
+    if ((double)d.B * d.N * d.Hq >= 2147483647.0) return MSA_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < ws_bytes(d, MSA_OP_SPARSE_ATTN_BWD)) return MSA_ERR_WORKSPACE;
     (void)hipGetLastError();
     const BwdWs ws = carve_bwd_ws(workspace, d);
     hipError_t e = launch_sparse_plan(block_idx, ws.plan, d, stream);
-    if (e == hipSuccess) e = launch_bwd_delta(o, d_o, ws.delta, d, stream);
-    if (e == hipSuccess) e = launch_bwd_main(q, k, v, d_o, lse, ws, d, stream);
+    if (e == hipSuccess) e = launch_bwd_delta(o, d_o, lse, ws.rowterm, d, stream);
+    if (e == hipSuccess) e = launch_bwd_main(q, k, v, d_o, ws, d, stream);
     if (e == hipSuccess) e = launch_bwd_dq_sum(block_idx, dq, ws, d, stream);
     if (e == hipSuccess) e = launch_bwd_dkdv_reduce(dk, dv, ws, d, stream);
     return hip_status(e);

@@ -21,6 +21,14 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x32_bf16. Operand layouts (checked on the device):
+//   A (16 x 32): lane l holds A[l % 16][8 * (l / 16) + e], e = 0..7
+//   B (32 x 16): lane l holds B[8 * (l / 16) + e][l % 16]
+//   D (16 x 16): lane l, register i holds D[4 * (l / 16) + i][l % 16]
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // Row of the 32x32 MFMA result held by lane-half `h` in register `i`.
 __device__ __forceinline__ int mfma32_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 

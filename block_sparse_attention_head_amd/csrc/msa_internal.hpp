@@ -53,17 +53,19 @@ hipError_t launch_sparse_combine(const int32_t* block_idx, void* o, float* lse, 
 // and work items, part_o / part_lse unused) followed by the backward's buffers.
 struct BwdWs {
     SparseWs plan;
-    float* delta;     // fp32 [B, N, Hq]               rowsum(dO * O)
-    void* dq_part;    // bf16 [B, N, top_k, 16, Hq, 8] unscaled dQ per (t, slot, head), chunk-major
+    float* rowterm;   // fp32 [2][B*N*Hq + 1]          LSE*log2(e), then D = rowsum(dO * O); + a pad row
+    void* dq_part;    // bf16 [B, N, top_k, 16, Hq, 8] unscaled dQ per (t, slot, head), chunk-major,
+                      // then a 256-byte sink for stores of padding rows
     float* dkv_part;  // fp32 [items, 2, 128, 128]     dK (scaled), dV per work item
 };
 size_t bwd_max_items(const Dims& d);
 size_t bwd_ws_bytes(const Dims& d);
 BwdWs carve_bwd_ws(void* base, const Dims& d);
 
-hipError_t launch_bwd_delta(const void* o, const void* d_o, float* delta, const Dims& d, hipStream_t stream);
-hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* d_o, const float* lse,
-                           const BwdWs& ws, const Dims& d, hipStream_t stream);
+hipError_t launch_bwd_delta(const void* o, const void* d_o, const float* lse, float* rowterm, const Dims& d,
+                            hipStream_t stream);
+hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* d_o, const BwdWs& ws,
+                           const Dims& d, hipStream_t stream);
 hipError_t launch_bwd_dq_sum(const int32_t* block_idx, void* dq, const BwdWs& ws, const Dims& d,
                              hipStream_t stream);
 hipError_t launch_bwd_dkdv_reduce(void* dk, void* dv, const BwdWs& ws, const Dims& d, hipStream_t stream);

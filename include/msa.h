@@ -176,7 +176,7 @@ msa_status msa_fwd(const msa_shape* shape, const void* q_idx, const void* k_idx,
  * their products, as in the forward). Per-slot dQ partials and per-task dK/dV
  * partials in the workspace (MSA_OP_SPARSE_ATTN_BWD) are summed by separate
  * passes: deterministic, no floating-point atomics. Rows with no valid entry
- * get dq = 0. */
+ * get dq = 0. Also needs batch * seqlen * h_q < 2^31 (else MSA_ERR_UNSUPPORTED). */
 msa_status msa_sparse_attn_bwd(const msa_shape* shape, const void* q, const void* k, const void* v,
                                const void* o, const float* lse, const void* d_o,
                                const int32_t* block_idx, void* dq, void* dk, void* dv,
