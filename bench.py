@@ -8,7 +8,9 @@ already resident in HBM when the timed region starts; each stage is bracketed
 by HIP events on the stream the library launches on.
 
 Prints ONE JSON line (rank 0): the contract fields, the roofline of the
-dominant kernel, per-stage figures and the CPU oracle baseline.
+dominant kernel, per-stage figures, the CPU oracle baseline, and (unless
+--no-backward) a "backward" object: msa_sparse_attn_bwd timed at the
+64K-token training shape.
 
     python bench.py [--steps K] [--warmup W] [--workload n128k] [--gpus 1]
 """
@@ -92,6 +94,54 @@ def cpu_baseline(w, x, budget_s: float, seed: int = 7):
     }
 
 
+def backward_report(w, steps: int, warmup: int):
+    """Time msa_sparse_attn_bwd (dQ, dK, dV over the forward's cached block indices) with HIP events."""
+    import torch
+
+    from block_sparse_attention_head_amd import msa
+    from block_sparse_attention_head_amd import perfmodel as P
+    from synth.msa_inputs import make_inputs
+
+    dev = torch.device("cuda:0")
+    print(f"[bench] backward: generating {w.name} inputs", file=sys.stderr, flush=True)
+    xg = {k: v.to(dev) for k, v in make_inputs(w.replace(with_grad=True)).items()}
+    B, N, Hq, Hkv, K = w.batch, w.seqlen, w.h_q, w.h_kv, w.top_k
+    block_idx, o, lse = msa.msa_fwd(xg["q_idx"], xg["k_idx"], xg["q"], xg["k"], xg["v"], K, w.softmax_scale)
+    shape = msa.make_shape(B, N, Hq, Hkv, K, w.softmax_scale)
+    ws = msa.alloc_workspace(shape, msa.OP_SPARSE_ATTN_BWD, dev)
+    dq, dk, dv = torch.empty_like(xg["q"]), torch.empty_like(xg["k"]), torch.empty_like(xg["v"])
+
+    def bwd():
+        msa.sparse_attn_bwd(xg["q"], xg["k"], xg["v"], o, lse, xg["d_o"], block_idx, w.softmax_scale, dq, dk, dv,
+                            ws)
+
+    def fwd():
+        msa.msa_fwd(xg["q_idx"], xg["k_idx"], xg["q"], xg["k"], xg["v"], K, w.softmax_scale, block_idx, o, lse)
+
+    res = {}
+    for name, fn in (("bwd", bwd), ("fwd", fwd)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps
+    s = P.Shape(B, N, Hq, Hkv, K)
+    tf = P.bwd_flops(s) / 1e12 / (res["bwd"] / 1e3)
+    del xg, ws, dq, dk, dv, block_idx, o, lse
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "config": {"batch": B, "seqlen": N, "h_q": Hq, "h_kv": Hkv, "top_k": K},
+            "what": "msa_sparse_attn_bwd: dQ, dK, dV of the main branch over the forward's block indices",
+            "ms": round(res["bwd"], 4), "tokens_s": round(B * N / (res["bwd"] / 1e3), 1),
+            "tflops": round(tf, 2), "frac_of_bf16_peak": round(tf / P.PEAK_BF16_TFLOPS, 4),
+            "algorithmic_tflop": round(P.bwd_flops(s) / 1e12, 4),
+            "fwd_ms_same_shape": round(res["fwd"], 4)}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,6 +150,11 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="n128k")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward measurement at the 64K-token training shape")
+    ap.add_argument("--backward-workload", default="n64k_train")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only the backward measurement (a JSON line with the backward object), for profiling")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one plain 1 GiB device-to-device copy (counter calibration)")
     a = ap.parse_args(argv)
@@ -119,6 +174,9 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 3
+    if a.backward_only:
+        print(json.dumps({"backward": backward_report(WORKLOADS[a.backward_workload], a.steps, a.warmup)}), flush=True)
+        return 0
     w = WORKLOADS[a.workload]
     dev = torch.device("cuda:0")
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
@@ -233,6 +291,8 @@ def main(argv=None) -> int:
     }
     del xg, pooled, block_idx, o, lse, ws
     torch.cuda.empty_cache()
+    if not a.no_backward:
+        out["backward"] = backward_report(WORKLOADS[a.backward_workload], a.steps, a.warmup)
     if not a.no_cpu_baseline:
         print(f"[bench] CPU oracle baseline (~{a.cpu_budget:.0f} s)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, x, a.cpu_budget)

@@ -88,6 +88,12 @@ def main_flops(s: Shape) -> float:
     return 4.0 * s.head_dim * s.h_q * s.batch * sum_attended_keys(s.seqlen, s.top_k, s.block)
 
 
+def bwd_flops(s: Shape) -> float:
+    """Backward of the main branch over cached indices: five 2*d products per (query head,
+    attended key) -- S recomputed, dP, dV, dK, dQ -- i.e. 2.5 x the forward's two."""
+    return 10.0 * s.head_dim * s.h_q * s.batch * sum_attended_keys(s.seqlen, s.top_k, s.block)
+
+
 def index_bytes(s: Shape) -> float:
     visible = s.batch * s.hidx * sum(min(s.block, s.seqlen - c * s.block) * (c + 1) for c in range(s.nblk))
     return (s.batch * s.seqlen * s.hidx * s.idx_dim * BF16 + s.batch * s.seqlen * s.idx_dim * BF16

@@ -37,4 +37,5 @@ def test_flops_of_the_128k_workload():
     assert P.index_flops(s) == pytest.approx(8.796e12, rel=1e-3)
     brute_keys = sum(128 * (min(16, t // 128 + 1) - 1) + t % 128 + 1 for t in range(0, 131072))
     assert P.main_flops(s) == 4 * 128 * 64 * brute_keys
+    assert P.bwd_flops(s) == 2.5 * P.main_flops(s)
     assert P.pair_rows(s) == 4 * 16 * sum(min(16, t // 128 + 1) for t in range(131072))
