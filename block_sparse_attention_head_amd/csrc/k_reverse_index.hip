@@ -19,6 +19,11 @@
 //   scatter: each range writes its entries from its own offsets, ranking equal
 //            tiles inside a chunk by thread index (no atomics decide a slot).
 // Bins beyond the LDS capacity are handled in chunks of kRevLdsBins tiles.
+//
+// The forward does not need that order (every query row of a tile is computed
+// on its own, so its results do not depend on where the row sits), and uses a
+// cheaper unordered scatter: each range reserves one sub-range per touched tile
+// with a single global atomic and hands out places from LDS counters.
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 
@@ -71,7 +76,8 @@ __global__ __launch_bounds__(kRevThreads) void k_rev_count(const int32_t* __rest
 
 // One workgroup: exclusive scans of the tile counts and of the work items per tile.
 __global__ __launch_bounds__(1024) void k_rev_scan(const int32_t* __restrict__ cnt, int32_t* __restrict__ off,
-                                                   int32_t* __restrict__ item_off, int n, int pos_per_tile) {
+                                                   int32_t* __restrict__ item_off, int32_t* __restrict__ cursor, int n,
+                                                   int pos_per_tile) {
     __shared__ int32_t s_a[1024];
     __shared__ int32_t s_b[1024];
     const int tid = threadIdx.x;
@@ -100,6 +106,7 @@ __global__ __launch_bounds__(1024) void k_rev_scan(const int32_t* __restrict__ c
         const int c = cnt[i];
         const int rt = (c + pos_per_tile - 1) / pos_per_tile;
         off[i] = ra;
+        cursor[i] = ra;
         item_off[i] = rb;
         ra += c;
         rb += (rt + kRowTilesPerItem - 1) / kRowTilesPerItem;
@@ -169,18 +176,63 @@ __global__ __launch_bounds__(kRevThreads) void k_rev_scatter(const int32_t* __re
     }
 }
 
-hipError_t launch_sparse_plan(const int32_t* block_idx, const SparseWs& ws, const Dims& d, hipStream_t stream) {
+// Unordered scatter (forward): places inside a tile come from atomics.
+__global__ __launch_bounds__(kRevThreads) void k_rev_scatter_any(const int32_t* __restrict__ block_idx,
+                                                                 int32_t* __restrict__ cursor,
+                                                                 int32_t* __restrict__ entries, int N, int nblk,
+                                                                 int top_k, int ppw) {
+    __shared__ int32_t bins[kRevLdsBins];
+    const bool use_lds = nblk <= kRevLdsBins;
+    const int bg = blockIdx.y, w = blockIdx.x;
+    const int t0 = w * ppw, t1 = min(N, t0 + ppw);
+    int32_t* cur = cursor + (size_t)bg * nblk;
+    if (use_lds) {
+        for (int i = threadIdx.x; i < nblk; i += kRevThreads) bins[i] = 0;
+        __syncthreads();
+        for (int t = t0 + threadIdx.x; t < t1; t += kRevThreads) {
+            const int32_t* row = block_idx + ((size_t)bg * N + t) * top_k;
+            for (int s = 0; s < top_k; ++s) {
+                const int c = row[s];
+                if (valid_entry(c, t)) atomicAdd(&bins[c], 1);
+            }
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < nblk; i += kRevThreads) {
+            const int n = bins[i];
+            bins[i] = n ? atomicAdd(&cur[i], n) : 0;
+        }
+        __syncthreads();
+    }
+    for (int t = t0 + threadIdx.x; t < t1; t += kRevThreads) {
+        const int32_t* row = block_idx + ((size_t)bg * N + t) * top_k;
+        for (int s = 0; s < top_k; ++s) {
+            const int c = row[s];
+            if (!valid_entry(c, t)) continue;
+            const int p = use_lds ? atomicAdd(&bins[c], 1) : atomicAdd(&cur[c], 1);
+            entries[p] = (t << 8) | s;
+        }
+    }
+}
+
+hipError_t launch_sparse_plan(const int32_t* block_idx, const SparseWs& ws, const Dims& d, bool canonical,
+                              hipStream_t stream) {
     const int n = d.B * d.Hkv * d.nblk;
     const int ppw = rev_positions_per_group(d.N), nwg = rev_groups(d.N);
     hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, stream, ws.cnt, 0, (long long)n);
     const dim3 rgrid(nwg, d.B * d.Hkv);
     hipLaunchKernelGGL(k_rev_count, rgrid, dim3(kRevThreads), 0, stream, block_idx, ws.cnt, ws.wgoff, d.N, d.nblk,
                        d.top_k, ppw);
-    hipLaunchKernelGGL(k_rev_scan, dim3(1), dim3(1024), 0, stream, ws.cnt, ws.off, ws.item_off, n,
+    hipLaunchKernelGGL(k_rev_scan, dim3(1), dim3(1024), 0, stream, ws.cnt, ws.off, ws.item_off, ws.cursor, n,
                        kBlock >> d.gshift);
-    hipLaunchKernelGGL(k_rev_wgoff, dim3((n + 255) / 256), dim3(256), 0, stream, ws.off, ws.wgoff, n, d.nblk, nwg);
-    hipLaunchKernelGGL(k_rev_scatter, rgrid, dim3(kRevThreads), 0, stream, block_idx, ws.wgoff, ws.entries, d.N,
-                       d.nblk, d.top_k, ppw);
+    if (canonical) {
+        hipLaunchKernelGGL(k_rev_wgoff, dim3((n + 255) / 256), dim3(256), 0, stream, ws.off, ws.wgoff, n, d.nblk,
+                           nwg);
+        hipLaunchKernelGGL(k_rev_scatter, rgrid, dim3(kRevThreads), 0, stream, block_idx, ws.wgoff, ws.entries, d.N,
+                           d.nblk, d.top_k, ppw);
+    } else {
+        hipLaunchKernelGGL(k_rev_scatter_any, rgrid, dim3(kRevThreads), 0, stream, block_idx, ws.cursor, ws.entries,
+                           d.N, d.nblk, d.top_k, ppw);
+    }
     return hipGetLastError();
 }
 

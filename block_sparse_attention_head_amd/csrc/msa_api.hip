@@ -61,7 +61,7 @@ msa_status check_shape(const msa_shape* s, Dims* d) {
 
 namespace {
 
-// Reverse index and work list (cnt, off, item_off, wgoff, entries): the common
+// Reverse index and work list (cnt, off, item_off, cursor, wgoff, entries): the common
 // prefix of the forward and backward workspaces.
 size_t plan_ws_bytes(const Dims& d) {
     const size_t n = (size_t)d.B * d.Hkv * d.nblk;
@@ -69,6 +69,7 @@ size_t plan_ws_bytes(const Dims& d) {
     s += align_up(n * 4, 256);                                    // cnt
     s += align_up((n + 1) * 4, 256);                              // off
     s += align_up((n + 1) * 4, 256);                              // item_off
+    s += align_up(n * 4, 256);                                    // cursor
     s += align_up(n * rev_groups(d.N) * 4, 256);                  // wgoff
     s += align_up((size_t)d.B * d.Hkv * d.N * d.top_k * 4, 256);  // entries
     return s;
@@ -81,6 +82,7 @@ SparseWs carve_plan_ws(void* base, const Dims& d) {
     w.cnt = (int32_t*)p;      p += align_up(n * 4, 256);
     w.off = (int32_t*)p;      p += align_up((n + 1) * 4, 256);
     w.item_off = (int32_t*)p; p += align_up((n + 1) * 4, 256);
+    w.cursor = (int32_t*)p;   p += align_up(n * 4, 256);
     w.wgoff = (int32_t*)p;    p += align_up(n * rev_groups(d.N) * 4, 256);
     w.entries = (int32_t*)p;
     w.part_o = nullptr;
@@ -209,7 +211,7 @@ msa_status msa_sparse_attn_fwd(const msa_shape* shape, const void* q, const void
     if (!workspace || workspace_bytes < need) return MSA_ERR_WORKSPACE;
     (void)hipGetLastError();
     const SparseWs ws = carve_sparse_ws(workspace, d);
-    hipError_t e = launch_sparse_plan(block_idx, ws, d, stream);
+    hipError_t e = launch_sparse_plan(block_idx, ws, d, false, stream);
     if (e == hipSuccess) e = launch_sparse_partial(q, k, v, ws, d, stream);
     if (e == hipSuccess) e = launch_sparse_combine(block_idx, o, lse, ws, d, stream);
     return hip_status(e);
@@ -223,7 +225,7 @@ msa_status msa_sparse_attn_plan(const msa_shape* shape, const int32_t* block_idx
     if (!block_idx) return MSA_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < ws_bytes(d, MSA_OP_SPARSE_ATTN_FWD)) return MSA_ERR_WORKSPACE;
     (void)hipGetLastError();
-    return hip_status(launch_sparse_plan(block_idx, carve_sparse_ws(workspace, d), d, stream));
+    return hip_status(launch_sparse_plan(block_idx, carve_sparse_ws(workspace, d), d, false, stream));
 }
 
 msa_status msa_sparse_attn_partial(const msa_shape* shape, const void* q, const void* k, const void* v,
@@ -266,7 +268,7 @@ msa_status msa_fwd(const msa_shape* shape, const void* q_idx, const void* k_idx,
     e = launch_block_topk(pooled, block_idx, d, stream);
     if (e != hipSuccess) return MSA_ERR_HIP;
     const SparseWs ws = carve_sparse_ws(rest, d);
-    e = launch_sparse_plan(block_idx, ws, d, stream);
+    e = launch_sparse_plan(block_idx, ws, d, false, stream);
     if (e == hipSuccess) e = launch_sparse_partial(q, k, v, ws, d, stream);
     if (e == hipSuccess) e = launch_sparse_combine(block_idx, o, lse, ws, d, stream);
     return hip_status(e);
@@ -284,7 +286,7 @@ msa_status msa_sparse_attn_bwd(const msa_shape* shape, const void* q, const void
     if (!workspace || workspace_bytes < ws_bytes(d, MSA_OP_SPARSE_ATTN_BWD)) return MSA_ERR_WORKSPACE;
     (void)hipGetLastError();
     const BwdWs ws = carve_bwd_ws(workspace, d);
-    hipError_t e = launch_sparse_plan(block_idx, ws.plan, d, stream);
+    hipError_t e = launch_sparse_plan(block_idx, ws.plan, d, true, stream);
     if (e == hipSuccess) e = launch_bwd_delta(o, d_o, lse, ws.rowterm, d, stream);
     if (e == hipSuccess) e = launch_bwd_main(q, k, v, d_o, ws, d, stream);
     if (e == hipSuccess) e = launch_bwd_dq_sum(block_idx, dq, ws, d, stream);

@@ -31,6 +31,7 @@ struct SparseWs {
     int32_t* cnt;       // [B*Hkv*nblk]    queries per (b, g, c) tile
     int32_t* off;       // [B*Hkv*nblk+1]  exclusive prefix of cnt
     int32_t* item_off;  // [B*Hkv*nblk+1]  exclusive prefix of work items per tile
+    int32_t* cursor;    // [B*Hkv*nblk]    next free place per tile (unordered scatter)
     int32_t* wgoff;     // [B*Hkv, rev_groups(N), nblk] per position range: entries, then first entry
     int32_t* entries;   // [B*Hkv*N*top_k] (t << 8 | slot), grouped by tile
     void* part_o;       // bf16 [B, N, top_k, Hq, 128] normalised partial outputs (lane order)
@@ -41,7 +42,10 @@ int rev_groups(int N);
 size_t sparse_ws_bytes(const Dims& d);
 SparseWs carve_sparse_ws(void* base, const Dims& d);
 
-hipError_t launch_sparse_plan(const int32_t* block_idx, const SparseWs& ws, const Dims& d, hipStream_t stream);
+// Reverse index and work list. `canonical`: the entry order inside a tile is a
+// function of block_idx alone (the backward needs it); otherwise it is unordered.
+hipError_t launch_sparse_plan(const int32_t* block_idx, const SparseWs& ws, const Dims& d, bool canonical,
+                              hipStream_t stream);
 hipError_t launch_sparse_partial(const void* q, const void* k, const void* v, const SparseWs& ws, const Dims& d,
                                  hipStream_t stream);
 // Dynamic LDS bytes of the combine kernel (must stay within 64 KB).
