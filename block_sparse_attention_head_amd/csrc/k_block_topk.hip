@@ -11,67 +11,24 @@
 // so one unsigned compare orders by (score desc, block asc) and keys are
 // unique. Steps:
 //   1. each lane takes the max key of its strided share of the row;
-//   2. a bitonic sort of the 64 lane maxima across the wave gives T, the
-//      need-th largest of them (need = top_k - 1). At least `need` keys are
-//      >= T, so T is a lower bound on the need-th largest key of the row, and
-//      only lanes whose max is >= T (exactly `need` of them) hold keys >= T;
+//   2. T, the need-th largest of the 64 lane maxima (need = top_k - 1), bounds
+//      the need-th largest key of the row from below (at least `need` keys are
+//      >= T), and only the lanes whose max is >= T hold keys >= T;
 //   3. the keys >= T are compacted into an LDS list with wave ballots (at most
 //      need * ceil(c_loc / 64) entries);
 //   4. each listed key is ranked by counting larger listed keys; ranks below
 //      `need` are the selection;
 //   5. the chosen blocks are put in ascending order, the local block last.
+// Rows of up to 1025 blocks keep their scores in registers and work on 32-bit
+// score keys first (msa_topk.hpp); longer rows use k_block_topk below.
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
+#include "msa_topk.hpp"
 
 namespace msa {
 
 constexpr int kTopkWaves = 4;
 constexpr int kTopkCap = 1024;  // LDS candidate slots per wave (plus 4 of padding)
-
-// Rank of `mine` among list[0..n4): how many listed keys are larger. n4 is a multiple
-// of 4 and list[n..n4) holds zero keys, below every real key. Four keys per step
-// with two 16-byte broadcast reads.
-__device__ __forceinline__ int rank_in_list(const uint64_t* list, int n4, uint64_t mine) {
-    int r = 0;
-    for (int j = 0; j < n4; j += 4) {
-        const ulonglong2 a = *(const ulonglong2*)(list + j);
-        const ulonglong2 b = *(const ulonglong2*)(list + j + 2);
-        r += (a.x > mine ? 1 : 0) + (a.y > mine ? 1 : 0) + (b.x > mine ? 1 : 0) + (b.y > mine ? 1 : 0);
-    }
-    return r;
-}
-
-// Steps 4 and 5 for one wave: rank the n listed keys, keep ranks below `need`,
-// write the chosen blocks ascending to dst[0..need) and the local block after them.
-__device__ __forceinline__ void rank_and_emit(uint64_t* list, int32_t* chosen, int n, int need, int cl,
-                                              int32_t* __restrict__ dst, int lane) {
-    const int n4 = (n + 3) & ~3;
-    if (lane < n4 - n) list[n + lane] = 0ull;
-    if (lane >= need && lane < ((need + 3) & ~3)) chosen[lane] = 0x7fffffff;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (int i = lane; i < n; i += 64) {
-        const uint64_t mine = list[i];
-        const int r = rank_in_list(list, n4, mine);
-        if (r < need) chosen[r] = key_block(mine);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ascending block order; the local block is larger than every chosen one
-    if (lane < need) {
-        const int mine = chosen[lane];
-        const int need4 = (need + 3) & ~3;
-        int pos = 0;
-        for (int j = 0; j < need4; j += 4) {
-            const int4 c4 = *(const int4*)(chosen + j);
-            pos += (c4.x < mine ? 1 : 0) + (c4.y < mine ? 1 : 0) + (c4.z < mine ? 1 : 0) + (c4.w < mine ? 1 : 0);
-        }
-        dst[pos] = mine;
-    }
-    if (lane == 0) dst[need] = cl;
-}
 
 bool topk_supported(int nblk, int top_k) {
     // Rows with c_loc + 1 <= top_k take every visible block and need no ranking.
@@ -157,17 +114,6 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
 // score keys, T32, is the high word of the need-th largest 64-bit lane maximum,
 // so every key of the exact selection has a score key >= T32. Only those
 // candidates get 64-bit (score, block) keys and are ranked exactly.
-constexpr int kTopkRegVals = 16;
-
-__device__ __forceinline__ void topk_load_row(const float* __restrict__ src, int cl, int lane,
-                                              float (&v)[kTopkRegVals]) {
-#pragma unroll
-    for (int i = 0; i < kTopkRegVals; ++i) {
-        const int c = lane + 64 * i;
-        v[i] = c < cl ? src[c] : 0.0f;
-    }
-}
-
 __global__ __launch_bounds__(256) void k_block_topk_reg(const float* __restrict__ pooled,
                                                         int32_t* __restrict__ block_idx, int N, int nblk, int top_k,
                                                         long long rows) {
@@ -205,43 +151,7 @@ __global__ __launch_bounds__(256) void k_block_topk_reg(const float* __restrict_
             if (lane == 0) dst[0] = cl;
             continue;
         }
-        // 1. 32-bit score keys (0 for blocks outside the row) and their lane maximum
-        uint32_t k32[kTopkRegVals];
-        uint32_t lmax = 0u;
-#pragma unroll
-        for (int i = 0; i < kTopkRegVals; ++i) {
-            k32[i] = lane + 64 * i < cl ? order_key(cur[i]) : 0u;
-            lmax = k32[i] > lmax ? k32[i] : lmax;
-        }
-        // 2. bitonic sort of the lane maxima, descending; T32 = the need-th largest (a real
-        // key: at least need + 1 lanes hold a block, since cl >= top_k)
-        uint32_t x = lmax;
-#pragma unroll
-        for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-            for (int j = k >> 1; j > 0; j >>= 1) {
-                const uint32_t y = __shfl_xor(x, j, 64);
-                const bool keep_big = ((lane & j) == 0) == ((lane & k) == 0);
-                x = keep_big ? (x > y ? x : y) : (x > y ? y : x);
-            }
-        }
-        const uint32_t T = __shfl(x, need - 1, 64);
-        // 3. candidates: score key >= T, as 64-bit (score, block) keys
-        int n = 0;
-#pragma unroll
-        for (int i = 0; i < kTopkRegVals; ++i) {
-            const bool take = k32[i] >= T;
-            const uint64_t mask = __ballot(take);
-            if (take)
-                list[n + __popcll(mask & ((1ull << lane) - 1ull))] =
-                    ((uint64_t)k32[i] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * i));
-            n += __popcll(mask);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // 4, 5. exact rank among the candidates; ascending output, local block last
-        rank_and_emit(list, chosen[wave], n, need, cl, dst, lane);
+        topk_row_from_regs(cur, cl, need, list, chosen[wave], dst, lane);
         // the next row reuses this wave's LDS lists
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();

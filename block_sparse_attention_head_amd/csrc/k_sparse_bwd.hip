@@ -94,7 +94,6 @@ __global__ __launch_bounds__(256) void k_bwd_delta(const __bf16* __restrict__ o,
 // ---------------------------------------------------------------------------
 constexpr int kBwdRows = 32;                                   // gathered rows per step
 constexpr int kBwdRing = 4;                                    // row-major stages
-constexpr int kBwdWaves = 8;
 constexpr int kBwdMaxItemEntries = kRowTilesPerItem * kBlock;  // entries of one item when G = 1
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
