@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the MSA forward hot path on one MI355X.
 
-One step = one full forward over one batch of the workload: index scores
-(causal block max-pool), top-k selection, reverse index + tile plan, KV-outer
-partial attention, softmax combine. Inputs are seeded synthetic bf16 tensors
+One step = one full forward over one batch of the workload: index scores,
+causal block max-pool and top-k selection (one single-pass kernel), reverse
+index + tile plan, KV-outer partial attention, softmax combine. The two-kernel
+selection (pooled scores through HBM, then a selection kernel) is timed beside
+it on the same inputs. Inputs are seeded synthetic bf16 tensors
 already resident in HBM when the timed region starts; each stage is bracketed
 by HIP events on the stream the library launches on.
 
@@ -31,6 +33,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 # kernel behind each single-kernel stage, the source it is built from, and its roofline bound
 STAGE_KERNEL = {
+    "index_topk": ("k_index_topk", "k_index_pool.hip", "mfma"),
     "index_pool": ("k_index_pool", "k_index_pool.hip", "mfma"),
     "topk": ("k_block_topk", "k_block_topk.hip", "hbm"),
     "partial": ("k_sparse_partial", "k_sparse_partial.hip", "hbm"),
@@ -142,6 +145,35 @@ def backward_report(w, steps: int, warmup: int):
             "fwd_ms_same_shape": round(res["fwd"], 4)}
 
 
+def two_kernel_selection(msa, xg, w, block_idx_single, steps: int, warmup: int):
+    """msa_index_scores (pooled scores to HBM) then msa_block_topk, on the step's inputs,
+    timed with HIP events per kernel; the indices must equal the single pass's."""
+    import torch
+
+    K = w.top_k
+    pooled = torch.empty((w.batch, w.h_idx, w.seqlen, w.nblk), dtype=torch.float32, device=xg["q"].device)
+    bi = torch.empty_like(block_idx_single)
+    for _ in range(warmup):
+        msa.index_scores(xg["q_idx"], xg["k_idx"], pooled, visible_only=True)
+        msa.block_topk(pooled, K, bi)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in evs:
+        e[0].record()
+        msa.index_scores(xg["q_idx"], xg["k_idx"], pooled, visible_only=True)
+        e[1].record()
+        msa.block_topk(pooled, K, bi)
+        e[2].record()
+    torch.cuda.synchronize()
+    ip = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    tk = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    same = bool(torch.equal(bi, block_idx_single))
+    del pooled, bi
+    torch.cuda.empty_cache()
+    return {"index_pool_ms": round(ip, 4), "topk_ms": round(tk, 4), "total_ms": round(ip + tk, 4),
+            "same_indices": same}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,37 +216,34 @@ def main(argv=None) -> int:
     xg = {k: v.to(dev) for k, v in x.items()}
     B, N, Hq, Hkv, K = w.batch, w.seqlen, w.h_q, w.h_kv, w.top_k
     shape = msa.make_shape(B, N, Hq, Hkv, K, w.softmax_scale)
-    pooled = torch.empty((B, Hkv, N, w.nblk), dtype=torch.float32, device=dev)
     block_idx = torch.empty((B, Hkv, N, K), dtype=torch.int32, device=dev)
     o = torch.empty_like(xg["q"])
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
     ws = msa.alloc_workspace(shape, msa.OP_SPARSE_ATTN_FWD, dev)
-    stages = ["index_pool", "topk", "plan", "partial", "combine"]
+    ws_sel = msa.alloc_workspace(shape, msa.OP_INDEX_TOPK, dev)
+    stages = ["index_topk", "plan", "partial", "combine"]
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        msa.index_scores(xg["q_idx"], xg["k_idx"], pooled, visible_only=True)
+        msa.index_topk(xg["q_idx"], xg["k_idx"], K, block_idx, workspace=ws_sel)
         if ev is not None:
             ev[1].record()
-        msa.block_topk(pooled, K, block_idx)
-        if ev is not None:
-            ev[2].record()
         msa.sparse_attn_plan(shape, block_idx, ws)
         if ev is not None:
-            ev[3].record()
+            ev[2].record()
         msa.sparse_attn_partial(shape, xg["q"], xg["k"], xg["v"], ws)
         if ev is not None:
-            ev[4].record()
+            ev[3].record()
         msa.sparse_attn_combine(shape, block_idx, o, lse, ws)
         if ev is not None:
-            ev[5].record()
+            ev[4].record()
 
     print(f"[bench] warmup {a.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(a.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
@@ -226,6 +255,7 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / a.steps
     stage_ms = {s: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / a.steps for j, s in enumerate(stages)}
+    two_kernel = two_kernel_selection(msa, xg, w, block_idx, a.steps, a.warmup)
 
     if a.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -237,8 +267,7 @@ def main(argv=None) -> int:
     s = P.Shape(B, N, Hq, Hkv, K)
     idx_f, main_f = P.index_flops(s), P.main_flops(s)
     work = {
-        "index_pool": ("TFLOP/s", idx_f / 1e12, P.PEAK_BF16_TFLOPS),
-        "topk": ("GB/s", P.topk_bytes(s) / 1e9, P.PEAK_HBM_GBS),
+        "index_topk": ("TFLOP/s", idx_f / 1e12, P.PEAK_BF16_TFLOPS),
         "partial": ("GB/s", P.partial_bytes(s) / 1e9, P.PEAK_HBM_GBS),
         "combine": ("GB/s", P.combine_bytes(s) / 1e9, P.PEAK_HBM_GBS),
     }
@@ -284,12 +313,17 @@ def main(argv=None) -> int:
         "tflops": round((idx_f + main_f) / 1e12 / (ms_step / 1e3), 2),
         "tflops_frac_of_bf16_peak": round((idx_f + main_f) / 1e12 / (ms_step / 1e3) / P.PEAK_BF16_TFLOPS, 4),
         "main_attention_tflops": round(main_f / 1e12 / (main_ms / 1e3), 2),
-        "index_tflops": round(idx_f / 1e12 / (stage_ms["index_pool"] / 1e3), 2),
+        "index_tflops": round(idx_f / 1e12 / (stage_ms["index_topk"] / 1e3), 2),
         "stages": stage_report,
+        "two_kernel_selection": {
+            **two_kernel, "single_pass_ms": round(stage_ms["index_topk"], 4),
+            "index_pool_tflops": round(idx_f / 1e12 / (two_kernel["index_pool_ms"] / 1e3), 2),
+            "topk_gbs": round(P.topk_bytes(s) / 1e9 / (two_kernel["topk_ms"] / 1e3), 2),
+            "saving_ms": round(two_kernel["total_ms"] - stage_ms["index_topk"], 4)},
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    del xg, pooled, block_idx, o, lse, ws
+    del xg, block_idx, o, lse, ws, ws_sel
     torch.cuda.empty_cache()
     if not a.no_backward:
         out["backward"] = backward_report(WORKLOADS[a.backward_workload], a.steps, a.warmup)

@@ -14,6 +14,13 @@
 // rows, so a lane holds one query row and the block max is an in-lane max plus
 // one exchange between the wave's halves. Each lane keeps its row's maxima for
 // the chunk in registers and writes them as one 128-byte run.
+//
+// Fused with the selection (k_index_topk): [MSA summary] "GPU kernel
+// co-design" selects on the raw pooled scores, and [Flash-MSA] "Proxy
+// attention" keeps the query's own block plus the top_k - 1 best earlier ones.
+// Since a lane already owns a row and key blocks arrive in ascending order, the
+// lane keeps its row's best blocks in registers as they arrive; the pooled
+// matrix never reaches memory and no selection pass follows.
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 
@@ -21,6 +28,7 @@ namespace msa {
 
 constexpr int kIdxTileRows = 256;  // (position, index head) rows per workgroup
 constexpr int kIdxChunk = 32;      // key blocks per workgroup: one 128-byte pooled run per row
+constexpr int kStreamCap = 16;     // list length of the single-pass selection: top_k <= 17
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -35,6 +43,68 @@ __device__ __forceinline__ void stage_key_block(const __bf16* __restrict__ src, 
         __builtin_amdgcn_global_load_lds((const void*)(src + row * kDim + logical * 8),
                                          (lds_ptr)(dst + (i * 4 + wave) * 64 * 8), 16, 0, 0);
     }
+}
+
+// B operand (Q^T) of a wave: lane holds row (r0 + wave*64 + nt*32 + l32), dims kk*16 + 8h .. +7;
+// rows past R are zero and get query position -1 (never the diagonal block).
+__device__ __forceinline__ void load_q_rows(const __bf16* __restrict__ qb, int r0, int R, int H, int wave, int h,
+                                            int l32, bf16x8 (&qf)[2][8], int (&trow)[2]) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int row = r0 + wave * 64 + nt * 32 + l32;
+        trow[nt] = row < R ? row / H : -1;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            if (row < R) {
+                qf[nt][kk] = *(const bf16x8*)(qb + (size_t)row * kDim + kk * 16 + 8 * h);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qf[nt][kk][e] = (__bf16)0.0f;
+            }
+        }
+    }
+}
+
+// Max score of this lane's row (row tile h of the wave) over the visible keys of key
+// block c, staged in LDS at kt.
+__device__ __forceinline__ float block_row_max(const __bf16* kt, const bf16x8 (&qf)[2][8], const int (&trow)[2],
+                                               int c, int h, int l32) {
+    const bool diag0 = (trow[0] >> 7) == c, diag1 = (trow[1] >> 7) == c;
+    const bool any_diag = __any(diag0 || diag1);
+    // key = mt*32 + 8*(i/4) + 4h + i%4 <= lim  <=>  mt*32 + 8*(i/4) + i%4 <= lim - 4h,
+    // so every comparison is against a compile-time constant
+    const int lim0 = (diag0 ? trow[0] - c * kBlock : kBlock - 1) - 4 * h;
+    const int lim1 = (diag1 ? trow[1] - c * kBlock : kBlock - 1) - 4 * h;
+    float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {  // one 32-key M tile at a time keeps the accumulators small
+        f32x16 acc0, acc1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const bf16x8 a = *(const bf16x8*)(kt + swz_chunk_offset(mt * 32 + l32, 2 * kk + h));
+            acc0 = mfma32(a, qf[0][kk], acc0);
+            acc1 = mfma32(a, qf[1][kk], acc1);
+        }
+        if (any_diag) {  // the query's own block: keep keys j <= t only
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key_h0 = mt * 32 + mfma32_row(i, 0);
+                if (key_h0 <= lim0) m0 = fmaxf(m0, acc0[i]);
+                if (key_h0 <= lim1) m1 = fmaxf(m1, acc1[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                m0 = fmaxf(m0, acc0[i]);
+                m1 = fmaxf(m1, acc1[i]);
+            }
+        }
+    }
+    m0 = wave_max_xor32(m0);
+    m1 = wave_max_xor32(m1);
+    return h ? m1 : m0;  // after the exchange lane-half h owns row tile h
 }
 
 __global__ __launch_bounds__(256, 2) void k_index_pool(const __bf16* __restrict__ q_idx,
@@ -56,24 +126,9 @@ __global__ __launch_bounds__(256, 2) void k_index_pool(const __bf16* __restrict_
     const __bf16* kb = k_idx + (size_t)b * N * kDim;
 
     stage_key_block(kb + (size_t)c0 * kBlock * kDim, ks[0], wave, lane);
-
-    // B operand (Q^T): lane holds row (wave*64 + nt*32 + l32), dims kk*16 + 8h .. +7.
     bf16x8 qf[2][8];
     int trow[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const int row = r0 + wave * 64 + nt * 32 + l32;
-        trow[nt] = row < R ? row / H : -1;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            if (row < R) {
-                qf[nt][kk] = *(const bf16x8*)(qb + (size_t)row * kDim + kk * 16 + 8 * h);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qf[nt][kk][e] = (__bf16)0.0f;
-            }
-        }
-    }
+    load_q_rows(qb, r0, R, H, wave, h, l32, qf, trow);
 
     // pv[j] ends up holding this lane's row max for key block c1 - kIdxChunk + j
     float pv[kIdxChunk];
@@ -85,46 +140,10 @@ __global__ __launch_bounds__(256, 2) void k_index_pool(const __bf16* __restrict_
         __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of block c have landed
         __syncthreads();                // ... and everyone's; the other buffer is free again
         if (c + 1 < c1) stage_key_block(kb + (size_t)(c + 1) * kBlock * kDim, ks[buf ^ 1], wave, lane);
-        const __bf16* kt = ks[buf];
-        const bool diag0 = (trow[0] >> 7) == c, diag1 = (trow[1] >> 7) == c;
-        const bool any_diag = __any(diag0 || diag1);
-        // key = mt*32 + 8*(i/4) + 4h + i%4 <= lim  <=>  mt*32 + 8*(i/4) + i%4 <= lim - 4h,
-        // so every comparison is against a compile-time constant
-        const int lim0 = (diag0 ? trow[0] - c * kBlock : kBlock - 1) - 4 * h;
-        const int lim1 = (diag1 ? trow[1] - c * kBlock : kBlock - 1) - 4 * h;
-        float m0 = -INFINITY, m1 = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {  // one 32-key M tile at a time keeps the accumulators small
-            f32x16 acc0, acc1;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.0f;
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const bf16x8 a = *(const bf16x8*)(kt + swz_chunk_offset(mt * 32 + l32, 2 * kk + h));
-                acc0 = mfma32(a, qf[0][kk], acc0);
-                acc1 = mfma32(a, qf[1][kk], acc1);
-            }
-            if (any_diag) {  // the query's own block: keep keys j <= t only
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key_h0 = mt * 32 + mfma32_row(i, 0);
-                    if (key_h0 <= lim0) m0 = fmaxf(m0, acc0[i]);
-                    if (key_h0 <= lim1) m1 = fmaxf(m1, acc1[i]);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    m0 = fmaxf(m0, acc0[i]);
-                    m1 = fmaxf(m1, acc1[i]);
-                }
-            }
-        }
-        m0 = wave_max_xor32(m0);
-        m1 = wave_max_xor32(m1);
-        // after the exchange lane-half h owns row tile h
+        const float m = block_row_max(ks[buf], qf, trow, c, h, l32);
 #pragma unroll
         for (int j = 0; j + 1 < kIdxChunk; ++j) pv[j] = pv[j + 1];
-        pv[kIdxChunk - 1] = h ? m1 : m0;
+        pv[kIdxChunk - 1] = m;
     }
 
     const int row = r0 + wave * 64 + h * 32 + l32;
@@ -146,6 +165,90 @@ __global__ __launch_bounds__(256, 2) void k_index_pool(const __bf16* __restrict_
     }
 }
 
+// Index scores and selection in one pass, with no pooled matrix in memory. A
+// workgroup owns a 256-row tile and walks every key block its rows can see, in
+// ascending order; after each block the lane owning a row inserts that block's
+// max into the row's running list of the kStreamCap best (score key, block)
+// pairs among the blocks before the row's own. The list stays sorted by score
+// key, descending; a block arriving later has a larger index than every listed
+// one, so a strict comparison keeps equal scores in ascending block order, which
+// is the order of the 64-bit keys used by the selection kernel: the chosen set is
+// the same. Tiles run heaviest (latest) first so the long causal rows start early.
+__global__ __launch_bounds__(256, 2) void k_index_topk(const __bf16* __restrict__ q_idx,
+                                                       const __bf16* __restrict__ k_idx,
+                                                       int32_t* __restrict__ block_idx, int N, int H, int top_k,
+                                                       int tiles) {
+    const int id = blockIdx.x, B = gridDim.x / tiles;
+    const int tile = tiles - 1 - id / B, b = id - (id / B) * B;
+    const int R = N * H;
+    const int r0 = tile * kIdxTileRows;
+    const int r_end = min(r0 + kIdxTileRows, R);
+    const int nkb = ((r_end - 1) / H) / kBlock + 1;
+
+    __shared__ __attribute__((aligned(16))) __bf16 ks[2][kBlock * kDim];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const __bf16* qb = q_idx + (size_t)b * R * kDim;
+    const __bf16* kb = k_idx + (size_t)b * N * kDim;
+
+    stage_key_block(kb, ks[0], wave, lane);
+    bf16x8 qf[2][8];
+    int trow[2];
+    load_q_rows(qb, r0, R, H, wave, h, l32, qf, trow);
+
+    const int row = r0 + wave * 64 + h * 32 + l32;
+    const int cl = row < R ? (row / H) >> 7 : -1;  // the row's own block; only blocks c < cl compete
+    // score key 0 sits below every finite score's key, so empty slots are never chosen
+    uint32_t ls[kStreamCap];
+    int lb[kStreamCap];
+#pragma unroll
+    for (int i = 0; i < kStreamCap; ++i) {
+        ls[i] = 0u;
+        lb[i] = -1;
+    }
+
+    for (int c = 0; c < nkb; ++c) {
+        const int buf = c & 1;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (c + 1 < nkb) stage_key_block(kb + (size_t)(c + 1) * kBlock * kDim, ks[buf ^ 1], wave, lane);
+        const float m = block_row_max(ks[buf], qf, trow, c, h, l32);
+        // insert before the first listed key it exceeds; everything after moves down one
+        // slot (comparing the displaced entry instead would reorder equal scores)
+        const uint32_t xs = c < cl ? order_key(m) : 0u;
+        bool gt[kStreamCap];
+#pragma unroll
+        for (int i = 0; i < kStreamCap; ++i) gt[i] = xs > ls[i];
+#pragma unroll
+        for (int i = kStreamCap - 1; i > 0; --i) {
+            ls[i] = gt[i] ? (gt[i - 1] ? ls[i - 1] : xs) : ls[i];
+            lb[i] = gt[i] ? (gt[i - 1] ? lb[i - 1] : c) : lb[i];
+        }
+        ls[0] = gt[0] ? xs : ls[0];
+        lb[0] = gt[0] ? c : lb[0];
+    }
+    if (row >= R) return;
+
+    const int t = row / H, g = row - t * H;
+    int32_t* dst = block_idx + (((size_t)b * H + g) * N + t) * top_k;
+    if (cl + 1 <= top_k) {  // every visible block
+        for (int s2 = 0; s2 < top_k; ++s2) dst[s2] = s2 <= cl ? s2 : -1;
+        return;
+    }
+    // the need best, in ascending block order, then the row's own block
+    const int need = top_k - 1;
+#pragma unroll
+    for (int i = 0; i < kStreamCap; ++i) {
+        if (i < need) {
+            int pos = 0;
+#pragma unroll
+            for (int j = 0; j < kStreamCap; ++j) pos += (j < need && lb[j] < lb[i]) ? 1 : 0;
+            dst[pos] = lb[i];
+        }
+    }
+    dst[need] = cl;
+}
+
 // pooled[b,g,t,c] = -inf for c > t/128 (the part no query can see).
 __global__ __launch_bounds__(256) void k_pooled_fill_upper(float* __restrict__ pooled, int N, int nblk,
                                                            long long rows) {
@@ -163,12 +266,24 @@ hipError_t launch_index_pool(const void* q_idx, const void* k_idx, float* pooled
     const int tiles = (int)((R + kIdxTileRows - 1) / kIdxTileRows);
     const int chunks = (d.nblk + kIdxChunk - 1) / kIdxChunk;
     dim3 grid(tiles, chunks, d.B);
-    hipLaunchKernelGGL(k_index_pool, grid, dim3(256), 0, stream, (const __bf16*)q_idx, (const __bf16*)k_idx,
-                       pooled, d.N, H, d.nblk);
+    hipLaunchKernelGGL(k_index_pool, grid, dim3(256), 0, stream, (const __bf16*)q_idx, (const __bf16*)k_idx, pooled,
+                       d.N, H, d.nblk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !fill_upper) return e;
     const long long rows = (long long)d.B * H * d.N;
     hipLaunchKernelGGL(k_pooled_fill_upper, dim3((unsigned)rows), dim3(256), 0, stream, pooled, d.N, d.nblk, rows);
+    return hipGetLastError();
+}
+
+bool index_topk_fusable(const Dims& d) { return d.top_k - 1 <= kStreamCap; }
+
+hipError_t launch_index_topk(const void* q_idx, const void* k_idx, int32_t* block_idx, const Dims& d,
+                             hipStream_t stream) {
+    const int H = d.Hkv;
+    const long long R = (long long)d.N * H;
+    const int tiles = (int)((R + kIdxTileRows - 1) / kIdxTileRows);
+    hipLaunchKernelGGL(k_index_topk, dim3((unsigned)(tiles * d.B)), dim3(256), 0, stream, (const __bf16*)q_idx,
+                       (const __bf16*)k_idx, block_idx, d.N, H, d.top_k, tiles);
     return hipGetLastError();
 }
 

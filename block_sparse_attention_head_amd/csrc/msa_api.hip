@@ -132,15 +132,29 @@ namespace {
 
 size_t pooled_bytes(const Dims& d) { return (size_t)d.B * d.Hkv * d.N * d.nblk * sizeof(float); }
 
+// the single-pass kernel needs nothing; otherwise the pooled scores
+size_t index_topk_ws_bytes(const Dims& d) { return index_topk_fusable(d) ? 0 : align_up(pooled_bytes(d), 256); }
+
 size_t ws_bytes(const Dims& d, msa_op op) {
     switch (op) {
         case MSA_OP_INDEX_SCORES: return 0;
         case MSA_OP_BLOCK_TOPK: return 0;
         case MSA_OP_SPARSE_ATTN_FWD: return sparse_ws_bytes(d);
-        case MSA_OP_FWD: return align_up(pooled_bytes(d), 256) + sparse_ws_bytes(d);
+        case MSA_OP_FWD: return index_topk_ws_bytes(d) + sparse_ws_bytes(d);
         case MSA_OP_SPARSE_ATTN_BWD: return bwd_ws_bytes(d);
+        case MSA_OP_INDEX_TOPK: return index_topk_ws_bytes(d);
     }
     return 0;
+}
+
+// index scores and selection: one pass when the list fits the single-pass kernel
+hipError_t run_index_topk(const void* q_idx, const void* k_idx, int32_t* block_idx, void* workspace, const Dims& d,
+                          hipStream_t stream) {
+    if (index_topk_fusable(d)) return launch_index_topk(q_idx, k_idx, block_idx, d, stream);
+    float* pooled = (float*)workspace;
+    hipError_t e = launch_index_pool(q_idx, k_idx, pooled, d, false, stream);
+    if (e == hipSuccess) e = launch_block_topk(pooled, block_idx, d, stream);
+    return e;
 }
 
 msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
@@ -168,7 +182,7 @@ extern "C" {
 
 msa_status msa_workspace_size(const msa_shape* shape, msa_op op, size_t* bytes) {
     if (!bytes) return MSA_ERR_INVALID_ARG;
-    if (op < MSA_OP_INDEX_SCORES || op > MSA_OP_SPARSE_ATTN_BWD) return MSA_ERR_INVALID_ARG;
+    if (op < MSA_OP_INDEX_SCORES || op > MSA_OP_INDEX_TOPK) return MSA_ERR_INVALID_ARG;
     Dims d;
     const msa_status st = check_shape(shape, &d);
     if (st != MSA_OK) return st;
@@ -257,21 +271,31 @@ msa_status msa_fwd(const msa_shape* shape, const void* q_idx, const void* k_idx,
     const msa_status st = check_shape(shape, &d);
     if (st != MSA_OK) return st;
     if (!q_idx || !k_idx || !q || !k || !v || !block_idx || !o || !lse) return MSA_ERR_INVALID_ARG;
-    if (!topk_supported(d.nblk, d.top_k)) return MSA_ERR_UNSUPPORTED;
+    if (!index_topk_fusable(d) && !topk_supported(d.nblk, d.top_k)) return MSA_ERR_UNSUPPORTED;
     const size_t need = ws_bytes(d, MSA_OP_FWD);
     if (!workspace || workspace_bytes < need) return MSA_ERR_WORKSPACE;
     (void)hipGetLastError();
-    float* pooled = (float*)workspace;
-    void* rest = (char*)workspace + align_up(pooled_bytes(d), 256);
-    hipError_t e = launch_index_pool(q_idx, k_idx, pooled, d, false, stream);
-    if (e != hipSuccess) return MSA_ERR_HIP;
-    e = launch_block_topk(pooled, block_idx, d, stream);
+    void* rest = (char*)workspace + index_topk_ws_bytes(d);
+    hipError_t e = run_index_topk(q_idx, k_idx, block_idx, workspace, d, stream);
     if (e != hipSuccess) return MSA_ERR_HIP;
     const SparseWs ws = carve_sparse_ws(rest, d);
     e = launch_sparse_plan(block_idx, ws, d, false, stream);
     if (e == hipSuccess) e = launch_sparse_partial(q, k, v, ws, d, stream);
     if (e == hipSuccess) e = launch_sparse_combine(block_idx, o, lse, ws, d, stream);
     return hip_status(e);
+}
+
+msa_status msa_index_topk(const msa_shape* shape, const void* q_idx, const void* k_idx, int32_t* block_idx,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    Dims d;
+    const msa_status st = check_shape(shape, &d);
+    if (st != MSA_OK) return st;
+    if (!q_idx || !k_idx || !block_idx) return MSA_ERR_INVALID_ARG;
+    if (!index_topk_fusable(d) && !topk_supported(d.nblk, d.top_k)) return MSA_ERR_UNSUPPORTED;
+    const size_t need = ws_bytes(d, MSA_OP_INDEX_TOPK);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return MSA_ERR_WORKSPACE;
+    (void)hipGetLastError();
+    return hip_status(run_index_topk(q_idx, k_idx, block_idx, workspace, d, stream));
 }
 
 msa_status msa_sparse_attn_bwd(const msa_shape* shape, const void* q, const void* k, const void* v, const void* o,

@@ -22,6 +22,11 @@ struct Dims {
 hipError_t launch_index_pool(const void* q_idx, const void* k_idx, float* pooled, const Dims& d,
                              bool fill_upper, hipStream_t stream);
 
+// Index scores + block max-pool + top-k selection in one pass with no pooled
+// scores in memory and no scratch; needs index_topk_fusable(d) (top_k <= 17).
+bool index_topk_fusable(const Dims& d);
+hipError_t launch_index_topk(const void* q_idx, const void* k_idx, int32_t* block_idx, const Dims& d,
+                             hipStream_t stream);
 // Largest top_k this build's selection kernel accepts for `nblk` key blocks.
 bool topk_supported(int nblk, int top_k);
 hipError_t launch_block_topk(const float* pooled, int32_t* block_idx, const Dims& d, hipStream_t stream);

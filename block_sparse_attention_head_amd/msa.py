@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
 MSA_OK = 0
 MSA_CAUSAL = 1
 MSA_POOLED_VISIBLE_ONLY = 2
-OP_INDEX_SCORES, OP_BLOCK_TOPK, OP_SPARSE_ATTN_FWD, OP_FWD, OP_SPARSE_ATTN_BWD = 0, 1, 2, 3, 4
+OP_INDEX_SCORES, OP_BLOCK_TOPK, OP_SPARSE_ATTN_FWD, OP_FWD, OP_SPARSE_ATTN_BWD, OP_INDEX_TOPK = 0, 1, 2, 3, 4, 5
 
 BLOCK_SIZE = 128
 HEAD_DIM = 128
@@ -60,6 +60,7 @@ _SIGNATURES = {
     "msa_sparse_attn_combine": [_S, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "msa_fwd": [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "msa_sparse_attn_bwd": [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "msa_index_topk": [_S, _P, _P, _P, _P, ctypes.c_size_t, _P],
 }
 
 _lib = None
@@ -166,6 +167,22 @@ def block_topk(pooled: torch.Tensor, top_k: int, block_idx: Optional[torch.Tenso
     shape = make_shape(B, N, H, H, top_k, 1.0)
     _check("msa_block_topk", lib().msa_block_topk(ctypes.byref(shape), _ptr(pooled), _ptr(block_idx), _P(0), 0,
                                                   _stream(pooled.device)))
+    return block_idx
+
+
+def index_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, top_k: int, block_idx: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """block_idx int32 [B, H_idx, N, top_k]: index scores and selection in one step (see msa_index_topk)."""
+    B, N, H, D = q_idx.shape
+    _need(q_idx, "q_idx", torch.bfloat16, (B, N, H, D))
+    _need(k_idx, "k_idx", torch.bfloat16, (B, N, D))
+    if block_idx is None:
+        block_idx = torch.empty((B, H, N, top_k), dtype=torch.int32, device=q_idx.device)
+    _need(block_idx, "block_idx", torch.int32, (B, H, N, top_k))
+    shape = make_shape(B, N, H, H, top_k, 1.0)
+    ws = _ws(workspace, shape, OP_INDEX_TOPK, q_idx.device)
+    _check("msa_index_topk", lib().msa_index_topk(ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(block_idx),
+                                                  _ptr(ws), ws.numel(), _stream(q_idx.device)))
     return block_idx
 
 

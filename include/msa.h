@@ -87,7 +87,8 @@ typedef enum msa_op {
     MSA_OP_BLOCK_TOPK = 1,
     MSA_OP_SPARSE_ATTN_FWD = 2,
     MSA_OP_FWD = 3,
-    MSA_OP_SPARSE_ATTN_BWD = 4
+    MSA_OP_SPARSE_ATTN_BWD = 4,
+    MSA_OP_INDEX_TOPK = 5
 } msa_op;
 
 /* Bytes of device workspace `op` needs for `shape` (0 is a valid answer).
@@ -113,6 +114,19 @@ msa_status msa_index_scores(const msa_shape* shape, const void* q_idx, const voi
  * Only the visible part (c <= c_loc) of `pooled` is read. Output ascending,
  * padded with -1. Deterministic; no workspace is needed today (pass NULL, 0). */
 msa_status msa_block_topk(const msa_shape* shape, const float* pooled, int32_t* block_idx,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* msa_index_scores followed by msa_block_topk, writing only `block_idx`
+ * (same layout and result, bit for bit). For top_k <= 17 one kernel does
+ * both in a single pass with no pooled scores in memory: each row keeps its
+ * best top_k - 1 earlier blocks in registers as the key blocks stream past
+ * ([Flash-MSA] "Proxy attention": the selection is kept inside the proxy
+ * kernel; [MSA summary] "GPU kernel co-design": exp-free selection on the raw
+ * pooled scores). That path needs no workspace (size 0; workspace may be NULL).
+ * For larger top_k the two kernels run in turn with the pooled scores (visible
+ * part only) in the workspace; ask msa_workspace_size(MSA_OP_INDEX_TOPK).
+ * msa_fwd uses this step. */
+msa_status msa_index_topk(const msa_shape* shape, const void* q_idx, const void* k_idx, int32_t* block_idx,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Exact causal softmax attention of every query head over the blocks its
@@ -149,9 +163,8 @@ msa_status msa_sparse_attn_partial(const msa_shape* shape, const void* q, const 
 msa_status msa_sparse_attn_combine(const msa_shape* shape, const int32_t* block_idx, void* o, float* lse,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* The whole forward: msa_index_scores (pooled kept in the workspace, only its
- * visible part computed), msa_block_topk into `block_idx`, then
- * msa_sparse_attn_fwd into `o` and `lse` ([Flash-MSA] "Forward": index branch
+/* The whole forward: msa_index_topk into `block_idx`, then msa_sparse_attn_fwd
+ * into `o` and `lse` ([Flash-MSA] "Forward": index branch
  * first, then sparse main attention; block indices and LSE are kept). */
 msa_status msa_fwd(const msa_shape* shape, const void* q_idx, const void* k_idx, const void* q,
                    const void* k, const void* v, int32_t* block_idx, void* o, float* lse,

@@ -54,16 +54,24 @@ def _ws(m, op=None, **kw):
 def test_workspace_size_valid(m):
     st, n = _ws(m)
     assert st == 0
-    # pooled [1,1,1024,8] fp32 + reverse index + partials [1,1024,4,4,128] bf16 + lse
-    assert n >= 1024 * 8 * 4 + 1024 * 4 * 4 * 128 * 2 + 1024 * 4 * 4 * 4
+    # reverse index + partials [1,1024,4,4,128] bf16 + lse (the selection runs in one pass)
+    assert n >= 1024 * 4 * 4 * 128 * 2 + 1024 * 4 * 4 * 4
     st, n = _ws(m, op=m.OP_INDEX_SCORES)
     assert (st, n) == (0, 0)
     st, n = _ws(m, op=m.OP_BLOCK_TOPK)
     assert (st, n) == (0, 0)
     st1, n1 = _ws(m, op=m.OP_SPARSE_ATTN_FWD)
     st2, n2 = _ws(m, op=m.OP_FWD)
-    assert st1 == st2 == 0 and n2 > n1
+    assert st1 == st2 == 0 and n2 == n1
+    # top_k = 18 runs index scores and selection as two kernels: pooled [1,1,4096,32] fp32 on top
+    st1, n1 = _ws(m, op=m.OP_SPARSE_ATTN_FWD, top_k=18, seqlen=4096)
+    st2, n2 = _ws(m, op=m.OP_FWD, top_k=18, seqlen=4096)
+    assert st1 == st2 == 0 and n2 >= n1 + 4096 * 32 * 4
     # backward: reverse index + D [1,1024,4] + dQ partials [1,1024,4,4,128] bf16 + dK/dV item partials
+    # index + selection: one pass without workspace for top_k <= 17, else the pooled scores
+    assert _ws(m, op=m.OP_INDEX_TOPK) == (0, 0)
+    st4, n4 = _ws(m, op=m.OP_INDEX_TOPK, top_k=18, seqlen=4096)
+    assert st4 == 0 and n4 >= 4096 * 32 * 4
     st3, n3 = _ws(m, op=m.OP_SPARSE_ATTN_BWD)
     assert st3 == 0 and n3 >= 1024 * 4 * 4 + 1024 * 4 * 4 * 128 * 2 + 2 * 128 * 128 * 4
 
@@ -93,6 +101,7 @@ def test_unsupported_dims_and_flags(m):
         setattr(t, field, val)
         assert m.lib().msa_workspace_size(ctypes.byref(t), m.OP_FWD, ctypes.byref(n)) == 2, field
     assert m.lib().msa_workspace_size(ctypes.byref(s), 9, ctypes.byref(n)) == 1
+    assert m.lib().msa_workspace_size(ctypes.byref(s), 6, ctypes.byref(n)) == 1
     assert m.lib().msa_workspace_size(None, m.OP_FWD, ctypes.byref(n)) == 1
     assert m.lib().msa_workspace_size(ctypes.byref(s), m.OP_FWD, None) == 1
 
@@ -112,6 +121,10 @@ def test_null_pointers_rejected_before_any_launch(m):
     assert lib.msa_sparse_attn_partial(ctypes.byref(s), one, one, one, one, 10, P(0)) == 3
     assert lib.msa_sparse_attn_combine(ctypes.byref(s), one, one, one, one, 10, P(0)) == 3
     assert lib.msa_fwd(None, one, one, one, one, one, one, one, one, one, 10, P(0)) == 1
+    assert lib.msa_index_topk(ctypes.byref(s), P(0), one, one, one, 1 << 40, P(0)) == 1
+    big = m.make_shape(batch=1, seqlen=4096, h_q=4, h_kv=1, top_k=18, softmax_scale=0.1)
+    assert lib.msa_index_topk(ctypes.byref(big), one, one, one, P(0), 1 << 40, P(0)) == 3
+    assert lib.msa_index_topk(ctypes.byref(big), one, one, one, one, 8, P(0)) == 3
     bwd = lib.msa_sparse_attn_bwd
     args = [one] * 10
     for i in range(10):  # each of q, k, v, o, lse, d_o, block_idx, dq, dk, dv

@@ -99,6 +99,48 @@ def test_shapes_parity(msa, N, hq, hkv, k, b):
     _full_parity(msa, w, make_inputs(w))
 
 
+FUSED_SHAPES = SHAPES + [
+    # list length at the register cap (17), past it (two kernels), many heads, full length
+    (4096, 8, 2, 17, 1), (4096, 8, 2, 18, 1), (8192, 32, 8, 16, 1), (131072, 4, 4, 16, 1)]
+
+
+@pytest.mark.parametrize("N,hq,hkv,k,b", FUSED_SHAPES)
+def test_fused_index_topk_matches_the_two_stages(msa, N, hq, hkv, k, b):
+    # one pass (scores, pool and a running per-row list) against msa_index_scores +
+    # msa_block_topk: the same pooled arithmetic and the same order, so identical indices
+    w = small_workload(N, hq, hkv, k, seed=300 + N + hq + k, batch=b)
+    x = make_inputs(w)
+    qi, ki = x["q_idx"].to(DEV), x["k_idx"].to(DEV)
+    _say(w.name, "fused index top-k")
+    fused = msa.index_topk(qi, ki, k)
+    staged = msa.block_topk(msa.index_scores(qi, ki, visible_only=True), k)
+    again = msa.index_topk(qi, ki, k)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, staged)
+    assert torch.equal(fused, again)
+
+
+def test_fused_index_topk_ties_take_lower_blocks(msa):
+    # key blocks repeat with period 3, so every row's block scores tie in threes
+    # (and q_idx = 0 rows tie everywhere): equal scores go to the lower block
+    w = small_workload(4096, 8, 2, 9, seed=41)
+    x = make_inputs(w)
+    qi, ki = x["q_idx"].clone(), x["k_idx"].clone()
+    for c in range(3, w.nblk):
+        ki[:, c * 128:(c + 1) * 128] = ki[:, (c % 3) * 128:(c % 3 + 1) * 128]
+    qi[:, 2000:2100] = 0
+    qi, ki = qi.to(DEV), ki.to(DEV)
+    _say(w.name, "fused index top-k with ties")
+    fused = msa.index_topk(qi, ki, w.top_k)
+    staged = msa.block_topk(msa.index_scores(qi, ki, visible_only=True), w.top_k)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, staged)
+    zero_rows = to_np(fused)[0, :, 2000:2100]
+    t = np.arange(2000, 2100)
+    want = np.concatenate([np.tile(np.arange(8), (100, 1)), (t // 128)[:, None]], axis=1)
+    assert (zero_rows == want[None]).all()
+
+
 def test_dense_reduction_on_gpu(msa):
     # top_k covering every block: the GPU path must equal dense causal GQA attention
     w = small_workload(1024, 8, 2, 8, seed=21)
