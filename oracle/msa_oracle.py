@@ -38,7 +38,9 @@ reason in the design notes at the repository root):
   R8  LSE is the natural log of sum_j exp(scale * q.k_j) over attended keys;
   R9  a row whose selection holds no attendable key (only possible for a
       caller-supplied selection) gets O = 0 and LSE = -inf, the limits of an
-      empty sum.
+      empty sum;
+  R14 a decode step for a sequence of length L computes what the forward
+      computes for position L - 1 over cache rows 0..L-1.
 """
 from __future__ import annotations
 
@@ -314,6 +316,75 @@ def positions_attending(block_idx, block: int, block_size: int = DEFAULT_BLOCK):
     t = np.arange(bi.shape[2])
     hit = np.any(bi == block, axis=-1) & (block <= t // block_size)[None, None]
     return hit  # [B, H_kv, N] boolean
+
+
+# ---------------------------------------------------------------------------
+# Decode: one new query per sequence against its cache
+# ---------------------------------------------------------------------------
+def msa_decode(q_idx, k_idx, q, k, v, seqlens, top_k: int, softmax_scale: float,
+               block_size: int = DEFAULT_BLOCK):
+    """One decode step for a batch of sequences of different lengths.
+
+    [MSA summary] "Why long context is the bottleneck": decoding adds one token
+    at a time against a KV cache that grows with the context; "Architecture"
+    and "Experimental results": the same selection (k = 16 blocks of 128, local
+    block kept) serves decoding. Reading R14: the step for a sequence of length
+    L computes what the forward computes for its last position t = L - 1, over
+    the cache rows 0..t; cache rows at or beyond L are never read.
+
+    q_idx [B, H_idx, D_idx], q [B, H_q, D]: the new token's index query heads
+    and query heads. k_idx [B, C, D_idx], k, v [B, C, H_kv, D]: caches of
+    capacity C >= max(seqlens). seqlens [B]: L per sequence; L = 0 is an empty
+    sequence (block_idx all -1, O = 0, LSE = -inf, as R9).
+
+    Written per sequence and head, without the forward's helpers:
+      s_j = q_idx[b,g] . k_idx[b,j] for j <= t;  pooled_c = max of s_j over
+      block c's rows;  keep c_loc = t // block_size, plus the top_k - 1
+      earlier blocks by (score desc, block asc), output ascending with c_loc
+      last (R3-R6); if c_loc + 1 <= top_k every block 0..c_loc, then -1;
+      o, lse = softmax attention of q[b,h] over the selected blocks' rows <= t.
+    Returns block_idx int32 [B, H_idx, top_k], O float64 [B, H_q, D], LSE [B, H_q].
+    """
+    qi, ki = _f64(q_idx), _f64(k_idx)
+    qq, kk, vv = _f64(q), _f64(k), _f64(v)
+    L = np.asarray(seqlens, dtype=np.int64)
+    B, H_idx, _ = qi.shape
+    _, H_q, D = qq.shape
+    H_kv = kk.shape[2]
+    G = H_q // H_kv
+    if H_idx != H_kv:
+        raise ValueError("one index head per KV head (R7)")
+    if kk.shape[1] < L.max(initial=0):
+        raise ValueError("cache capacity below the longest sequence")
+    sel = np.full((B, H_idx, top_k), -1, dtype=np.int32)
+    out = np.zeros((B, H_q, D))
+    lse = np.full((B, H_q), -np.inf)
+    for b in range(B):
+        n = int(L[b])
+        if n <= 0:
+            continue
+        t = n - 1
+        cl = t // block_size
+        for g in range(H_idx):
+            scores = ki[b, :n] @ qi[b, g]
+            pooled = [scores[c * block_size:min((c + 1) * block_size, n)].max() for c in range(cl + 1)]
+            if cl + 1 <= top_k:
+                chosen = list(range(cl + 1))
+            else:
+                ranked = sorted(range(cl), key=lambda c: (-pooled[c], c))
+                chosen = sorted(ranked[:top_k - 1]) + [cl]
+            sel[b, g, :len(chosen)] = chosen
+        for g in range(H_kv):
+            rows = np.concatenate([np.arange(c * block_size, min((c + 1) * block_size, n))
+                                   for c in sel[b, g] if 0 <= c <= cl])
+            keys, vals = kk[b, rows, g], vv[b, rows, g]
+            for h in range(g * G, (g + 1) * G):
+                z = softmax_scale * (keys @ qq[b, h])
+                m = z.max()
+                w = np.exp(z - m)
+                lse[b, h] = m + np.log(w.sum())
+                out[b, h] = (w / w.sum()) @ vals
+    return sel, out, lse
 
 
 # ---------------------------------------------------------------------------

@@ -17,6 +17,15 @@ Recipe (the same for every workload):
     index scores a block structure, as trained index keys would have);
   * every tensor rounded to bfloat16 (round-to-nearest-even).
 
+Decode workloads (one new token per sequence against its cache) use their own
+generator, ``make_decode_inputs``, on the CPU or on a GPU, in this order:
+  1. L      [B] sequence lengths, uniform integers in [min_len, max_len]
+  2. Q      [B, H_q, 128]      3. Q_idx [B, H_idx, 128]
+  then per sequence b: 4. K [C, H_kv, 128]  5. V [C, H_kv, 128]
+  6. K_idx [C, 128]  7. U [ceil(C/128), 128] unit rows, K_idx[j] += 0.5 U[j // 128]
+with C the cache capacity; cache rows at or beyond L are drawn too (an
+allocation holds whatever it holds) unless ``poison_tail`` fills them with NaN.
+
 The pages measure on trained models and public benchmarks that are not
 available here; these inputs stand in for them with the head shapes the pages
 name (64 query heads, 4 KV heads, head dim 128 for the 109B model).
@@ -109,6 +118,94 @@ def make_inputs(w: Workload, generator_seed: Optional[int] = None) -> Dict[str, 
     if w.with_grad:
         out["d_o"] = torch.randn((B, N, w.h_q, w.head_dim), generator=g, dtype=f32).to(torch.bfloat16)
     return out
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    batch: int
+    capacity: int
+    h_q: int
+    h_kv: int
+    h_idx: int
+    top_k: int
+    seed: int
+    min_len: int
+    max_len: int
+    head_dim: int = HEAD_DIM
+    idx_dim: int = HEAD_DIM
+    block_size: int = BLOCK_SIZE
+    offset_scale: float = 0.5
+
+    @property
+    def nblk(self) -> int:
+        return -(-self.capacity // self.block_size)
+
+    @property
+    def group(self) -> int:
+        return self.h_q // self.h_kv
+
+    @property
+    def softmax_scale(self) -> float:
+        return self.head_dim ** -0.5
+
+    def replace(self, **kw) -> "DecodeWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+DECODE_WORKLOADS: Dict[str, DecodeWorkload] = {
+    # the deployment batch of the pages' selection kernel (128 sequences, top-16) on the
+    # 109B model's attention shape, contexts of 64K-128K tokens
+    "dec_b128_n128k": DecodeWorkload("dec_b128_n128k", batch=128, capacity=131072, h_q=64, h_kv=4, h_idx=4,
+                                     top_k=16, seed=5, min_len=65536, max_len=131072),
+    # 16 sequences of 768K-1M tokens: the context length of the pages' decoding figure
+    "dec_b16_n1m": DecodeWorkload("dec_b16_n1m", batch=16, capacity=1048576, h_q=64, h_kv=4, h_idx=4,
+                                  top_k=16, seed=6, min_len=786432, max_len=1048576),
+}
+
+
+def make_decode_inputs(w: DecodeWorkload, device: str = "cpu", poison_tail: bool = False,
+                       lengths: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Draw a decode step's inputs on `device` (bfloat16, seqlens int32).
+
+    Returns q, q_idx [B, H, 128]; k, v [B, C, H_kv, 128]; k_idx [B, C, 128];
+    seqlens [B]. `lengths` overrides the drawn lengths (the draws still happen,
+    so the other tensors do not change)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed)
+    B, C = w.batch, w.capacity
+    f32, bf = torch.float32, torch.bfloat16
+    seqlens = torch.randint(w.min_len, w.max_len + 1, (B,), generator=g, device=device, dtype=torch.int64)
+    if lengths is not None:
+        seqlens = torch.as_tensor(lengths, dtype=torch.int64, device=device).clone()
+    q = torch.randn((B, w.h_q, w.head_dim), generator=g, device=device, dtype=f32).to(bf)
+    q_idx = torch.randn((B, w.h_idx, w.idx_dim), generator=g, device=device, dtype=f32).to(bf)
+    k = torch.empty((B, C, w.h_kv, w.head_dim), device=device, dtype=bf)
+    v = torch.empty_like(k)
+    k_idx = torch.empty((B, C, w.idx_dim), device=device, dtype=bf)
+    nb = -(-C // w.block_size)
+    block_of = torch.arange(C, device=device) // w.block_size
+    for b in range(B):
+        k[b] = torch.randn((C, w.h_kv, w.head_dim), generator=g, device=device, dtype=f32).to(bf)
+        v[b] = torch.randn((C, w.h_kv, w.head_dim), generator=g, device=device, dtype=f32).to(bf)
+        ki = torch.randn((C, w.idx_dim), generator=g, device=device, dtype=f32)
+        u = torch.randn((nb, w.idx_dim), generator=g, device=device, dtype=f32)
+        u = u / u.norm(dim=-1, keepdim=True)
+        k_idx[b] = (ki + w.offset_scale * u[block_of]).to(bf)
+        if poison_tail:
+            n = int(seqlens[b])
+            k[b, n:] = float("nan")
+            v[b, n:] = float("nan")
+            k_idx[b, n:] = float("nan")
+    return {"q": q, "q_idx": q_idx, "k": k, "v": v, "k_idx": k_idx, "seqlens": seqlens.to(torch.int32)}
+
+
+def small_decode_workload(capacity: int, h_q: int, h_kv: int, top_k: int, seed: int, batch: int,
+                          min_len: int = 1, max_len: Optional[int] = None) -> DecodeWorkload:
+    """A named-by-shape decode workload for parity tests."""
+    return DecodeWorkload(f"dec_b{batch}_c{capacity}_hq{h_q}_hkv{h_kv}_k{top_k}_s{seed}", batch=batch,
+                          capacity=capacity, h_q=h_q, h_kv=h_kv, h_idx=h_kv, top_k=top_k, seed=seed,
+                          min_len=min_len, max_len=capacity if max_len is None else max_len)
 
 
 def small_workload(seqlen: int, h_q: int, h_kv: int, top_k: int, seed: int, batch: int = 1,
