@@ -10,9 +10,10 @@ already resident in HBM when the timed region starts; each stage is bracketed
 by HIP events on the stream the library launches on.
 
 Prints ONE JSON line (rank 0): the contract fields, the roofline of the
-dominant kernel, per-stage figures, the CPU oracle baseline, and (unless
+dominant kernel, per-stage figures, the CPU oracle baseline, (unless
 --no-backward) a "backward" object: msa_sparse_attn_bwd timed at the
-64K-token training shape.
+64K-token training shape, and (unless --no-decode) a "decode" object: one
+decode step (msa_decode's three stages) for 128 sequences of 64K-128K tokens.
 
     python bench.py [--steps K] [--warmup W] [--workload n128k] [--gpus 1]
 """
@@ -40,6 +41,11 @@ STAGE_KERNEL = {
     "combine": ("k_combine", "k_combine.hip", "hbm"),
 }
 SHARED_HEADERS = ("msa_device.hpp", "msa_internal.hpp")
+DECODE_KERNEL = {
+    "index": ("k_dec_index", "k_decode.hip"),
+    "topk": ("k_dec_topk", "k_decode.hip"),
+    "attn": ("k_dec_attn", "k_decode.hip"),
+}
 
 
 def source_sha(fname: str) -> str:
@@ -145,6 +151,71 @@ def backward_report(w, steps: int, warmup: int):
             "fwd_ms_same_shape": round(res["fwd"], 4)}
 
 
+def decode_report(w, steps: int, warmup: int):
+    """Time one decode step per stage with HIP events; inputs drawn on the GPU."""
+    import torch
+
+    from block_sparse_attention_head_amd import msa
+    from block_sparse_attention_head_amd import perfmodel as P
+    from synth.msa_inputs import make_decode_inputs
+
+    print(f"[bench] decode: generating {w.name} inputs on the GPU", file=sys.stderr, flush=True)
+    x = make_decode_inputs(w, device="cuda:0")
+    B, C, Hq, Hkv, K = w.batch, w.capacity, w.h_q, w.h_kv, w.top_k
+    dev = x["q"].device
+    pooled = torch.empty((B, Hkv, C // 128), dtype=torch.float32, device=dev)
+    bi = torch.empty((B, Hkv, K), dtype=torch.int32, device=dev)
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        msa.decode_index_scores(x["q_idx"], x["k_idx"], x["seqlens"], pooled)
+        if ev is not None:
+            ev[1].record()
+        msa.decode_topk(pooled, x["seqlens"], K, C, bi)
+        if ev is not None:
+            ev[2].record()
+        msa.decode_attn(x["q"], x["k"], x["v"], x["seqlens"], bi, w.softmax_scale, o, lse)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for e in evs:
+        step(e)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    lens = x["seqlens"].tolist()
+    nbytes = P.decode_bytes(lens, Hq, Hkv, K)
+    stages = {}
+    for j, name in enumerate(("index", "topk", "attn")):
+        ms = sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
+        gbs = nbytes[name] / 1e9 / (ms / 1e3)
+        kern, src = DECODE_KERNEL[name]
+        stages[name] = {"ms": round(ms, 4), "algorithmic_GB": round(nbytes[name] / 1e9, 4), "achieved": round(gbs, 1),
+                        "unit": "GB/s", "frac": round(gbs / P.PEAK_HBM_GBS, 4), "kernel": kern,
+                        "traffic": _traffic(kern, w.name, src)}
+    del x, pooled, bi, o, lse
+    torch.cuda.empty_cache()
+    total = sum(nbytes.values())
+    return {"workload": w.name,
+            "config": {"batch": B, "cache_capacity": C, "seqlen_min": min(lens), "seqlen_max": max(lens),
+                       "seqlen_mean": round(sum(lens) / len(lens), 1), "h_q": Hq, "h_kv": Hkv, "h_idx": w.h_idx,
+                       "top_k": K, "seed": w.seed},
+            "what": "msa_decode stages: one new token per sequence against its KV cache",
+            "ms_per_step": round(ms_step, 4), "tokens_s": round(B / (ms_step / 1e3), 1),
+            "achieved_GBs": round(total / 1e9 / (ms_step / 1e3), 1),
+            "frac_of_hbm": round(total / 1e9 / (ms_step / 1e3) / P.PEAK_HBM_GBS, 4),
+            "stages": stages}
+
+
 def two_kernel_selection(msa, xg, w, block_idx_single, steps: int, warmup: int):
     """msa_index_scores (pooled scores to HBM) then msa_block_topk, on the step's inputs,
     timed with HIP events per kernel; the indices must equal the single pass's."""
@@ -187,6 +258,10 @@ def main(argv=None) -> int:
     ap.add_argument("--backward-workload", default="n64k_train")
     ap.add_argument("--backward-only", action="store_true",
                     help="only the backward measurement (a JSON line with the backward object), for profiling")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
+    ap.add_argument("--decode-workload", default="dec_b128_n128k")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode measurement (a JSON line with the decode object), for profiling")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one plain 1 GiB device-to-device copy (counter calibration)")
     a = ap.parse_args(argv)
@@ -201,11 +276,19 @@ def main(argv=None) -> int:
 
     from block_sparse_attention_head_amd import msa
     from block_sparse_attention_head_amd import perfmodel as P
-    from synth.msa_inputs import WORKLOADS, make_inputs
+    from synth.msa_inputs import DECODE_WORKLOADS, WORKLOADS, make_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 3
+    if a.decode_only:
+        out = {"decode": decode_report(DECODE_WORKLOADS[a.decode_workload], a.steps, a.warmup)}
+        if a.copy_calibration:
+            src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+            torch.empty_like(src).copy_(src)
+            torch.cuda.synchronize()
+        print(json.dumps(out), flush=True)
+        return 0
     if a.backward_only:
         print(json.dumps({"backward": backward_report(WORKLOADS[a.backward_workload], a.steps, a.warmup)}), flush=True)
         return 0
@@ -327,6 +410,8 @@ def main(argv=None) -> int:
     torch.cuda.empty_cache()
     if not a.no_backward:
         out["backward"] = backward_report(WORKLOADS[a.backward_workload], a.steps, a.warmup)
+    if not a.no_decode:
+        out["decode"] = decode_report(DECODE_WORKLOADS[a.decode_workload], a.steps, a.warmup)
     if not a.no_cpu_baseline:
         print(f"[bench] CPU oracle baseline (~{a.cpu_budget:.0f} s)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, x, a.cpu_budget)

@@ -1,0 +1,362 @@
+// Decode step: one new query per sequence against its KV cache.
+//
+// [MSA summary] "Why long context is the bottleneck": decoding adds one token
+// at a time against a cache that grows with the context; "Architecture" and
+// "Experimental results": the same index branch and selection (k blocks of
+// 128, local block kept) serve decoding. The step for a sequence of length L
+// computes what the forward computes for its last position t = L - 1, over
+// cache rows 0..t. Every stage streams from HBM with little reuse, so the
+// kernels are laid out for bandwidth:
+//   k_dec_index  scores of the H_idx index heads against every cached index key,
+//                max-pooled per 128-key block (one wave per block);
+//   k_dec_topk   the selection per (sequence, index head) row;
+//   k_dec_attn   softmax attention of each query head over its group's blocks.
+#include "msa_device.hpp"
+#include "msa_internal.hpp"
+#include "msa_topk.hpp"
+
+namespace msa {
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(3))) bf16x4* lds_bf16x4_ptr;
+
+// s_waitcnt vmcnt(0) only (gfx9 encoding), after a compiler barrier so no LDS read moves above it
+#define MSA_DEC_WAIT_VMCNT0()                  \
+    do {                                       \
+        asm volatile("" ::: "memory");         \
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); \
+    } while (0)
+
+constexpr int kDecIdxWaves = 4;   // key blocks per index workgroup (one per wave)
+constexpr int kDecAttnWaves = 4;  // 32 keys of every selected block per wave
+
+// Sequence length as the kernels use it: clamped to the cache capacity; <= 0 is empty.
+__device__ __forceinline__ int dec_len(const int32_t* __restrict__ seqlens, int b, int C) {
+    return min(seqlens[b], C);
+}
+
+// ---------------------------------------------------------------------------
+// Index scores + block max. A wave owns key block c of sequence b: the block's
+// 128 index keys are the A operand of v_mfma_f32_16x16x32_bf16 (16 keys x 32
+// dims per tile, lane l reading key l % 16, dims 32kk + 8(l/16) .. +7 straight
+// from memory), the index queries of up to 16 heads the B operand. The result
+// holds keys 4(l/16) + i of head l % 16 in lane l, so the block max is an
+// in-lane max plus two exchanges. Keys past t are masked (and never loaded:
+// their rows are clamped to t). Blocks after the sequence's own get -inf.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_dec_index(const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx,
+                                                   const int32_t* __restrict__ seqlens, float* __restrict__ pooled,
+                                                   int C, int H, int nblk) {
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = blockIdx.x * kDecIdxWaves + wave;
+    if (c >= nblk) return;
+    const int L = dec_len(seqlens, b, C);
+    const int t = L - 1;
+    const int cl = L > 0 ? t / kBlock : -1;
+    float* prow = pooled + (size_t)b * H * nblk + c;
+    if (c > cl) {
+        for (int g = lane; g < H; g += 64) prow[(size_t)g * nblk] = -INFINITY;
+        return;
+    }
+    const int q4 = lane >> 4, n = lane & 15;
+    const int rmax = t - c * kBlock;  // last valid key of the block (>= 0)
+    const __bf16* kb = k_idx + ((size_t)b * C + (size_t)c * kBlock) * kDim;
+    bf16x8 kf[8][4];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+        const int row = min(16 * mt + n, rmax);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) kf[mt][kk] = *(const bf16x8*)(kb + (size_t)row * kDim + 32 * kk + 8 * q4);
+    }
+    for (int ht = 0; ht < H; ht += 16) {
+        const int h = ht + n;
+        bf16x8 qf[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if (h < H) {
+                qf[kk] = *(const bf16x8*)(q_idx + ((size_t)b * H + h) * kDim + 32 * kk + 8 * q4);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)0.0f;
+            }
+        }
+        float m = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acc = mfma16(kf[mt][kk], qf[kk], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (16 * mt + 4 * q4 + i <= rmax) m = fmaxf(m, acc[i]);
+        }
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        if (q4 == 0 && h < H) prow[(size_t)h * nblk] = m;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Selection per (sequence, index head) row, one wave each: the same steps as the
+// forward's selection kernel on a row of any length. The lane maxima of the
+// 32-bit score keys give T, the (top_k-1)-th largest; every key of the exact
+// selection is >= T; candidates >= T go to an LDS list of 64-bit (score, block)
+// keys (sized for the whole row, so any tie pattern fits) and are ranked exactly.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_dec_topk(const float* __restrict__ pooled, const int32_t* __restrict__ seqlens,
+                                                 int32_t* __restrict__ block_idx, int C, int H, int nblk, int top_k) {
+    extern __shared__ __attribute__((aligned(16))) uint64_t dec_list[];  // nblk + 4 keys, then 64 ints
+    const int row = blockIdx.x, b = row / H;
+    const int lane = threadIdx.x;
+    const int L = dec_len(seqlens, b, C);
+    int32_t* dst = block_idx + (size_t)row * top_k;
+    if (L <= 0) {
+        for (int s = lane; s < top_k; s += 64) dst[s] = -1;
+        return;
+    }
+    const int cl = (L - 1) / kBlock;
+    if (cl + 1 <= top_k) {  // every visible block
+        for (int s = lane; s < top_k; s += 64) dst[s] = s <= cl ? s : -1;
+        return;
+    }
+    const int need = top_k - 1;
+    if (need == 0) {
+        if (lane == 0) dst[0] = cl;
+        return;
+    }
+    const float* src = pooled + (size_t)row * nblk;
+    uint32_t lmax = 0u;
+    for (int c = lane; c < cl; c += 64) {
+        const uint32_t k = order_key(src[c]);
+        lmax = k > lmax ? k : lmax;
+    }
+    // need <= 64 and cl >= need + 1, so at least `need` lanes hold a block
+    uint32_t T = 0u;
+#pragma unroll
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand_t = T | (1u << bit);
+        if (__popcll(__ballot(lmax >= cand_t)) >= need) T = cand_t;
+    }
+    uint64_t* list = dec_list;
+    int32_t* chosen = (int32_t*)(dec_list + nblk + 4);
+    int n = 0;
+    for (int c0 = 0; c0 < cl; c0 += 64) {
+        const int c = c0 + lane;
+        const uint32_t k = c < cl ? order_key(src[c]) : 0u;
+        const bool take = c < cl && k >= T;
+        const uint64_t mask = __ballot(take);
+        if (take)
+            list[n + __popcll(mask & ((1ull << lane) - 1ull))] =
+                ((uint64_t)k << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)c);
+        n += __popcll(mask);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    rank_and_emit(list, chosen, n, need, cl, dst, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Attention over the selected blocks. A workgroup owns (sequence b, KV head g,
+// a tile of up to 16 of the group's query heads); wave w takes keys
+// 32w .. 32w+31 of every selected block and keeps an online softmax over them.
+//   S^T = K Q^T: K rows are the A operand, read from memory (rows past t clamped
+//   to t and masked), Q the B operand; lane l holds keys 16mt + 4(l/16) + i of
+//   head l % 16.
+//   O += P V: those P values, rounded to bf16, are the A operand as they sit in
+//   the registers (lane l: head l % 16; slot e of the 8 goes to key
+//   16(e/4) + 4(l/16) + e%4); the V rows of the same keys come from the wave's
+//   LDS tile (filled by global->LDS loads) through ds_read_b64_tr_b16, which
+//   hands each lane one dim of 4 consecutive keys.
+// The four waves' (m, l, O) are merged in LDS at the end.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bf16x4 dec_tr_rows4(const __bf16* tile, int r0, int c0, int li) {
+    const int row = r0 + (li >> 2), col = c0 + 4 * (li & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(tile + row * kDim + col));
+}
+
+__global__ __launch_bounds__(256) void k_dec_attn(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                                  const __bf16* __restrict__ v, const int32_t* __restrict__ seqlens,
+                                                  const int32_t* __restrict__ block_idx, __bf16* __restrict__ o,
+                                                  float* __restrict__ lse, int C, int Hq, int Hkv, int G, int top_k,
+                                                  float scale_log2) {
+    const int ht = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q4 = lane >> 4, n = lane & 15;
+    const int L = dec_len(seqlens, b, C);
+    const int t = L - 1;
+    const int cl = L > 0 ? t / kBlock : -1;
+    const int h0 = g * G + ht * 16;
+    const int hn = min(16, G - ht * 16);
+
+    __shared__ __attribute__((aligned(16))) __bf16 vs[kDecAttnWaves][32 * kDim];  // 8 KB of V rows per wave
+    __shared__ float sm[kDecAttnWaves][16], sl[kDecAttnWaves][16];
+    __bf16* vw = vs[wave];
+
+    bf16x8 qf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        if (n < hn) {
+            qf[kk] = *(const bf16x8*)(q + ((size_t)b * Hq + h0 + n) * kDim + 32 * kk + 8 * q4);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)0.0f;
+        }
+    }
+    float m_run = -INFINITY, l_run = 0.0f;  // of head n, over this wave's keys so far
+    f32x4 oacc[8];                          // O[head 4(l/16) + i][dim 16dt + l % 16]
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oacc[dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int32_t* sel = block_idx + ((size_t)b * Hkv + g) * top_k;
+    const size_t kv_row = (size_t)Hkv * kDim;  // elements between consecutive cache rows
+    const __bf16* kseq = k + ((size_t)b * C * Hkv + g) * kDim;
+    const __bf16* vseq = v + ((size_t)b * C * Hkv + g) * kDim;
+    for (int s = 0; s < top_k; ++s) {
+        const int c = sel[s];
+        if (c < 0 || c > cl) continue;  // padding or not visible
+        const int kbase = c * kBlock + 32 * wave;
+        const int rmax = t - kbase;  // last valid key of this wave's 32
+        if (rmax < 0) continue;      // the whole slice lies after t
+        // V rows kbase .. kbase+31 (clamped to t) into LDS, row-major: instruction i
+        // fills rows 4i .. 4i+3, lane l row 4i + l/16, dims 8(l%16) .. +7
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = min(4 * i + (lane >> 4), rmax);
+            __builtin_amdgcn_global_load_lds((const void*)(vseq + (size_t)(kbase + r) * kv_row + 8 * (lane & 15)),
+                                             (lds_ptr)(vw + 4 * i * kDim), 16, 0, 0);
+        }
+        bf16x8 kf[2][4];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int r = min(16 * mt + n, rmax);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                kf[mt][kk] = *(const bf16x8*)(kseq + (size_t)(kbase + r) * kv_row + 32 * kk + 8 * q4);
+        }
+        f32x4 sacc[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            sacc[mt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) sacc[mt] = mfma16(kf[mt][kk], qf[kk], sacc[mt]);
+        }
+        float mb = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float sv = (16 * mt + 4 * q4 + i <= rmax) ? sacc[mt][i] * scale_log2 : -INFINITY;
+                sacc[mt][i] = sv;
+                mb = fmaxf(mb, sv);
+            }
+        mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+        mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+        const float m_new = fmaxf(m_run, mb);  // finite: key kbase <= t is valid
+        const float alpha = exp2f(m_run - m_new);
+        float ps = 0.0f;
+        bf16x8 pa;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = exp2f(sacc[mt][i] - m_new);
+                ps += p;
+                pa[4 * mt + i] = (__bf16)p;
+            }
+        ps += __shfl_xor(ps, 16, 64);
+        ps += __shfl_xor(ps, 32, 64);
+        l_run = l_run * alpha + ps;
+        m_run = m_new;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float a = __shfl(alpha, 4 * q4 + i, 64);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) oacc[dt][i] *= a;
+        }
+        MSA_DEC_WAIT_VMCNT0();  // this wave's V rows have landed in LDS
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const bf16x4 lo = dec_tr_rows4(vw, 4 * q4, 16 * dt, n);
+            const bf16x4 hi = dec_tr_rows4(vw, 16 + 4 * q4, 16 * dt, n);
+            const bf16x8 vb = (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            oacc[dt] = mfma16(pa, vb, oacc[dt]);
+        }
+    }
+
+    // merge the four waves: weights 2^(m_w - M) per head, O and l summed
+    __syncthreads();  // every wave is done with its V tile; the tiles become the merge buffer
+    float* red = (float*)&vs[0][0];  // [wave][16 heads][128 dims] fp32, 32 KB
+    if (q4 == 0) {
+        sm[wave][n] = m_run;
+        sl[wave][n] = l_run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int h = 4 * q4 + i;
+        float M = sm[0][h];
+#pragma unroll
+        for (int w = 1; w < kDecAttnWaves; ++w) M = fmaxf(M, sm[w][h]);
+        const float mw = sm[wave][h];
+        const float wt = mw == -INFINITY ? 0.0f : exp2f(mw - M);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) red[(wave * 16 + h) * kDim + 16 * dt + n] = oacc[dt][i] * wt;
+    }
+    __syncthreads();
+    const int h = tid >> 4, d0 = (tid & 15) * 8;
+    if (h >= hn) return;
+    float M = sm[0][h];
+#pragma unroll
+    for (int w = 1; w < kDecAttnWaves; ++w) M = fmaxf(M, sm[w][h]);
+    float Lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kDecAttnWaves; ++w) Lsum += sm[w][h] == -INFINITY ? 0.0f : exp2f(sm[w][h] - M) * sl[w][h];
+    const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+    bf16x8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kDecAttnWaves; ++w) acc += red[(w * 16 + h) * kDim + d0 + e];
+        out[e] = (__bf16)(acc * inv);
+    }
+    *(bf16x8*)(o + ((size_t)b * Hq + h0 + h) * kDim + d0) = out;
+    if ((tid & 15) == 0)
+        lse[(size_t)b * Hq + h0 + h] = Lsum > 0.0f ? (M + log2f(Lsum)) * 0.69314718055994531f : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+size_t dec_topk_lds_bytes(const Dims& d) { return ((size_t)d.nblk + 4) * 8 + 64 * 4; }
+
+hipError_t launch_dec_index(const void* q_idx, const void* k_idx, const int32_t* seqlens, float* pooled, const Dims& d,
+                            hipStream_t stream) {
+    dim3 grid((unsigned)((d.nblk + kDecIdxWaves - 1) / kDecIdxWaves), (unsigned)d.B);
+    hipLaunchKernelGGL(k_dec_index, grid, dim3(64 * kDecIdxWaves), 0, stream, (const __bf16*)q_idx,
+                       (const __bf16*)k_idx, seqlens, pooled, d.N, d.Hkv, d.nblk);
+    return hipGetLastError();
+}
+
+hipError_t launch_dec_topk(const float* pooled, const int32_t* seqlens, int32_t* block_idx, const Dims& d,
+                           hipStream_t stream) {
+    const size_t lds = dec_topk_lds_bytes(d);
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute((const void*)k_dec_topk, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_dec_topk, dim3((unsigned)(d.B * d.Hkv)), dim3(64), lds, stream, pooled, seqlens, block_idx,
+                       d.N, d.Hkv, d.nblk, d.top_k);
+    return hipGetLastError();
+}
+
+hipError_t launch_dec_attn(const void* q, const void* k, const void* v, const int32_t* seqlens,
+                           const int32_t* block_idx, void* o, float* lse, const Dims& d, hipStream_t stream) {
+    dim3 grid((unsigned)((d.G + 15) / 16), (unsigned)d.Hkv, (unsigned)d.B);
+    hipLaunchKernelGGL(k_dec_attn, grid, dim3(64 * kDecAttnWaves), 0, stream, (const __bf16*)q, (const __bf16*)k,
+                       (const __bf16*)v, seqlens, block_idx, (__bf16*)o, lse, d.N, d.Hq, d.Hkv, d.G, d.top_k,
+                       d.scale * 1.4426950408889634f);
+    return hipGetLastError();
+}
+
+}  // namespace msa

@@ -57,6 +57,38 @@ msa_status check_shape(const msa_shape* s, Dims* d) {
     return MSA_OK;
 }
 
+// Decode: shape->seqlen is the cache capacity C. Host only.
+constexpr int kDecMaxCapacity = 1 << 21;  // keeps the selection's LDS list (8 B per block) within 160 KB
+
+msa_status check_decode_shape(const msa_shape* s, Dims* d) {
+    if (!s || !d) return MSA_ERR_INVALID_ARG;
+    if (s->batch < 1 || s->seqlen < 1 || s->h_q < 1 || s->h_kv < 1 || s->h_idx < 1 || s->top_k < 1)
+        return MSA_ERR_INVALID_ARG;
+    if (s->h_q % s->h_kv != 0) return MSA_ERR_INVALID_ARG;
+    if (!(s->softmax_scale > 0.0f) || !isfinite(s->softmax_scale)) return MSA_ERR_INVALID_ARG;
+    if (!(s->flags & MSA_CAUSAL)) return MSA_ERR_UNSUPPORTED;
+    if (s->head_dim != kDim || s->idx_dim != kDim || s->block_size != kBlock) return MSA_ERR_UNSUPPORTED;
+    if (s->h_idx != s->h_kv) return MSA_ERR_UNSUPPORTED;
+    const int G = s->h_q / s->h_kv;
+    if (!is_pow2(G) || G > kBlock) return MSA_ERR_UNSUPPORTED;
+    if (s->seqlen % kBlock != 0 || s->seqlen > kDecMaxCapacity) return MSA_ERR_UNSUPPORTED;
+    if (s->top_k > 65) return MSA_ERR_UNSUPPORTED;  // the exact rank emits at most one block per lane
+    if (s->batch > 65535 || s->h_kv > 65535) return MSA_ERR_UNSUPPORTED;  // grid y / z extents
+    if ((double)s->batch * s->h_kv >= 2147483647.0) return MSA_ERR_UNSUPPORTED;
+    d->B = s->batch;
+    d->N = s->seqlen;
+    d->Hq = s->h_q;
+    d->Hkv = s->h_kv;
+    d->G = G;
+    d->gshift = log2i(G);
+    d->nblk = s->seqlen / kBlock;
+    d->top_k = s->top_k;
+    d->scale = s->softmax_scale;
+    return MSA_OK;
+}
+
+size_t dec_ws_bytes(const Dims& d) { return align_up((size_t)d.B * d.Hkv * d.nblk * sizeof(float), 256); }
+
 }  // namespace
 
 namespace {
@@ -143,6 +175,7 @@ size_t ws_bytes(const Dims& d, msa_op op) {
         case MSA_OP_FWD: return index_topk_ws_bytes(d) + sparse_ws_bytes(d);
         case MSA_OP_SPARSE_ATTN_BWD: return bwd_ws_bytes(d);
         case MSA_OP_INDEX_TOPK: return index_topk_ws_bytes(d);
+        case MSA_OP_DECODE: return dec_ws_bytes(d);
     }
     return 0;
 }
@@ -182,8 +215,14 @@ extern "C" {
 
 msa_status msa_workspace_size(const msa_shape* shape, msa_op op, size_t* bytes) {
     if (!bytes) return MSA_ERR_INVALID_ARG;
-    if (op < MSA_OP_INDEX_SCORES || op > MSA_OP_INDEX_TOPK) return MSA_ERR_INVALID_ARG;
+    if (op < MSA_OP_INDEX_SCORES || op > MSA_OP_DECODE) return MSA_ERR_INVALID_ARG;
     Dims d;
+    if (op == MSA_OP_DECODE) {
+        const msa_status st = check_decode_shape(shape, &d);
+        if (st != MSA_OK) return st;
+        *bytes = dec_ws_bytes(d);
+        return MSA_OK;
+    }
     const msa_status st = check_shape(shape, &d);
     if (st != MSA_OK) return st;
     *bytes = ws_bytes(d, op);
@@ -296,6 +335,53 @@ msa_status msa_index_topk(const msa_shape* shape, const void* q_idx, const void*
     if (need > 0 && (!workspace || workspace_bytes < need)) return MSA_ERR_WORKSPACE;
     (void)hipGetLastError();
     return hip_status(run_index_topk(q_idx, k_idx, block_idx, workspace, d, stream));
+}
+
+msa_status msa_decode_index_scores(const msa_shape* shape, const void* q_idx, const void* k_idx,
+                                   const int32_t* seqlens, float* pooled, hipStream_t stream) {
+    Dims d;
+    const msa_status st = check_decode_shape(shape, &d);
+    if (st != MSA_OK) return st;
+    if (!q_idx || !k_idx || !seqlens || !pooled) return MSA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return hip_status(launch_dec_index(q_idx, k_idx, seqlens, pooled, d, stream));
+}
+
+msa_status msa_decode_topk(const msa_shape* shape, const float* pooled, const int32_t* seqlens, int32_t* block_idx,
+                           hipStream_t stream) {
+    Dims d;
+    const msa_status st = check_decode_shape(shape, &d);
+    if (st != MSA_OK) return st;
+    if (!pooled || !seqlens || !block_idx) return MSA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return hip_status(launch_dec_topk(pooled, seqlens, block_idx, d, stream));
+}
+
+msa_status msa_decode_attn(const msa_shape* shape, const void* q, const void* k, const void* v,
+                           const int32_t* seqlens, const int32_t* block_idx, void* o, float* lse,
+                           hipStream_t stream) {
+    Dims d;
+    const msa_status st = check_decode_shape(shape, &d);
+    if (st != MSA_OK) return st;
+    if (!q || !k || !v || !seqlens || !block_idx || !o || !lse) return MSA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return hip_status(launch_dec_attn(q, k, v, seqlens, block_idx, o, lse, d, stream));
+}
+
+msa_status msa_decode(const msa_shape* shape, const void* q_idx, const void* k_idx, const void* q, const void* k,
+                      const void* v, const int32_t* seqlens, int32_t* block_idx, void* o, float* lse,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    Dims d;
+    const msa_status st = check_decode_shape(shape, &d);
+    if (st != MSA_OK) return st;
+    if (!q_idx || !k_idx || !q || !k || !v || !seqlens || !block_idx || !o || !lse) return MSA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < dec_ws_bytes(d)) return MSA_ERR_WORKSPACE;
+    (void)hipGetLastError();
+    float* pooled = (float*)workspace;
+    hipError_t e = launch_dec_index(q_idx, k_idx, seqlens, pooled, d, stream);
+    if (e == hipSuccess) e = launch_dec_topk(pooled, seqlens, block_idx, d, stream);
+    if (e == hipSuccess) e = launch_dec_attn(q, k, v, seqlens, block_idx, o, lse, d, stream);
+    return hip_status(e);
 }
 
 msa_status msa_sparse_attn_bwd(const msa_shape* shape, const void* q, const void* k, const void* v, const void* o,

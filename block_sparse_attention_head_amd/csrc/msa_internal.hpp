@@ -22,6 +22,18 @@ struct Dims {
 hipError_t launch_index_pool(const void* q_idx, const void* k_idx, float* pooled, const Dims& d,
                              bool fill_upper, hipStream_t stream);
 
+// Decode step (one query per sequence; seqlens on the device, clamped to the
+// capacity d.N, <= 0 empty): index scores + block max into pooled [B, H, nblk],
+// the selection into block_idx [B, H, top_k], attention into o [B, Hq, 128] and
+// lse [B, Hq]. The selection needs dec_topk_lds_bytes(d) of LDS.
+size_t dec_topk_lds_bytes(const Dims& d);
+hipError_t launch_dec_index(const void* q_idx, const void* k_idx, const int32_t* seqlens, float* pooled, const Dims& d,
+                            hipStream_t stream);
+hipError_t launch_dec_topk(const float* pooled, const int32_t* seqlens, int32_t* block_idx, const Dims& d,
+                           hipStream_t stream);
+hipError_t launch_dec_attn(const void* q, const void* k, const void* v, const int32_t* seqlens,
+                           const int32_t* block_idx, void* o, float* lse, const Dims& d, hipStream_t stream);
+
 // Index scores + block max-pool + top-k selection in one pass with no pooled
 // scores in memory and no scratch; needs index_topk_fusable(d) (top_k <= 17).
 bool index_topk_fusable(const Dims& d);

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
 MSA_OK = 0
 MSA_CAUSAL = 1
 MSA_POOLED_VISIBLE_ONLY = 2
-OP_INDEX_SCORES, OP_BLOCK_TOPK, OP_SPARSE_ATTN_FWD, OP_FWD, OP_SPARSE_ATTN_BWD, OP_INDEX_TOPK = 0, 1, 2, 3, 4, 5
+OP_INDEX_SCORES, OP_BLOCK_TOPK, OP_SPARSE_ATTN_FWD, OP_FWD, OP_SPARSE_ATTN_BWD, OP_INDEX_TOPK, OP_DECODE = range(7)
 
 BLOCK_SIZE = 128
 HEAD_DIM = 128
@@ -61,6 +61,10 @@ _SIGNATURES = {
     "msa_fwd": [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "msa_sparse_attn_bwd": [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "msa_index_topk": [_S, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "msa_decode_index_scores": [_S, _P, _P, _P, _P, _P],
+    "msa_decode_topk": [_S, _P, _P, _P, _P],
+    "msa_decode_attn": [_S, _P, _P, _P, _P, _P, _P, _P, _P],
+    "msa_decode": [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
 }
 
 _lib = None
@@ -269,4 +273,92 @@ def msa_fwd(q_idx, k_idx, q, k, v, top_k: int, softmax_scale: float, block_idx=N
     ws = _ws(workspace, shape, OP_FWD, q.device)
     _check("msa_fwd", lib().msa_fwd(ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k), _ptr(v),
                                     _ptr(block_idx), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(q.device)))
+    return block_idx, o, lse
+
+
+# ---------------------------------------------------------------------------
+# Decode: one new query per sequence against its caches (see the decode calls in msa.h)
+# ---------------------------------------------------------------------------
+def _decode_shape(q_idx, k_idx, q, k, v, seqlens, top_k: int, softmax_scale: float) -> MsaShape:
+    B, H, D = q_idx.shape
+    C = k_idx.shape[1]
+    Hq = q.shape[1]
+    Hkv = k.shape[2]
+    _need(q_idx, "q_idx", torch.bfloat16, (B, H, D))
+    _need(k_idx, "k_idx", torch.bfloat16, (B, C, D))
+    _need(q, "q", torch.bfloat16, (B, Hq, D))
+    _need(k, "k", torch.bfloat16, (B, C, Hkv, D))
+    _need(v, "v", torch.bfloat16, (B, C, Hkv, D))
+    _need(seqlens, "seqlens", torch.int32, (B,))
+    if H != Hkv:
+        raise ValueError("one index head per KV head")
+    return make_shape(B, C, Hq, Hkv, top_k, softmax_scale)
+
+
+def decode_index_scores(q_idx, k_idx, seqlens, pooled=None) -> torch.Tensor:
+    """pooled fp32 [B, H_idx, C/128] of the new token (see msa_decode_index_scores)."""
+    B, H, D = q_idx.shape
+    C = k_idx.shape[1]
+    _need(q_idx, "q_idx", torch.bfloat16, (B, H, D))
+    _need(k_idx, "k_idx", torch.bfloat16, (B, C, D))
+    _need(seqlens, "seqlens", torch.int32, (B,))
+    nb = C // 128
+    pooled = torch.empty((B, H, nb), dtype=torch.float32, device=q_idx.device) if pooled is None else pooled
+    _need(pooled, "pooled", torch.float32, (B, H, nb))
+    shape = make_shape(B, C, H, H, 1, 1.0)
+    _check("msa_decode_index_scores", lib().msa_decode_index_scores(
+        ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(seqlens), _ptr(pooled), _stream(q_idx.device)))
+    return pooled
+
+
+def decode_topk(pooled, seqlens, top_k: int, capacity: int, block_idx=None) -> torch.Tensor:
+    """block_idx int32 [B, H_idx, top_k] (see msa_decode_topk)."""
+    B, H, nb = pooled.shape
+    _need(pooled, "pooled", torch.float32, (B, H, capacity // 128))
+    _need(seqlens, "seqlens", torch.int32, (B,))
+    block_idx = torch.empty((B, H, top_k), dtype=torch.int32, device=pooled.device) if block_idx is None \
+        else block_idx
+    _need(block_idx, "block_idx", torch.int32, (B, H, top_k))
+    shape = make_shape(B, capacity, H, H, top_k, 1.0)
+    _check("msa_decode_topk", lib().msa_decode_topk(ctypes.byref(shape), _ptr(pooled), _ptr(seqlens),
+                                                    _ptr(block_idx), _stream(pooled.device)))
+    return block_idx
+
+
+def decode_attn(q, k, v, seqlens, block_idx, softmax_scale: float, o=None, lse=None):
+    """(O bf16 [B, H_q, 128], LSE fp32 [B, H_q]) over the selected blocks (see msa_decode_attn)."""
+    B, Hq, D = q.shape
+    C, Hkv = k.shape[1], k.shape[2]
+    top_k = block_idx.shape[-1]
+    _need(q, "q", torch.bfloat16, (B, Hq, D))
+    _need(k, "k", torch.bfloat16, (B, C, Hkv, D))
+    _need(v, "v", torch.bfloat16, (B, C, Hkv, D))
+    _need(seqlens, "seqlens", torch.int32, (B,))
+    _need(block_idx, "block_idx", torch.int32, (B, Hkv, top_k))
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, "o", torch.bfloat16, (B, Hq, D))
+    _need(lse, "lse", torch.float32, (B, Hq))
+    shape = make_shape(B, C, Hq, Hkv, top_k, softmax_scale)
+    _check("msa_decode_attn", lib().msa_decode_attn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens),
+                                                    _ptr(block_idx), _ptr(o), _ptr(lse), _stream(q.device)))
+    return o, lse
+
+
+def decode(q_idx, k_idx, q, k, v, seqlens, top_k: int, softmax_scale: float, block_idx=None, o=None, lse=None,
+           workspace=None):
+    """(block_idx [B, H_idx, top_k], O [B, H_q, 128], LSE [B, H_q]) of one decode step (see msa_decode)."""
+    shape = _decode_shape(q_idx, k_idx, q, k, v, seqlens, top_k, softmax_scale)
+    B, H, _ = q_idx.shape
+    Hq = q.shape[1]
+    block_idx = torch.empty((B, H, top_k), dtype=torch.int32, device=q.device) if block_idx is None else block_idx
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(block_idx, "block_idx", torch.int32, (B, H, top_k))
+    _need(o, "o", torch.bfloat16, q.shape)
+    _need(lse, "lse", torch.float32, (B, Hq))
+    ws = _ws(workspace, shape, OP_DECODE, q.device)
+    _check("msa_decode", lib().msa_decode(ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(seqlens), _ptr(block_idx), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
+                                          _stream(q.device)))
     return block_idx, o, lse

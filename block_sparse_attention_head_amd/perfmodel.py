@@ -14,6 +14,14 @@ work the method needs, not what a particular kernel happens to do:
   combine          read every partial O row and LSE, read the selection rows,
                    write O (bf16) and LSE (fp32)
 
+Decode (one query per sequence, length L, t = L - 1, c_loc = t // B_k):
+  index            read the L cached index keys (bf16) and the H_idx index
+                   queries; write the c_loc + 1 visible pooled scores per head
+  top-k            read the c_loc earlier pooled scores per head; write top_k int32
+  attention        read the K and V rows of the selected keys (min(top_k,
+                   c_loc + 1) blocks, the local one up to t), the block indices
+                   and the H_q queries; write O (bf16) and LSE (fp32)
+
 Pins (tests): with 64 query heads, 4 index heads, d = d_idx = 128, k = 16,
 B_k = 128 and N = 2^20, full attention needs 28.44x the per-token FLOP of
 MSA ([MSA summary] "Summary" / "Experimental results": 28.4x); KV-outer
@@ -143,3 +151,19 @@ def kv_outer_intensity(block: int, d: int, partial_o_bytes: int = FP32) -> float
 def q_outer_intensity(group: int) -> float:
     """Query-outer: a K/V block is loaded for the G heads of one query, so FLOP/byte equals G."""
     return float(group)
+
+
+def decode_bytes(seqlens, h_q: int, h_kv: int, top_k: int, d: int = HEAD_DIM, block: int = BLOCK):
+    """Algorithmic HBM bytes of one decode step per stage: {'index', 'topk', 'attn'}."""
+    idx = topk = attn = 0.0
+    for L in seqlens:
+        L = int(L)
+        if L <= 0:
+            continue
+        t = L - 1
+        cl = t // block
+        idx += L * d * BF16 + h_kv * d * BF16 + h_kv * (cl + 1) * FP32
+        topk += h_kv * (cl * FP32 + top_k * INT32)
+        keys = (valid_blocks(t, top_k, block) - 1) * block + (t % block + 1)
+        attn += h_kv * (keys * 2 * d * BF16 + top_k * INT32) + h_q * (2 * d * BF16 + FP32)
+    return {"index": idx, "topk": topk, "attn": attn}

@@ -88,7 +88,8 @@ typedef enum msa_op {
     MSA_OP_SPARSE_ATTN_FWD = 2,
     MSA_OP_FWD = 3,
     MSA_OP_SPARSE_ATTN_BWD = 4,
-    MSA_OP_INDEX_TOPK = 5
+    MSA_OP_INDEX_TOPK = 5,
+    MSA_OP_DECODE = 6
 } msa_op;
 
 /* Bytes of device workspace `op` needs for `shape` (0 is a valid answer).
@@ -194,6 +195,45 @@ msa_status msa_sparse_attn_bwd(const msa_shape* shape, const void* q, const void
                                const void* o, const float* lse, const void* d_o,
                                const int32_t* block_idx, void* dq, void* dk, void* dv,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- Decode: one new query per sequence against its KV cache ----
+ * [MSA summary] "Why long context is the bottleneck" (decoding adds one token
+ * at a time against a cache that grows with the context) and "Experimental
+ * results" (the same sparse attention serves decoding). The step for a
+ * sequence of length L computes what msa_fwd computes for its last position
+ * t = L - 1, over cache rows 0..t; rows at or past L are never read.
+ * For these calls shape->seqlen is the cache capacity C (a multiple of 128,
+ * C <= 2^21); 1 <= top_k <= 65; batch and h_kv <= 65535; other fields as for
+ * the forward (the combine bound does not apply).
+ *   q_idx    bf16  [B, H_idx, 128]      the new token's index queries
+ *   q        bf16  [B, H_q, 128]        its queries
+ *   k_idx    bf16  [B, C, 128]          index-key cache
+ *   k, v     bf16  [B, C, H_kv, 128]    KV cache
+ *   seqlens  int32 [B] (device)         L per sequence; L > C is read as C, L <= 0 as
+ *                                        an empty sequence (block_idx -1, o 0, lse -inf)
+ *   pooled   fp32  [B, H_idx, C/128]    block maxima; -inf for blocks past t/128
+ *   block_idx int32 [B, H_idx, top_k]   ascending, local block last, -1 padded
+ *   o        bf16  [B, H_q, 128];  lse fp32 [B, H_q] (natural log) */
+
+/* Index scores of the new token against every cached index key, max-pooled per block. */
+msa_status msa_decode_index_scores(const msa_shape* shape, const void* q_idx, const void* k_idx,
+                                   const int32_t* seqlens, float* pooled, hipStream_t stream);
+
+/* Selection per (sequence, index head) with the same rule as msa_block_topk, on rows of
+ * any length up to the capacity. */
+msa_status msa_decode_topk(const msa_shape* shape, const float* pooled, const int32_t* seqlens,
+                           int32_t* block_idx, hipStream_t stream);
+
+/* Softmax attention of each query head over its group's selected blocks (entries
+ * outside [0, t/128] ignored; a repeated entry counts twice, as in the forward). */
+msa_status msa_decode_attn(const msa_shape* shape, const void* q, const void* k, const void* v,
+                           const int32_t* seqlens, const int32_t* block_idx, void* o, float* lse,
+                           hipStream_t stream);
+
+/* The three steps in turn; the pooled scores live in the workspace (MSA_OP_DECODE). */
+msa_status msa_decode(const msa_shape* shape, const void* q_idx, const void* k_idx, const void* q,
+                      const void* k, const void* v, const int32_t* seqlens, int32_t* block_idx,
+                      void* o, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, never-NULL description of a status code. */
 const char* msa_status_string(msa_status status);

@@ -101,7 +101,7 @@ def test_unsupported_dims_and_flags(m):
         setattr(t, field, val)
         assert m.lib().msa_workspace_size(ctypes.byref(t), m.OP_FWD, ctypes.byref(n)) == 2, field
     assert m.lib().msa_workspace_size(ctypes.byref(s), 9, ctypes.byref(n)) == 1
-    assert m.lib().msa_workspace_size(ctypes.byref(s), 6, ctypes.byref(n)) == 1
+    assert m.lib().msa_workspace_size(ctypes.byref(s), 7, ctypes.byref(n)) == 1
     assert m.lib().msa_workspace_size(None, m.OP_FWD, ctypes.byref(n)) == 1
     assert m.lib().msa_workspace_size(ctypes.byref(s), m.OP_FWD, None) == 1
 
@@ -148,3 +148,34 @@ def test_binding_rejects_cpu_tensors(m):
     k = torch.zeros(1, 128, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         m.index_scores(q, k)
+
+
+def test_decode_shape_validation_and_workspace(m):
+    lib = m.lib()
+    P = ctypes.c_void_p
+    one = P(16)  # never dereferenced: validation fails first
+    n = ctypes.c_size_t(0)
+    # capacity 4096 (32 blocks), 4 KV heads, batch 8: pooled [8, 4, 32] fp32
+    s = m.make_shape(8, 4096, 64, 4, 16, 128 ** -0.5)
+    assert lib.msa_workspace_size(ctypes.byref(s), m.OP_DECODE, ctypes.byref(n)) == 0
+    assert n.value >= 8 * 4 * 32 * 4
+    for kw, code in [(dict(seqlen=4000), 2), (dict(top_k=66), 2), (dict(seqlen=(1 << 21) + 128), 2),
+                     (dict(h_q=48), 2), (dict(h_q=6), 1), (dict(softmax_scale=0.0), 1)]:
+        args = dict(batch=8, seqlen=4096, h_q=64, h_kv=4, top_k=16, softmax_scale=0.1)
+        args.update(kw)
+        bad = m.make_shape(**args)
+        assert lib.msa_workspace_size(ctypes.byref(bad), m.OP_DECODE, ctypes.byref(n)) == code, kw
+        assert lib.msa_decode_topk(ctypes.byref(bad), one, one, one, P(0)) == code, kw
+    # the decode limits differ from the forward's: a capacity of 2^23 tokens is no forward shape
+    # either, but top_k = 65 at 1M tokens is a decode shape only
+    ok = m.make_shape(2, 1 << 20, 64, 4, 65, 0.1)
+    assert lib.msa_workspace_size(ctypes.byref(ok), m.OP_DECODE, ctypes.byref(n)) == 0
+    args = [one] * 9
+    for i in range(9):  # q_idx, k_idx, q, k, v, seqlens, block_idx, o, lse
+        a = list(args)
+        a[i] = P(0)
+        assert lib.msa_decode(ctypes.byref(s), *a, one, 1 << 40, P(0)) == 1, i
+    assert lib.msa_decode(ctypes.byref(s), *args, one, 8, P(0)) == 3
+    assert lib.msa_decode(ctypes.byref(s), *args, P(0), 1 << 40, P(0)) == 3
+    assert lib.msa_decode_index_scores(ctypes.byref(s), one, one, P(0), one, P(0)) == 1
+    assert lib.msa_decode_attn(ctypes.byref(s), one, one, one, one, one, one, P(0), P(0)) == 1

@@ -39,3 +39,16 @@ def test_flops_of_the_128k_workload():
     assert P.main_flops(s) == 4 * 128 * 64 * brute_keys
     assert P.bwd_flops(s) == 2.5 * P.main_flops(s)
     assert P.pair_rows(s) == 4 * 16 * sum(min(16, t // 128 + 1) for t in range(131072))
+
+
+def test_decode_bytes_closed_form():
+    from block_sparse_attention_head_amd.perfmodel import decode_bytes
+
+    # L = 1000: t = 999, c_loc = 7; top_k = 4 -> blocks 3 full + local keys 896..999 (104)
+    b = decode_bytes([1000], h_q=8, h_kv=2, top_k=4)
+    assert b["index"] == 1000 * 256 + 2 * 256 + 2 * 8 * 4
+    assert b["topk"] == 2 * (7 * 4 + 4 * 4)
+    assert b["attn"] == 2 * ((3 * 128 + 104) * 512 + 16) + 8 * (512 + 4)
+    # short sequence: every block, an empty one adds nothing
+    s = decode_bytes([200, 0], h_q=4, h_kv=1, top_k=16)
+    assert s["attn"] == (128 + 72) * 512 + 64 + 4 * 516
