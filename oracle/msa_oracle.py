@@ -322,7 +322,7 @@ def positions_attending(block_idx, block: int, block_size: int = DEFAULT_BLOCK):
 # Decode: one new query per sequence against its cache
 # ---------------------------------------------------------------------------
 def msa_decode(q_idx, k_idx, q, k, v, seqlens, top_k: int, softmax_scale: float,
-               block_size: int = DEFAULT_BLOCK):
+               block_size: int = DEFAULT_BLOCK, block_idx=None):
     """One decode step for a batch of sequences of different lengths.
 
     [MSA summary] "Why long context is the bottleneck": decoding adds one token
@@ -343,7 +343,12 @@ def msa_decode(q_idx, k_idx, q, k, v, seqlens, top_k: int, softmax_scale: float,
       earlier blocks by (score desc, block asc), output ascending with c_loc
       last (R3-R6); if c_loc + 1 <= top_k every block 0..c_loc, then -1;
       o, lse = softmax attention of q[b,h] over the selected blocks' rows <= t.
-    Returns block_idx int32 [B, H_idx, top_k], O float64 [B, H_q, D], LSE [B, H_q].
+    With ``block_idx`` [B, H_kv, top_k] given, the attention uses those blocks
+    instead (entries outside [0, c_loc] ignored, a repeated block counted twice,
+    as the forward's sparse attention treats a caller's selection).
+    Returns block_idx int32 [B, H_idx, top_k] (the one used), O float64
+    [B, H_q, D], LSE [B, H_q], and pooled float64 [B, H_idx, ceil(C/block_size)]
+    (-inf for blocks after the sequence's own).
     """
     qi, ki = _f64(q_idx), _f64(k_idx)
     qq, kk, vv = _f64(q), _f64(k), _f64(v)
@@ -357,6 +362,7 @@ def msa_decode(q_idx, k_idx, q, k, v, seqlens, top_k: int, softmax_scale: float,
     if kk.shape[1] < L.max(initial=0):
         raise ValueError("cache capacity below the longest sequence")
     sel = np.full((B, H_idx, top_k), -1, dtype=np.int32)
+    pooled_all = np.full((B, H_idx, -(-kk.shape[1] // block_size)), -np.inf)
     out = np.zeros((B, H_q, D))
     lse = np.full((B, H_q), -np.inf)
     for b in range(B):
@@ -368,15 +374,20 @@ def msa_decode(q_idx, k_idx, q, k, v, seqlens, top_k: int, softmax_scale: float,
         for g in range(H_idx):
             scores = ki[b, :n] @ qi[b, g]
             pooled = [scores[c * block_size:min((c + 1) * block_size, n)].max() for c in range(cl + 1)]
+            pooled_all[b, g, :cl + 1] = pooled
             if cl + 1 <= top_k:
                 chosen = list(range(cl + 1))
             else:
                 ranked = sorted(range(cl), key=lambda c: (-pooled[c], c))
                 chosen = sorted(ranked[:top_k - 1]) + [cl]
             sel[b, g, :len(chosen)] = chosen
+        if block_idx is not None:
+            sel[b] = np.asarray(block_idx[b], dtype=np.int32)
         for g in range(H_kv):
-            rows = np.concatenate([np.arange(c * block_size, min((c + 1) * block_size, n))
-                                   for c in sel[b, g] if 0 <= c <= cl])
+            parts = [np.arange(c * block_size, min((c + 1) * block_size, n)) for c in sel[b, g] if 0 <= c <= cl]
+            if not parts:
+                continue
+            rows = np.concatenate(parts)
             keys, vals = kk[b, rows, g], vv[b, rows, g]
             for h in range(g * G, (g + 1) * G):
                 z = softmax_scale * (keys @ qq[b, h])
@@ -384,7 +395,7 @@ def msa_decode(q_idx, k_idx, q, k, v, seqlens, top_k: int, softmax_scale: float,
                 w = np.exp(z - m)
                 lse[b, h] = m + np.log(w.sum())
                 out[b, h] = (w / w.sum()) @ vals
-    return sel, out, lse
+    return sel, out, lse, pooled_all
 
 
 # ---------------------------------------------------------------------------
