@@ -40,7 +40,10 @@ reason in the design notes at the repository root):
       caller-supplied selection) gets O = 0 and LSE = -inf, the limits of an
       empty sum;
   R14 a decode step for a sequence of length L computes what the forward
-      computes for position L - 1 over cache rows 0..L-1.
+      computes for position L - 1 over cache rows 0..L-1;
+  R15-R17 the index branch's gradient (index_kl_grad): proxy logits scaled by
+      the main softmax scale unless another is given, the KL term weighted by
+      the caller's kl_weight, over the main branch's attended set.
 """
 from __future__ import annotations
 
@@ -308,6 +311,65 @@ def sparse_attention_bwd(q, k, v, block_idx, d_o, softmax_scale: float, block_si
                     dV[b, lo:hi, g] += gv[o:o + hi - lo]
                     o += hi - lo
     return dQ, dK, dV
+
+
+def index_kl_grad(q_idx, k_idx, q, k, block_idx, softmax_scale: float, index_scale: Optional[float] = None,
+                  kl_weight: float = 1.0, block_size: int = DEFAULT_BLOCK,
+                  positions: Optional[Sequence[int]] = None):
+    """Gradient of the index (proxy) branch from the KL alignment loss, selection held fixed.
+
+    [MSA summary] "Training stability": the top-k has no gradient, so the index
+    projections learn from a KL alignment loss whose teacher averages each
+    query head's softmax over the selected tokens, the main branch detached.
+    [Flash-MSA] "KL Divergence Loss": with the teacher p and the proxy
+    distribution p_px over the same tokens, L = sum_t KL(p_t || p_px,t) and
+    dL/dz_px,j = p_px,j - p_j, so the loss itself is never needed.
+    Readings R15-R17: the proxy logits use `index_scale` (default: the main
+    softmax scale, the one scale the call takes); `kl_weight` is the gradient
+    of the caller's total loss with respect to L; the attended set is the main
+    branch's (selected blocks, keys <= t, a repeated block twice).
+
+    For group g, position t with attended keys A:
+        p_j    = (1/G) sum_{h in g} softmax_j(softmax_scale * q[b,t,h] . k[b,j,g])
+        z_j    = index_scale * q_idx[b,t,g] . k_idx[b,j]
+        p_px   = softmax_j(z)
+        dz_j   = kl_weight * (p_px_j - p_j)
+        dq_idx[b,t,g] = index_scale * sum_j dz_j k_idx[b,j]
+        dk_idx[b,j]  += index_scale * dz_j q_idx[b,t,g]   (over t and g: one shared index key head)
+    block_idx: [B, H_kv, P, top_k] rows for the P positions (default all N).
+    Returns dq_idx float64 [B, P, H_idx, D_idx], dk_idx float64 [B, N, D_idx], and
+    the loss kl_weight * sum over (b, g, t) of sum_j p_j (log p_j - log p_px_j).
+    """
+    qi, ki, qq, kk = _f64(q_idx), _f64(k_idx), _f64(q), _f64(k)
+    bi = np.asarray(block_idx)
+    B, N, Hq, _ = qq.shape
+    Hkv = kk.shape[2]
+    G = Hq // Hkv
+    s_idx = softmax_scale if index_scale is None else index_scale
+    pos = _positions(N, positions)
+    if bi.shape[:3] != (B, Hkv, pos.size):
+        raise ValueError("block_idx must be [B, H_kv, P, top_k] for the requested positions")
+    dq = np.zeros((B, pos.size, Hkv, qi.shape[-1]))
+    dk = np.zeros_like(ki)
+    loss = 0.0
+    for b in range(B):
+        for i, t in enumerate(pos):
+            t = int(t)
+            for g in range(Hkv):
+                keys = attended_keys(bi[b, g, i], t, block_size)
+                if keys.size == 0:
+                    continue
+                z_main = softmax_scale * (qq[b, t, g * G:(g + 1) * G] @ kk[b, keys, g].T)   # [G, n]
+                pm = np.exp(z_main - z_main.max(axis=-1, keepdims=True))
+                pm /= pm.sum(axis=-1, keepdims=True)
+                teacher = pm.mean(axis=0)                                                # [n]
+                z = s_idx * (ki[b, keys] @ qi[b, t, g])                                  # [n]
+                log_px = z - (z.max() + np.log(np.exp(z - z.max()).sum()))
+                dz = kl_weight * (np.exp(log_px) - teacher)
+                dq[b, i, g] = s_idx * (dz @ ki[b, keys])
+                np.add.at(dk[b], keys, s_idx * np.outer(dz, qi[b, t, g]))
+                loss += kl_weight * float((teacher * (np.log(teacher) - log_px)).sum())
+    return dq, dk, loss
 
 
 def positions_attending(block_idx, block: int, block_size: int = DEFAULT_BLOCK):
