@@ -127,8 +127,15 @@ def backward_report(w, steps: int, warmup: int):
     def fwd():
         msa.msa_fwd(xg["q_idx"], xg["k_idx"], xg["q"], xg["k"], xg["v"], K, w.softmax_scale, block_idx, o, lse)
 
+    ws_idx = msa.alloc_workspace(shape, msa.OP_INDEX_BWD, dev)
+    dq_idx, dk_idx = torch.empty_like(xg["q_idx"]), torch.empty_like(xg["k_idx"])
+
+    def idx_bwd():
+        msa.index_bwd(xg["q_idx"], xg["k_idx"], xg["q"], xg["k"], lse, block_idx, w.softmax_scale, dq_idx=dq_idx,
+                      dk_idx=dk_idx, workspace=ws_idx)
+
     res = {}
-    for name, fn in (("bwd", bwd), ("fwd", fwd)):
+    for name, fn in (("bwd", bwd), ("fwd", fwd), ("idx", idx_bwd)):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -141,14 +148,19 @@ def backward_report(w, steps: int, warmup: int):
         res[name] = e0.elapsed_time(e1) / steps
     s = P.Shape(B, N, Hq, Hkv, K)
     tf = P.bwd_flops(s) / 1e12 / (res["bwd"] / 1e3)
-    del xg, ws, dq, dk, dv, block_idx, o, lse
+    tf_idx = P.index_bwd_flops(s) / 1e12 / (res["idx"] / 1e3)
+    del xg, ws, dq, dk, dv, block_idx, o, lse, ws_idx, dq_idx, dk_idx
     torch.cuda.empty_cache()
     return {"workload": w.name, "config": {"batch": B, "seqlen": N, "h_q": Hq, "h_kv": Hkv, "top_k": K},
             "what": "msa_sparse_attn_bwd: dQ, dK, dV of the main branch over the forward's block indices",
             "ms": round(res["bwd"], 4), "tokens_s": round(B * N / (res["bwd"] / 1e3), 1),
             "tflops": round(tf, 2), "frac_of_bf16_peak": round(tf / P.PEAK_BF16_TFLOPS, 4),
             "algorithmic_tflop": round(P.bwd_flops(s) / 1e12, 4),
-            "fwd_ms_same_shape": round(res["fwd"], 4)}
+            "fwd_ms_same_shape": round(res["fwd"], 4),
+            "index_branch": {"what": "msa_index_bwd: dq_idx, dk_idx from the KL alignment term over the same indices",
+                             "ms": round(res["idx"], 4), "tflops": round(tf_idx, 2),
+                             "frac_of_bf16_peak": round(tf_idx / P.PEAK_BF16_TFLOPS, 4),
+                             "algorithmic_tflop": round(P.index_bwd_flops(s) / 1e12, 4)}}
 
 
 def decode_report(w, steps: int, warmup: int):

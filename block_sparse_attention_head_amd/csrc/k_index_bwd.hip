@@ -1,0 +1,391 @@
+// Gradient of the index (proxy) branch from the KL alignment loss, over the
+// forward's cached block indices.
+//
+// [MSA summary] "Training stability": the top-k has no gradient, so the index
+// projections learn from a KL alignment loss whose teacher averages each query
+// head's softmax over the selected tokens (the main branch detached).
+// [Flash-MSA] "KL Divergence Loss": with teacher p and proxy distribution p_px
+// over the same tokens, dL/dz_px,j = p_px,j - p_j, so the loss is never formed;
+// "Backward": the proxy LSE comes from a cheap sparse recompute, and the work is
+// scheduled per key block over the inverted index. For group g, position t and
+// an attended key j (scaled by the caller's weight w and the proxy scale s):
+//   p_j  = (1/G) sum_h exp(scale q_h . k_j - lse_h(t))      main, from the forward's LSE
+//   px_j = exp(s q_idx(t) . k_idx_j - lse_px(t))           proxy
+//   dZ_j = w s (px_j - p_j)
+//   dq_idx(t) = sum_j dZ_j k_idx_j;  dk_idx_j = sum_(t,g) dZ_j q_idx(t)
+// Passes (all per work item of the backward's canonical plan, so every sum runs
+// in a fixed order and the result is bitwise reproducible):
+//   k_kl_dz     per 128-row tile (positions x G heads): S^T = K Q^T and the proxy
+//               Z^T = K_idx Q_idx^T on MFMA, p averaged over the G heads of a
+//               position by lane exchanges, dZ rows to the workspace in bf16;
+//   k_kl_grad   per chunk of 32 entries: dq_idx^T = K_idx^T dZ^T (one record per
+//               (t, slot)) and dk_idx += dZ^T Q_idx (per item), on MFMA;
+//   k_kl_dq_sum, k_kl_dk_reduce  the sums over slots, and over items and groups
+//               (one index key head serves every group).
+#include "msa_device.hpp"
+#include "msa_internal.hpp"
+
+namespace msa {
+
+typedef __attribute__((address_space(3))) bf16x4* kl_lds_bf16x4_ptr;
+
+constexpr int kKlMaxItemEntries = kRowTilesPerItem * kBlock;  // entries of one item when G = 1
+constexpr int kKlChunk = 32;                                  // entries per k_kl_grad step
+
+// Row-major 128-element rows with chunk ch (8 elements) of row r at slot ch ^ rsw(r):
+// rows read together by one transposing load fall on distinct slots.
+__device__ __forceinline__ int kl_rsw(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int kl_row_off(int row, int ch) { return row * kDim + ((ch ^ kl_rsw(row)) << 3); }
+
+// ds_read_b64_tr_b16 on such a tile: inside each 16-lane group, lane li addresses
+// row r0 + li/4, columns c0 + 4(li%4) .. +3, and receives column c0 + li of rows
+// r0 .. r0+3. c0 is a multiple of 16.
+__device__ __forceinline__ bf16x4 kl_tr4(const __bf16* tile, int r0, int c0, int li) {
+    const int row = r0 + (li >> 2), col = c0 + 4 * (li & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((kl_lds_bf16x4_ptr)(tile + kl_row_off(row, col >> 3) + (col & 7)));
+}
+__device__ __forceinline__ bf16x8 kl_cat8(bf16x4 a, bf16x4 b) {
+    return (bf16x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// The work item's tile: the last index with item_off[tile] <= item.
+__device__ __forceinline__ int kl_item_tile(const int32_t* __restrict__ item_off, int n_tiles, int item) {
+    int lo = 0, hi = n_tiles;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (item_off[mid] <= item) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// k_idx [B, N, 128] repeated over H heads: [B, N, H, 128] (the proxy LSE pass reads
+// one key head per group, as the forward does).
+__global__ __launch_bounds__(256) void k_kl_rep(const __bf16* __restrict__ k_idx, __bf16* __restrict__ k_rep,
+                                                long long rows, int H) {
+    const long long total = rows * H * 16;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
+        const long long rh = i >> 4, r = rh / H;
+        const int ch = (int)(i & 15);
+        *(uint4*)(k_rep + rh * kDim + ch * 8) = *(const uint4*)(k_idx + r * kDim + ch * 8);
+    }
+}
+
+// A 128 x 128 tile with row stride `stride` into LDS at swz_chunk_offset.
+__device__ __forceinline__ void kl_stage_rows(const __bf16* __restrict__ src, int stride, __bf16* dst, int tid) {
+    const int row0 = tid >> 4, ch = tid & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = row0 + 16 * i;
+        *(uint4*)(dst + swz_chunk_offset(row, ch)) = *(const uint4*)(src + (size_t)row * stride + ch * 8);
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void k_kl_dz(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ q_idx,
+    const __bf16* __restrict__ k_idx, const float* __restrict__ lse, const float* __restrict__ lse_px,
+    const int32_t* __restrict__ off, const int32_t* __restrict__ item_off, const int32_t* __restrict__ entries,
+    __bf16* __restrict__ dz, int N, int Hq, int Hkv, int gshift, int nblk, int n_tiles, float c_main,
+    float c_idx, float dz_scale) {
+    __shared__ __attribute__((aligned(16))) __bf16 ks[kBlock * kDim];   // K[key][dim], swizzled
+    __shared__ __attribute__((aligned(16))) __bf16 kis[kBlock * kDim];  // K_idx[key][dim], swizzled
+    __shared__ int32_t ent[kKlMaxItemEntries];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const int G = 1 << gshift;
+    const int P = kBlock >> gshift;  // positions per 128-row tile
+    const int r = wave * 32 + l32;   // this lane's row: position slot r / G, head r % G
+    const int pslot = r >> gshift, hh = r & (G - 1);
+    const float log2e = 1.4426950408889634f, invG = 1.0f / (float)G;
+    const int total_items = item_off[n_tiles];
+
+    for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
+        const int tile = kl_item_tile(item_off, n_tiles, item);
+        const int c = tile % nblk, bg = tile / nblk, g = bg % Hkv, b = bg / Hkv;
+        const int e0 = off[tile], npos = off[tile + 1] - e0;
+        const int n_rt = (npos + P - 1) / P;
+        const int rt0 = (item - item_off[tile]) * kRowTilesPerItem;
+        const int rt1 = min(rt0 + kRowTilesPerItem, n_rt);
+        const int ne = min(rt1 * P, npos) - rt0 * P;
+        const int ebase = e0 + rt0 * P;  // entry index of this item's first entry
+
+        __syncthreads();  // the previous item's LDS reads are done
+        for (int i = tid; i < ne; i += 256) ent[i] = entries[ebase + i];
+        kl_stage_rows(k + (((size_t)b * N + (size_t)c * kBlock) * Hkv + g) * kDim, Hkv * kDim, ks, tid);
+        kl_stage_rows(k_idx + ((size_t)b * N + (size_t)c * kBlock) * kDim, kDim, kis, tid);
+        __syncthreads();
+
+        for (int rt = rt0; rt < rt1; ++rt) {
+            const int li = (rt - rt0) * P + pslot;
+            const bool valid = li < ne;
+            const int t = ent[valid ? li : 0] >> 8;  // rows past the item's entries reuse a valid row
+            const int head = g * G + hh;
+            bf16x8 qf[8];
+            const __bf16* qrow = q + (((size_t)b * N + t) * Hq + head) * kDim + 8 * h;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) qf[kk] = *(const bf16x8*)(qrow + kk * 16);
+            asm volatile("" ::: "memory");
+            f32x16 sacc[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sacc[mt][i] = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const bf16x8 a = *(const bf16x8*)(ks + swz_chunk_offset(mt * 32 + l32, 2 * kk + h));
+                    sacc[mt] = mfma32(a, qf[kk], sacc[mt]);
+                }
+            // the proxy query of the position (the same for its G rows)
+            const __bf16* qirow = q_idx + (((size_t)b * N + t) * Hkv + g) * kDim + 8 * h;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) qf[kk] = *(const bf16x8*)(qirow + kk * 16);
+            const float lm = lse[((size_t)b * Hq + head) * N + t] * log2e;
+            const int lim = ((t >> 7) == c ? t - c * kBlock : kBlock - 1);  // keys <= lim are attended
+            // main probabilities, averaged over the position's G rows (lanes l32 ^ 1 .. G/2)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = mt * 32 + mfma32_row(i, h);
+                    sacc[mt][i] = key <= lim ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i], c_main, -lm)) : 0.0f;
+                }
+            for (int sft = 1; sft < G; sft <<= 1)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sacc[mt][i] += __shfl_xor(sacc[mt][i], sft, 64);
+            asm volatile("" ::: "memory");
+            f32x16 zacc[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) zacc[mt][i] = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const bf16x8 a = *(const bf16x8*)(kis + swz_chunk_offset(mt * 32 + l32, 2 * kk + h));
+                    zacc[mt] = mfma32(a, qf[kk], zacc[mt]);
+                }
+            if (valid && hh == 0) {
+                const float lp = lse_px[((size_t)b * Hkv + g) * N + t] * log2e;
+                __bf16* dst = dz + (size_t)(ebase + li) * kBlock;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int i0 = 0; i0 < 16; i0 += 4) {
+                        bf16x4 w;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int key = mt * 32 + mfma32_row(i0 + j, h);
+                            const float px =
+                                key <= lim ? __builtin_amdgcn_exp2f(__builtin_fmaf(zacc[mt][i0 + j], c_idx, -lp)) : 0.0f;
+                            w[j] = (__bf16)(dz_scale * (px - sacc[mt][i0 + j] * invG));
+                        }
+                        *(bf16x4*)(dst + mt * 32 + mfma32_row(i0, h)) = w;
+                    }
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void k_kl_grad(
+    const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx, const __bf16* __restrict__ dz,
+    const int32_t* __restrict__ off, const int32_t* __restrict__ item_off, const int32_t* __restrict__ entries,
+    __bf16* __restrict__ dq_part, float* __restrict__ dk_part, int N, int Hkv, int gshift, int nblk, int top_k,
+    int n_tiles) {
+    __shared__ __attribute__((aligned(16))) __bf16 kit[kDim * kBlock];   // K_idx^T[dim][key], swizzled
+    __shared__ __attribute__((aligned(16))) __bf16 dzs[kKlChunk * kDim];  // dZ rows [entry][key]
+    __shared__ __attribute__((aligned(16))) __bf16 qis[kKlChunk * kDim];  // q_idx rows [entry][dim]
+    __shared__ int32_t ent[kKlMaxItemEntries];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const int li16 = lane & 15, hi16 = (lane >> 4) & 1;  // lane inside its 16-lane group, and which half of 32
+    const int P = kBlock >> gshift;
+    const int total_items = item_off[n_tiles];
+
+    for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
+        const int tile = kl_item_tile(item_off, n_tiles, item);
+        const int c = tile % nblk, bg = tile / nblk, g = bg % Hkv, b = bg / Hkv;
+        const int e0 = off[tile], npos = off[tile + 1] - e0;
+        const int n_rt = (npos + P - 1) / P;
+        const int rt0 = (item - item_off[tile]) * kRowTilesPerItem;
+        const int rt1 = min(rt0 + kRowTilesPerItem, n_rt);
+        const int ne = min(rt1 * P, npos) - rt0 * P;
+        const int ebase = e0 + rt0 * P;
+
+        __syncthreads();
+        for (int i = tid; i < ne; i += 256) ent[i] = entries[ebase + i];
+        {
+            // K_idx transposed: thread takes keys 4 key0 + 64 i .. +3, dims 8 ch .. +7
+            const __bf16* kb = k_idx + ((size_t)b * N + (size_t)c * kBlock) * kDim;
+            const int key0 = tid >> 4, ch = tid & 15;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int kq = 4 * key0 + 64 * i;
+                bf16x8 rows[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) rows[rr] = *(const bf16x8*)(kb + (size_t)(kq + rr) * kDim + ch * 8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    bf16x4 w;
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) w[rr] = rows[rr][e];
+                    *(bf16x4*)(kit + swz_chunk_offset(ch * 8 + e, kq >> 3) + (kq & 7)) = w;
+                }
+            }
+        }
+        f32x16 dk[4];  // dK_idx[key 32 wave + row][dim 32 dt + l32]
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) dk[dt][i] = 0.0f;
+
+        for (int cb = 0; cb < ne; cb += kKlChunk) {
+            __syncthreads();  // kit and ent are written; the previous chunk's reads are done
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                const int row = (tid >> 4) + 16 * it, ch = tid & 15;
+                uint4 vz = {0u, 0u, 0u, 0u}, vq = {0u, 0u, 0u, 0u};
+                if (cb + row < ne) {
+                    const int t = ent[cb + row] >> 8;
+                    vz = *(const uint4*)(dz + (size_t)(ebase + cb + row) * kBlock + ch * 8);
+                    vq = *(const uint4*)(q_idx + (((size_t)b * N + t) * Hkv + g) * kDim + ch * 8);
+                }
+                *(uint4*)(dzs + kl_row_off(row, ch)) = vz;
+                *(uint4*)(qis + kl_row_off(row, ch)) = vq;
+            }
+            __syncthreads();
+            // dq_idx^T for dims 32 wave .. +31 and the chunk's 32 entries, over the 128 keys
+            {
+                f32x16 acc;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    const bf16x8 a = *(const bf16x8*)(kit + swz_chunk_offset(wave * 32 + l32, 2 * kk + h));
+                    const bf16x8 bb = *(const bf16x8*)(dzs + kl_row_off(l32, 2 * kk + h));
+                    acc = mfma32(a, bb, acc);
+                }
+                if (cb + l32 < ne) {
+                    const int en = ent[cb + l32], t = en >> 8, slot = en & 255;
+                    __bf16* dst = dq_part + ((((size_t)b * Hkv + g) * N + t) * top_k + slot) * kDim + wave * 32;
+#pragma unroll
+                    for (int i0 = 0; i0 < 16; i0 += 4) {
+                        const bf16x4 w = {(__bf16)acc[i0], (__bf16)acc[i0 + 1], (__bf16)acc[i0 + 2], (__bf16)acc[i0 + 3]};
+                        *(bf16x4*)(dst + mfma32_row(i0, h)) = w;
+                    }
+                }
+            }
+            // dk_idx += dZ^T Q_idx over the chunk's entries (rows of both tiles, read transposed)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int r0 = 16 * kk + 8 * h;
+                const bf16x8 a = kl_cat8(kl_tr4(dzs, r0, wave * 32 + 16 * hi16, li16),
+                                         kl_tr4(dzs, r0 + 4, wave * 32 + 16 * hi16, li16));
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    const bf16x8 bb = kl_cat8(kl_tr4(qis, r0, dt * 32 + 16 * hi16, li16),
+                                              kl_tr4(qis, r0 + 4, dt * 32 + 16 * hi16, li16));
+                    dk[dt] = mfma32(a, bb, dk[dt]);
+                }
+            }
+        }
+        float* dst = dk_part + (size_t)item * kBlock * kDim;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                dst[(size_t)(wave * 32 + mfma32_row(i, h)) * kDim + dt * 32 + l32] = dk[dt][i];
+    }
+}
+
+// dq_idx[b, t, g] = sum of the (t, slot) records over the slots whose block is attended.
+__global__ __launch_bounds__(256) void k_kl_dq_sum(const int32_t* __restrict__ block_idx,
+                                                   const __bf16* __restrict__ dq_part, __bf16* __restrict__ dq_idx,
+                                                   int N, int Hkv, int top_k, long long rows) {
+    const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);  // (b, g, t)
+    if (row >= rows) return;
+    const int ch = threadIdx.x & 15;
+    const int t = (int)(row % N);
+    const long long bg = row / N;
+    const int g = (int)(bg % Hkv);
+    const long long b = bg / Hkv;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int s = 0; s < top_k; ++s) {
+        const int c = block_idx[row * top_k + s];
+        if (c < 0 || c > (t >> 7)) continue;
+        const bf16x8 v = *(const bf16x8*)(dq_part + (row * top_k + s) * kDim + ch * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += (float)v[e];
+    }
+    bf16x8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (__bf16)acc[e];
+    *(bf16x8*)(dq_idx + ((b * N + t) * Hkv + g) * kDim + ch * 8) = out;
+}
+
+// dk_idx of key block c = the partials of every item of the tiles (b, g, c), over g.
+__global__ __launch_bounds__(256) void k_kl_dk_reduce(const float* __restrict__ dk_part,
+                                                      const int32_t* __restrict__ item_off, __bf16* __restrict__ dk_idx,
+                                                      int N, int Hkv, int nblk) {
+    const int c = blockIdx.x % nblk, b = blockIdx.x / nblk;
+    const size_t part = (size_t)kBlock * kDim;
+    for (int e = threadIdx.x; e < kBlock * kDim / 4; e += 256) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int g = 0; g < Hkv; ++g) {
+            const int tile = (b * Hkv + g) * nblk + c;
+            for (int it = item_off[tile]; it < item_off[tile + 1]; ++it)
+                acc += *(const f32x4*)(dk_part + (size_t)it * part + e * 4);
+        }
+        const bf16x4 w = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
+        *(bf16x4*)(dk_idx + ((size_t)b * N + (size_t)c * kBlock) * kDim + e * 4) = w;
+    }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_kl_rep(const void* k_idx, void* k_rep, const Dims& d, hipStream_t stream) {
+    const long long rows = (long long)d.B * d.N;
+    const long long total = rows * d.Hkv * 16;
+    const long long blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(k_kl_rep, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, stream,
+                       (const __bf16*)k_idx, (__bf16*)k_rep, rows, d.Hkv);
+    return hipGetLastError();
+}
+
+hipError_t launch_kl_dz(const void* q, const void* k, const void* q_idx, const void* k_idx, const float* lse,
+                        const float* lse_px, const SparseWs& plan, void* dz, float index_scale, float kl_weight,
+                        const Dims& d, hipStream_t stream) {
+    const int n = d.B * d.Hkv * d.nblk;
+    const float log2e = 1.4426950408889634f;
+    hipLaunchKernelGGL(k_kl_dz, dim3(2 * device_cu_count()), dim3(256), 0, stream, (const __bf16*)q,
+                       (const __bf16*)k, (const __bf16*)q_idx, (const __bf16*)k_idx, lse, lse_px, plan.off,
+                       plan.item_off, plan.entries, (__bf16*)dz, d.N, d.Hq, d.Hkv, d.gshift, d.nblk, n,
+                       d.scale * log2e, index_scale * log2e, kl_weight * index_scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_kl_grad(const void* q_idx, const void* k_idx, const void* dz, const SparseWs& plan, void* dq_part,
+                          float* dk_part, const Dims& d, hipStream_t stream) {
+    const int n = d.B * d.Hkv * d.nblk;
+    hipLaunchKernelGGL(k_kl_grad, dim3(2 * device_cu_count()), dim3(256), 0, stream, (const __bf16*)q_idx,
+                       (const __bf16*)k_idx, (const __bf16*)dz, plan.off, plan.item_off, plan.entries,
+                       (__bf16*)dq_part, dk_part, d.N, d.Hkv, d.gshift, d.nblk, d.top_k, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_kl_reduce(const int32_t* block_idx, const void* dq_part, const float* dk_part, const SparseWs& plan,
+                            void* dq_idx, void* dk_idx, const Dims& d, hipStream_t stream) {
+    const long long rows = (long long)d.B * d.Hkv * d.N;
+    hipLaunchKernelGGL(k_kl_dq_sum, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, block_idx,
+                       (const __bf16*)dq_part, (__bf16*)dq_idx, d.N, d.Hkv, d.top_k, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_kl_dk_reduce, dim3((unsigned)(d.B * d.nblk)), dim3(256), 0, stream, dk_part, plan.item_off,
+                       (__bf16*)dk_idx, d.N, d.Hkv, d.nblk);
+    return hipGetLastError();
+}
+
+}  // namespace msa

@@ -92,6 +92,16 @@ hipError_t launch_bwd_dq_sum(const int32_t* block_idx, void* dq, const BwdWs& ws
 hipError_t launch_bwd_dkdv_reduce(void* dk, void* dv, const BwdWs& ws, const Dims& d, hipStream_t stream);
 
 // Compute-unit count of the current device (cached per device).
+// Index-branch gradient from the KL alignment loss (k_index_bwd.hip).
+hipError_t launch_kl_rep(const void* k_idx, void* k_rep, const Dims& d, hipStream_t stream);
+hipError_t launch_kl_dz(const void* q, const void* k, const void* q_idx, const void* k_idx, const float* lse,
+                        const float* lse_px, const SparseWs& plan, void* dz, float index_scale, float kl_weight,
+                        const Dims& d, hipStream_t stream);
+hipError_t launch_kl_grad(const void* q_idx, const void* k_idx, const void* dz, const SparseWs& plan, void* dq_part,
+                          float* dk_part, const Dims& d, hipStream_t stream);
+hipError_t launch_kl_reduce(const int32_t* block_idx, const void* dq_part, const float* dk_part, const SparseWs& plan,
+                            void* dq_idx, void* dk_idx, const Dims& d, hipStream_t stream);
+
 int device_cu_count();
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
 MSA_OK = 0
 MSA_CAUSAL = 1
 MSA_POOLED_VISIBLE_ONLY = 2
-OP_INDEX_SCORES, OP_BLOCK_TOPK, OP_SPARSE_ATTN_FWD, OP_FWD, OP_SPARSE_ATTN_BWD, OP_INDEX_TOPK, OP_DECODE = range(7)
+(OP_INDEX_SCORES, OP_BLOCK_TOPK, OP_SPARSE_ATTN_FWD, OP_FWD, OP_SPARSE_ATTN_BWD, OP_INDEX_TOPK, OP_DECODE,
+ OP_INDEX_BWD) = range(8)
 
 BLOCK_SIZE = 128
 HEAD_DIM = 128
@@ -65,6 +66,7 @@ _SIGNATURES = {
     "msa_decode_topk": [_S, _P, _P, _P, _P],
     "msa_decode_attn": [_S, _P, _P, _P, _P, _P, _P, _P, _P],
     "msa_decode": [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "msa_index_bwd": [_S, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P],
 }
 
 _lib = None
@@ -237,6 +239,27 @@ def sparse_attn_bwd(q, k, v, o, lse, d_o, block_idx, softmax_scale: float, dq=No
                                      _ptr(block_idx), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
                                      _stream(q.device)))
     return dq, dk, dv
+
+
+def index_bwd(q_idx, k_idx, q, k, lse, block_idx, softmax_scale: float, index_scale: Optional[float] = None,
+              kl_weight: float = 1.0, dq_idx=None, dk_idx=None, workspace=None):
+    """(dq_idx bf16 [B,N,H_idx,128], dk_idx bf16 [B,N,128]): the index branch's KL gradient (see msa_index_bwd)."""
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    shape = _attn_shape(q, k, k, block_idx, softmax_scale)
+    _need(q_idx, "q_idx", torch.bfloat16, (B, N, Hkv, D))
+    _need(k_idx, "k_idx", torch.bfloat16, (B, N, D))
+    _need(lse, "lse", torch.float32, (B, Hq, N))
+    dq_idx = torch.empty_like(q_idx) if dq_idx is None else dq_idx
+    dk_idx = torch.empty_like(k_idx) if dk_idx is None else dk_idx
+    _need(dq_idx, "dq_idx", torch.bfloat16, (B, N, Hkv, D))
+    _need(dk_idx, "dk_idx", torch.bfloat16, (B, N, D))
+    ws = _ws(workspace, shape, OP_INDEX_BWD, q.device)
+    s_idx = softmax_scale if index_scale is None else index_scale
+    _check("msa_index_bwd", lib().msa_index_bwd(ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k),
+                                                _ptr(lse), _ptr(block_idx), float(s_idx), float(kl_weight),
+                                                _ptr(dq_idx), _ptr(dk_idx), _ptr(ws), ws.numel(), _stream(q.device)))
+    return dq_idx, dk_idx
 
 
 def sparse_attn_plan(shape: MsaShape, block_idx: torch.Tensor, workspace: torch.Tensor) -> None:

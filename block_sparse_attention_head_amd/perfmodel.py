@@ -102,6 +102,13 @@ def bwd_flops(s: Shape) -> float:
     return 10.0 * s.head_dim * s.h_q * s.batch * sum_attended_keys(s.seqlen, s.top_k, s.block)
 
 
+def index_bwd_flops(s: Shape) -> float:
+    """Index branch's KL gradient: per attended (position, key) the main scores of the G heads
+    (2 d G) for the teacher, then per group the proxy logits, dq_idx and dk_idx (3 x 2 d)."""
+    return (2.0 * s.head_dim * s.h_q + 6.0 * s.idx_dim * s.hidx) * s.batch * sum_attended_keys(s.seqlen, s.top_k,
+                                                                                                 s.block)
+
+
 def index_bytes(s: Shape) -> float:
     visible = s.batch * s.hidx * sum(min(s.block, s.seqlen - c * s.block) * (c + 1) for c in range(s.nblk))
     return (s.batch * s.seqlen * s.hidx * s.idx_dim * BF16 + s.batch * s.seqlen * s.idx_dim * BF16

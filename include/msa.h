@@ -89,7 +89,8 @@ typedef enum msa_op {
     MSA_OP_FWD = 3,
     MSA_OP_SPARSE_ATTN_BWD = 4,
     MSA_OP_INDEX_TOPK = 5,
-    MSA_OP_DECODE = 6
+    MSA_OP_DECODE = 6,
+    MSA_OP_INDEX_BWD = 7
 } msa_op;
 
 /* Bytes of device workspace `op` needs for `shape` (0 is a valid answer).
@@ -195,6 +196,34 @@ msa_status msa_sparse_attn_bwd(const msa_shape* shape, const void* q, const void
                                const void* o, const float* lse, const void* d_o,
                                const int32_t* block_idx, void* dq, void* dk, void* dv,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Gradient of the index (proxy) branch from the KL alignment loss, over the
+ * forward's cached block indices ([MSA summary] "Training stability": the
+ * top-k has no gradient, so the index projections learn from a KL loss whose
+ * teacher averages the group's query heads' softmax over the selected tokens,
+ * the main branch detached; [Flash-MSA] "KL Divergence Loss": the gradient to
+ * a proxy logit is the proxy probability minus the teacher's, so the loss is
+ * never formed; "Backward": the proxy LSE is recomputed over the selected
+ * blocks). For group g, position t and each attended key j (as in
+ * msa_sparse_attn_fwd: selected blocks, j <= t, a repeated entry twice):
+ *   p_j  = (1/G) sum_{h in g} exp(softmax_scale q[b,t,h] . k[b,j,g] - lse[b,h,t])
+ *   px_j = softmax_j(index_scale q_idx[b,t,g] . k_idx[b,j])
+ *   dz_j = kl_weight * (px_j - p_j)
+ *   dq_idx[b,t,g] = index_scale sum_j dz_j k_idx[b,j]
+ *   dk_idx[b,j]   = index_scale sum_{(t,g) attending j} dz_j q_idx[b,t,g]
+ * lse is the forward's main LSE; index_scale > 0 (the main softmax scale is the
+ * plain choice: the call of the pages takes one scale) and kl_weight is the
+ * gradient of the caller's total loss with respect to the KL term. Outputs
+ * (bf16, every element written): dq_idx [B, N, H_idx, 128], dk_idx [B, N, 128]
+ * (summed over the groups: one shared index key head). With a selection of every
+ * visible block (top_k >= nblk) this is the dense warmup mode's gradient.
+ * Deterministic (canonical plan, no floating-point atomics). Also needs
+ * G = h_q / h_kv <= 32 and batch * seqlen * h_q < 2^31 (else MSA_ERR_UNSUPPORTED).
+ * Workspace: msa_workspace_size(MSA_OP_INDEX_BWD). */
+msa_status msa_index_bwd(const msa_shape* shape, const void* q_idx, const void* k_idx, const void* q,
+                         const void* k, const float* lse, const int32_t* block_idx, float index_scale,
+                         float kl_weight, void* dq_idx, void* dk_idx, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
 
 /* ---- Decode: one new query per sequence against its KV cache ----
  * [MSA summary] "Why long context is the bottleneck" (decoding adds one token

@@ -101,7 +101,7 @@ def test_unsupported_dims_and_flags(m):
         setattr(t, field, val)
         assert m.lib().msa_workspace_size(ctypes.byref(t), m.OP_FWD, ctypes.byref(n)) == 2, field
     assert m.lib().msa_workspace_size(ctypes.byref(s), 9, ctypes.byref(n)) == 1
-    assert m.lib().msa_workspace_size(ctypes.byref(s), 7, ctypes.byref(n)) == 1
+    assert m.lib().msa_workspace_size(ctypes.byref(s), 8, ctypes.byref(n)) == 1
     assert m.lib().msa_workspace_size(None, m.OP_FWD, ctypes.byref(n)) == 1
     assert m.lib().msa_workspace_size(ctypes.byref(s), m.OP_FWD, None) == 1
 
@@ -179,3 +179,26 @@ def test_decode_shape_validation_and_workspace(m):
     assert lib.msa_decode(ctypes.byref(s), *args, P(0), 1 << 40, P(0)) == 3
     assert lib.msa_decode_index_scores(ctypes.byref(s), one, one, P(0), one, P(0)) == 1
     assert lib.msa_decode_attn(ctypes.byref(s), one, one, one, one, one, one, P(0), P(0)) == 1
+
+
+def test_index_bwd_validation(m):
+    lib = m.lib()
+    P = ctypes.c_void_p
+    one = P(16)
+    s = m.make_shape(1, 1024, 8, 2, 4, 0.1)
+    n = ctypes.c_size_t(0)
+    assert lib.msa_workspace_size(ctypes.byref(s), m.OP_INDEX_BWD, ctypes.byref(n)) == 0
+    # dZ and dq_idx partials: 2 groups x 1024 positions x 4 slots x 128 keys/dims, bf16 each
+    assert n.value >= 2 * (2 * 1024 * 4 * 128 * 2)
+    args = [one] * 6
+    for i in range(6):  # q_idx, k_idx, q, k, lse, block_idx
+        a = list(args)
+        a[i] = P(0)
+        assert lib.msa_index_bwd(ctypes.byref(s), *a, ctypes.c_float(0.1), ctypes.c_float(1.0), one, one, one,
+                                 1 << 40, P(0)) == 1, i
+    call = lambda sh, sc, w, ws, nb: lib.msa_index_bwd(ctypes.byref(sh), *args, ctypes.c_float(sc), ctypes.c_float(w),
+                                                       one, one, ws, nb, P(0))
+    assert call(s, 0.0, 1.0, one, 1 << 40) == 1
+    assert call(s, 0.1, float("nan"), one, 1 << 40) == 1
+    assert call(s, 0.1, 1.0, one, 8) == 3
+    assert call(m.make_shape(1, 1024, 128, 2, 4, 0.1), 0.1, 1.0, one, 1 << 40) == 2  # 64 heads per group

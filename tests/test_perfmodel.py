@@ -52,3 +52,11 @@ def test_decode_bytes_closed_form():
     # short sequence: every block, an empty one adds nothing
     s = decode_bytes([200, 0], h_q=4, h_kv=1, top_k=16)
     assert s["attn"] == (128 + 72) * 512 + 64 + 4 * 516
+
+
+def test_index_bwd_flops_closed_form():
+    from block_sparse_attention_head_amd.perfmodel import Shape, index_bwd_flops, sum_attended_keys
+
+    s = Shape(batch=2, seqlen=1024, h_q=8, h_kv=2, top_k=4)
+    # per attended (position, group, key): the G = 4 main heads' scores plus three index products
+    assert index_bwd_flops(s) == 2 * sum_attended_keys(1024, 4) * (2 * 128 * 8 + 3 * 2 * 128 * 2)
