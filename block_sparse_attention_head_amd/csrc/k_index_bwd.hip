@@ -15,6 +15,9 @@
 //   dq_idx(t) = sum_j dZ_j k_idx_j;  dk_idx_j = sum_(t,g) dZ_j q_idx(t)
 // Passes (all per work item of the backward's canonical plan, so every sum runs
 // in a fixed order and the result is bitwise reproducible):
+//   k_kl_lse_part, k_kl_lse_combine  the proxy LSE: per (t, slot) the max and the
+//               sum of exponentials of the proxy logits over the block's attended
+//               keys (MFMA), then merged over the slots;
 //   k_kl_dz     per 128-row tile (positions x G heads): S^T = K Q^T and the proxy
 //               Z^T = K_idx Q_idx^T on MFMA, p averaged over the G heads of a
 //               position by lane exchanges, dZ rows to the workspace in bf16;
@@ -59,18 +62,6 @@ __device__ __forceinline__ int kl_item_tile(const int32_t* __restrict__ item_off
     return lo;
 }
 
-// k_idx [B, N, 128] repeated over H heads: [B, N, H, 128] (the proxy LSE pass reads
-// one key head per group, as the forward does).
-__global__ __launch_bounds__(256) void k_kl_rep(const __bf16* __restrict__ k_idx, __bf16* __restrict__ k_rep,
-                                                long long rows, int H) {
-    const long long total = rows * H * 16;
-    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
-        const long long rh = i >> 4, r = rh / H;
-        const int ch = (int)(i & 15);
-        *(uint4*)(k_rep + rh * kDim + ch * 8) = *(const uint4*)(k_idx + r * kDim + ch * 8);
-    }
-}
-
 // A 128 x 128 tile with row stride `stride` into LDS at swz_chunk_offset.
 __device__ __forceinline__ void kl_stage_rows(const __bf16* __restrict__ src, int stride, __bf16* dst, int tid) {
     const int row0 = tid >> 4, ch = tid & 15;
@@ -79,6 +70,110 @@ __device__ __forceinline__ void kl_stage_rows(const __bf16* __restrict__ src, in
         const int row = row0 + 16 * i;
         *(uint4*)(dst + swz_chunk_offset(row, ch)) = *(const uint4*)(src + (size_t)row * stride + ch * 8);
     }
+}
+
+// Proxy logits of an item's entries, 128 at a time (lane l32 of wave w holds entry
+// 32 w + l32, keys mt*32 + mfma32_row(i, h)): per entry the max of the logits
+// over the block's attended keys and the sum of 2^(logit - max), both in log2
+// units, to the (t, slot) record.
+__global__ __launch_bounds__(256, 2) void k_kl_lse_part(
+    const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx, const int32_t* __restrict__ off,
+    const int32_t* __restrict__ item_off, const int32_t* __restrict__ entries, float2* __restrict__ lse_part,
+    int N, int Hkv, int gshift, int nblk, int top_k, int n_tiles, float c_idx) {
+    __shared__ __attribute__((aligned(16))) __bf16 kis[kBlock * kDim];  // K_idx[key][dim], swizzled
+    __shared__ int32_t ent[kKlMaxItemEntries];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const int P = kBlock >> gshift;
+    const int total_items = item_off[n_tiles];
+
+    for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
+        const int tile = kl_item_tile(item_off, n_tiles, item);
+        const int c = tile % nblk, bg = tile / nblk, g = bg % Hkv, b = bg / Hkv;
+        const int e0 = off[tile], npos = off[tile + 1] - e0;
+        const int n_rt = (npos + P - 1) / P;
+        const int rt0 = (item - item_off[tile]) * kRowTilesPerItem;
+        const int rt1 = min(rt0 + kRowTilesPerItem, n_rt);
+        const int ne = min(rt1 * P, npos) - rt0 * P;
+        const int ebase = e0 + rt0 * P;
+
+        __syncthreads();
+        for (int i = tid; i < ne; i += 256) ent[i] = entries[ebase + i];
+        kl_stage_rows(k_idx + ((size_t)b * N + (size_t)c * kBlock) * kDim, kDim, kis, tid);
+        __syncthreads();
+
+        for (int cb = 0; cb < ne; cb += kBlock) {
+            const int li = cb + wave * 32 + l32;
+            const bool valid = li < ne;
+            const int en = ent[valid ? li : 0], t = en >> 8;
+            bf16x8 qf[8];
+            const __bf16* qirow = q_idx + (((size_t)b * N + t) * Hkv + g) * kDim + 8 * h;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) qf[kk] = *(const bf16x8*)(qirow + kk * 16);
+            asm volatile("" ::: "memory");
+            f32x16 zacc[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) zacc[mt][i] = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const bf16x8 a = *(const bf16x8*)(kis + swz_chunk_offset(mt * 32 + l32, 2 * kk + h));
+                    zacc[mt] = mfma32(a, qf[kk], zacc[mt]);
+                }
+            const int lim = ((t >> 7) == c ? t - c * kBlock : kBlock - 1);
+            float m = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float zz = mt * 32 + mfma32_row(i, h) <= lim ? zacc[mt][i] * c_idx : -INFINITY;
+                    zacc[mt][i] = zz;
+                    m = fmaxf(m, zz);
+                }
+            m = wave_max_xor32(m);  // key 128 c <= t is always attended, so m is finite
+            float l = 0.0f;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) l += __builtin_amdgcn_exp2f(zacc[mt][i] - m);
+            l += __shfl_xor(l, 32, 64);
+            if (valid && h == 0)
+                lse_part[(((size_t)b * Hkv + g) * N + t) * top_k + (en & 255)] = make_float2(m, l);
+        }
+    }
+}
+
+// lse_px[b, g, t] (natural log) from the records of the slots whose block is attended:
+// 16 lanes per row, each taking every 16th slot, merged by lane exchanges.
+__global__ __launch_bounds__(256) void k_kl_lse_combine(const int32_t* __restrict__ block_idx,
+                                                        const float2* __restrict__ lse_part,
+                                                        float* __restrict__ lse_px, int N, int top_k,
+                                                        long long rows) {
+    const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);  // (b, g, t)
+    const int sl = threadIdx.x & 15;
+    const bool live = row < rows;
+    const int t = live ? (int)(row % N) : 0;
+    float M = -INFINITY, L = 0.0f;
+    for (int s = sl; live && s < top_k; s += 16) {
+        const int c = block_idx[row * top_k + s];
+        if (c < 0 || c > (t >> 7)) continue;
+        const float2 r = lse_part[row * top_k + s];
+        const float m2 = fmaxf(M, r.x);
+        L = L * __builtin_amdgcn_exp2f(M - m2) + r.y * __builtin_amdgcn_exp2f(r.x - m2);
+        M = m2;
+    }
+#pragma unroll
+    for (int sft = 1; sft < 16; sft <<= 1) {
+        const float Mo = __shfl_xor(M, sft, 64), Lo = __shfl_xor(L, sft, 64);
+        const float m2 = fmaxf(M, Mo);
+        L = (M == -INFINITY ? 0.0f : L * __builtin_amdgcn_exp2f(M - m2)) +
+            (Mo == -INFINITY ? 0.0f : Lo * __builtin_amdgcn_exp2f(Mo - m2));
+        M = m2;
+    }
+    if (live && sl == 0) lse_px[row] = L > 0.0f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
 __global__ __launch_bounds__(256, 2) void k_kl_dz(
@@ -115,78 +210,98 @@ __global__ __launch_bounds__(256, 2) void k_kl_dz(
         kl_stage_rows(k_idx + ((size_t)b * N + (size_t)c * kBlock) * kDim, kDim, kis, tid);
         __syncthreads();
 
+        // Rows of tile rt: this lane's entry and its query rows. Rows past the item's
+        // entries reuse a valid row and are never written. The next tile's rows are
+        // loaded while the current one computes.
+        const int head = g * G + hh;
+        auto row_t = [&](int rt, bool& valid) {
+            const int li = (rt - rt0) * P + pslot;
+            valid = li < ne;
+            return ent[valid ? li : 0] >> 8;
+        };
+        auto load_q = [&](int t, bf16x8 (&buf)[8]) {
+            const __bf16* row = q + (((size_t)b * N + t) * Hq + head) * kDim + 8 * h;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) buf[kk] = *(const bf16x8*)(row + kk * 16);
+        };
+        auto load_qi = [&](int t, bf16x8 (&buf)[8]) {
+            const __bf16* row = q_idx + (((size_t)b * N + t) * Hkv + g) * kDim + 8 * h;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) buf[kk] = *(const bf16x8*)(row + kk * 16);
+        };
+        bool valid;
+        int t = row_t(rt0, valid);
+        bf16x8 qf[8], qif[8];
+        load_q(t, qf);
+        load_qi(t, qif);
         for (int rt = rt0; rt < rt1; ++rt) {
             const int li = (rt - rt0) * P + pslot;
-            const bool valid = li < ne;
-            const int t = ent[valid ? li : 0] >> 8;  // rows past the item's entries reuse a valid row
-            const int head = g * G + hh;
-            bf16x8 qf[8];
-            const __bf16* qrow = q + (((size_t)b * N + t) * Hq + head) * kDim + 8 * h;
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) qf[kk] = *(const bf16x8*)(qrow + kk * 16);
-            asm volatile("" ::: "memory");
-            f32x16 sacc[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) sacc[mt][i] = 0.0f;
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    const bf16x8 a = *(const bf16x8*)(ks + swz_chunk_offset(mt * 32 + l32, 2 * kk + h));
-                    sacc[mt] = mfma32(a, qf[kk], sacc[mt]);
-                }
-            // the proxy query of the position (the same for its G rows)
-            const __bf16* qirow = q_idx + (((size_t)b * N + t) * Hkv + g) * kDim + 8 * h;
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) qf[kk] = *(const bf16x8*)(qirow + kk * 16);
+            bool nvalid = false;
+            const int tn = rt + 1 < rt1 ? row_t(rt + 1, nvalid) : t;
             const float lm = lse[((size_t)b * Hq + head) * N + t] * log2e;
+            const float lp = lse_px[((size_t)b * Hkv + g) * N + t] * log2e;
             const int lim = ((t >> 7) == c ? t - c * kBlock : kBlock - 1);  // keys <= lim are attended
-            // main probabilities, averaged over the position's G rows (lanes l32 ^ 1 .. G/2)
+            // Every step is elementwise in the key (P uses the forward's LSE), so the 128 keys
+            // go in two halves of 64 and only half of the accumulators are live.
+#pragma unroll 1
+            for (int mh = 0; mh < 2; ++mh) {
+                asm volatile("" ::: "memory");
+                f32x16 sacc[2], zacc[2];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+                for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = mt * 32 + mfma32_row(i, h);
-                    sacc[mt][i] = key <= lim ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i], c_main, -lm)) : 0.0f;
-                }
-            for (int sft = 1; sft < G; sft <<= 1)
+                    for (int i = 0; i < 16; ++i) sacc[m2][i] = zacc[m2][i] = 0.0f;
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
+                for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) sacc[mt][i] += __shfl_xor(sacc[mt][i], sft, 64);
-            asm volatile("" ::: "memory");
-            f32x16 zacc[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) zacc[mt][i] = 0.0f;
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    const bf16x8 a = *(const bf16x8*)(kis + swz_chunk_offset(mt * 32 + l32, 2 * kk + h));
-                    zacc[mt] = mfma32(a, qf[kk], zacc[mt]);
-                }
-            if (valid && hh == 0) {
-                const float lp = lse_px[((size_t)b * Hkv + g) * N + t] * log2e;
-                __bf16* dst = dz + (size_t)(ebase + li) * kBlock;
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int i0 = 0; i0 < 16; i0 += 4) {
-                        bf16x4 w;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int key = mt * 32 + mfma32_row(i0 + j, h);
-                            const float px =
-                                key <= lim ? __builtin_amdgcn_exp2f(__builtin_fmaf(zacc[mt][i0 + j], c_idx, -lp)) : 0.0f;
-                            w[j] = (__bf16)(dz_scale * (px - sacc[mt][i0 + j] * invG));
-                        }
-                        *(bf16x4*)(dst + mt * 32 + mfma32_row(i0, h)) = w;
+                    for (int m2 = 0; m2 < 2; ++m2) {
+                        const bf16x8 a = *(const bf16x8*)(ks + swz_chunk_offset((2 * mh + m2) * 32 + l32, 2 * kk + h));
+                        sacc[m2] = mfma32(a, qf[kk], sacc[m2]);
                     }
+                if (mh == 1 && rt + 1 < rt1) load_q(tn, qf);
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                    for (int m2 = 0; m2 < 2; ++m2) {
+                        const bf16x8 a = *(const bf16x8*)(kis + swz_chunk_offset((2 * mh + m2) * 32 + l32, 2 * kk + h));
+                        zacc[m2] = mfma32(a, qif[kk], zacc[m2]);
+                    }
+                if (mh == 1 && rt + 1 < rt1) load_qi(tn, qif);
+                // main probabilities, averaged over the position's G rows (lanes l32 ^ 1 .. G/2)
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = (2 * mh + m2) * 32 + mfma32_row(i, h);
+                        sacc[m2][i] =
+                            key <= lim ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[m2][i], c_main, -lm)) : 0.0f;
+                    }
+                for (int sft = 1; sft < G; sft <<= 1)
+#pragma unroll
+                    for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) sacc[m2][i] += __shfl_xor(sacc[m2][i], sft, 64);
+                if (valid && hh == 0) {
+                    __bf16* dst = dz + (size_t)(ebase + li) * kBlock;
+#pragma unroll
+                    for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                        for (int i0 = 0; i0 < 16; i0 += 4) {
+                            const int k0 = (2 * mh + m2) * 32 + mfma32_row(i0, h);
+                            bf16x4 w;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const float px = k0 + j <= lim ? __builtin_amdgcn_exp2f(
+                                                                     __builtin_fmaf(zacc[m2][i0 + j], c_idx, -lp))
+                                                               : 0.0f;
+                                w[j] = (__bf16)(dz_scale * (px - sacc[m2][i0 + j] * invG));
+                            }
+                            *(bf16x4*)(dst + k0) = w;
+                        }
+                }
             }
+            t = tn;
+            valid = nvalid;
         }
     }
 }
@@ -333,7 +448,9 @@ __global__ __launch_bounds__(256) void k_kl_dk_reduce(const float* __restrict__ 
                                                       int N, int Hkv, int nblk) {
     const int c = blockIdx.x % nblk, b = blockIdx.x / nblk;
     const size_t part = (size_t)kBlock * kDim;
-    for (int e = threadIdx.x; e < kBlock * kDim / 4; e += 256) {
+    // a quarter of the block's 128 x 128 values per workgroup (blockIdx.y)
+    const int e_end = (blockIdx.y + 1) * (kBlock * kDim / 16);
+    for (int e = blockIdx.y * (kBlock * kDim / 16) + threadIdx.x; e < e_end; e += 256) {
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int g = 0; g < Hkv; ++g) {
             const int tile = (b * Hkv + g) * nblk + c;
@@ -346,12 +463,17 @@ __global__ __launch_bounds__(256) void k_kl_dk_reduce(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_kl_rep(const void* k_idx, void* k_rep, const Dims& d, hipStream_t stream) {
-    const long long rows = (long long)d.B * d.N;
-    const long long total = rows * d.Hkv * 16;
-    const long long blocks = (total + 255) / 256;
-    hipLaunchKernelGGL(k_kl_rep, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, stream,
-                       (const __bf16*)k_idx, (__bf16*)k_rep, rows, d.Hkv);
+hipError_t launch_kl_lse(const void* q_idx, const void* k_idx, const int32_t* block_idx, const SparseWs& plan,
+                         float2* lse_part, float* lse_px, float index_scale, const Dims& d, hipStream_t stream) {
+    const int n = d.B * d.Hkv * d.nblk;
+    hipLaunchKernelGGL(k_kl_lse_part, dim3(2 * device_cu_count()), dim3(256), 0, stream, (const __bf16*)q_idx,
+                       (const __bf16*)k_idx, plan.off, plan.item_off, plan.entries, lse_part, d.N, d.Hkv, d.gshift,
+                       d.nblk, d.top_k, n, index_scale * 1.4426950408889634f);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long rows = (long long)d.B * d.Hkv * d.N;
+    hipLaunchKernelGGL(k_kl_lse_combine, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, block_idx,
+                       lse_part, lse_px, d.N, d.top_k, rows);
     return hipGetLastError();
 }
 
@@ -383,7 +505,7 @@ hipError_t launch_kl_reduce(const int32_t* block_idx, const void* dq_part, const
                        (const __bf16*)dq_part, (__bf16*)dq_idx, d.N, d.Hkv, d.top_k, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_kl_dk_reduce, dim3((unsigned)(d.B * d.nblk)), dim3(256), 0, stream, dk_part, plan.item_off,
+    hipLaunchKernelGGL(k_kl_dk_reduce, dim3((unsigned)(d.B * d.nblk), 4), dim3(256), 0, stream, dk_part, plan.item_off,
                        (__bf16*)dk_idx, d.N, d.Hkv, d.nblk);
     return hipGetLastError();
 }

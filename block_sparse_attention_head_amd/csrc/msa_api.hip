@@ -167,7 +167,7 @@ size_t pooled_bytes(const Dims& d) { return (size_t)d.B * d.Hkv * d.N * d.nblk *
 // the single-pass kernel needs nothing; otherwise the pooled scores
 size_t index_topk_ws_bytes(const Dims& d) { return index_topk_fusable(d) ? 0 : align_up(pooled_bytes(d), 256); }
 
-size_t index_bwd_ws_bytes(const Dims& d, float index_scale);
+size_t index_bwd_ws_bytes(const Dims& d);
 
 size_t ws_bytes(const Dims& d, msa_op op) {
     switch (op) {
@@ -178,50 +178,33 @@ size_t ws_bytes(const Dims& d, msa_op op) {
         case MSA_OP_SPARSE_ATTN_BWD: return bwd_ws_bytes(d);
         case MSA_OP_INDEX_TOPK: return index_topk_ws_bytes(d);
         case MSA_OP_DECODE: return dec_ws_bytes(d);
-        case MSA_OP_INDEX_BWD: return index_bwd_ws_bytes(d, d.scale);
+        case MSA_OP_INDEX_BWD: return index_bwd_ws_bytes(d);
     }
     return 0;
 }
 
-// The proxy attention of the index branch as a sparse forward: the index heads are
-// the queries (G = 1), the index key head repeated per group the keys.
-Dims proxy_dims(const Dims& d, float index_scale) {
-    Dims p = d;
-    p.Hq = d.Hkv;
-    p.G = 1;
-    p.gshift = 0;
-    p.scale = index_scale;
-    return p;
-}
-
 struct IndexBwdWs {
-    SparseWs plan;   // canonical plan of the main groups
-    void* k_rep;     // bf16 [B, N, H_idx, 128]
-    void* o_px;      // bf16 [B, N, H_idx, 128] (unused output of the proxy pass)
-    float* lse_px;   // fp32 [B, H_idx, N]
-    SparseWs px;     // the proxy pass's own plan and partials
-    void* dz;        // bf16 [entries][128]
-    void* dq_part;   // bf16 [B*H_idx*N*top_k][128]
-    float* dk_part;  // fp32 [items][128][128]
+    SparseWs plan;     // canonical plan of the main groups
+    float2* lse_part;  // [B*H_idx*N*top_k] proxy (max, sum) per (t, slot), log2 units
+    float* lse_px;     // fp32 [B, H_idx, N]
+    void* dz;          // bf16 [entries][128]
+    void* dq_part;     // bf16 [B*H_idx*N*top_k][128]
+    float* dk_part;    // fp32 [items][128][128]
 };
 
-size_t index_bwd_ws_bytes(const Dims& d, float index_scale) {
-    const Dims p = proxy_dims(d, index_scale);
+size_t index_bwd_ws_bytes(const Dims& d) {
     const size_t rows = (size_t)d.B * d.N * d.Hkv, recs = rows * d.top_k;
-    return plan_ws_bytes(d) + 2 * align_up(rows * kDim * 2, 256) + align_up(rows * 4, 256) + sparse_ws_bytes(p) +
-           2 * align_up(recs * kDim * 2, 256) + align_up(bwd_max_items(d) * kBlock * kDim * 4, 256);
+    return plan_ws_bytes(d) + align_up(recs * 8, 256) + align_up(rows * 4, 256) + 2 * align_up(recs * kDim * 2, 256) +
+           align_up(bwd_max_items(d) * kBlock * kDim * 4, 256);
 }
 
-IndexBwdWs carve_index_bwd_ws(void* base, const Dims& d, float index_scale) {
-    const Dims p = proxy_dims(d, index_scale);
+IndexBwdWs carve_index_bwd_ws(void* base, const Dims& d) {
     const size_t rows = (size_t)d.B * d.N * d.Hkv, recs = rows * d.top_k;
     char* c = (char*)base;
     IndexBwdWs w;
     w.plan = carve_plan_ws(c, d);     c += plan_ws_bytes(d);
-    w.k_rep = c;                      c += align_up(rows * kDim * 2, 256);
-    w.o_px = c;                       c += align_up(rows * kDim * 2, 256);
+    w.lse_part = (float2*)c;          c += align_up(recs * 8, 256);
     w.lse_px = (float*)c;             c += align_up(rows * 4, 256);
-    w.px = carve_sparse_ws(c, p);     c += sparse_ws_bytes(p);
     w.dz = c;                         c += align_up(recs * kDim * 2, 256);
     w.dq_part = c;                    c += align_up(recs * kDim * 2, 256);
     w.dk_part = (float*)c;
@@ -462,15 +445,11 @@ msa_status msa_index_bwd(const msa_shape* shape, const void* q_idx, const void* 
     if (!(index_scale > 0.0f) || !isfinite(index_scale) || !isfinite(kl_weight)) return MSA_ERR_INVALID_ARG;
     if (d.G > 32) return MSA_ERR_UNSUPPORTED;  // a position's heads are averaged inside one 32-lane half
     if ((double)d.B * d.N * d.Hq >= 2147483647.0) return MSA_ERR_UNSUPPORTED;
-    if (!workspace || workspace_bytes < index_bwd_ws_bytes(d, index_scale)) return MSA_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < index_bwd_ws_bytes(d)) return MSA_ERR_WORKSPACE;
     (void)hipGetLastError();
-    const Dims p = proxy_dims(d, index_scale);
-    const IndexBwdWs ws = carve_index_bwd_ws(workspace, d, index_scale);
+    const IndexBwdWs ws = carve_index_bwd_ws(workspace, d);
     hipError_t e = launch_sparse_plan(block_idx, ws.plan, d, true, stream);
-    if (e == hipSuccess) e = launch_kl_rep(k_idx, ws.k_rep, d, stream);
-    if (e == hipSuccess) e = launch_sparse_plan(block_idx, ws.px, p, false, stream);
-    if (e == hipSuccess) e = launch_sparse_partial(q_idx, ws.k_rep, ws.k_rep, ws.px, p, stream);
-    if (e == hipSuccess) e = launch_sparse_combine(block_idx, ws.o_px, ws.lse_px, ws.px, p, stream);
+    if (e == hipSuccess) e = launch_kl_lse(q_idx, k_idx, block_idx, ws.plan, ws.lse_part, ws.lse_px, index_scale, d, stream);
     if (e == hipSuccess)
         e = launch_kl_dz(q, k, q_idx, k_idx, lse, ws.lse_px, ws.plan, ws.dz, index_scale, kl_weight, d, stream);
     if (e == hipSuccess) e = launch_kl_grad(q_idx, k_idx, ws.dz, ws.plan, ws.dq_part, ws.dk_part, d, stream);

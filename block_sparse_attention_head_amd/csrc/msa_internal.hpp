@@ -93,7 +93,8 @@ hipError_t launch_bwd_dkdv_reduce(void* dk, void* dv, const BwdWs& ws, const Dim
 
 // Compute-unit count of the current device (cached per device).
 // Index-branch gradient from the KL alignment loss (k_index_bwd.hip).
-hipError_t launch_kl_rep(const void* k_idx, void* k_rep, const Dims& d, hipStream_t stream);
+hipError_t launch_kl_lse(const void* q_idx, const void* k_idx, const int32_t* block_idx, const SparseWs& plan,
+                         float2* lse_part, float* lse_px, float index_scale, const Dims& d, hipStream_t stream);
 hipError_t launch_kl_dz(const void* q, const void* k, const void* q_idx, const void* k_idx, const float* lse,
                         const float* lse_px, const SparseWs& plan, void* dz, float index_scale, float kl_weight,
                         const Dims& d, hipStream_t stream);

@@ -115,8 +115,9 @@ def test_index_bwd_deterministic(msa):
 
 
 def test_index_bwd_full_size_sampled(msa):
-    """The 64K-token training shape: dq_idx on sampled positions; dk_idx on the last key block and a
-    middle one (the oracle over every position that attends the block in any group)."""
+    """The 64K-token training shape: dq_idx on sampled positions; dk_idx on the last key block and
+    the one at 7/8 of the sequence (the oracle over every position that attends the block in any
+    group: about 2000 here, against about 9600 for the middle block)."""
     w = WORKLOADS["n64k_train"]
     _say(w.name, "generating inputs")
     x = make_inputs(w)
@@ -129,7 +130,7 @@ def test_index_bwd_full_size_sampled(msa):
     _say(w.name, f"oracle dq_idx on {len(pos)} positions")
     rq, _, _ = O.index_kl_grad(x["q_idx"], x["k_idx"], x["q"], x["k"], gi[:, :, pos], w.softmax_scale, positions=pos)
     _say(w.name, "dq_idx", check_grads((to_np(dq[:, pos]),), (rq,), f"{w.name}/dq_idx"))
-    for c in (w.nblk - 1, w.nblk // 2):
+    for c in (w.nblk - 1, 7 * w.nblk // 8):
         hit = np.nonzero(O.positions_attending(gi, c)[0].any(axis=0))[0]
         _say(w.name, f"oracle dk_idx of block {c} over {len(hit)} positions")
         _, rk, _ = O.index_kl_grad(x["q_idx"], x["k_idx"], x["q"], x["k"], gi[:, :, hit], w.softmax_scale,
