@@ -491,7 +491,9 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv_reduce(const float* __restrict
     const int c = tile % nblk, bg = tile / nblk, g = bg % Hkv, b = bg / Hkv;
     const int i0 = item_off[tile], i1 = item_off[tile + 1];
     const size_t part = (size_t)kBlock * kDim;
-    for (int e = threadIdx.x; e < kBlock * kDim / 4; e += 256) {  // 4 elements per unit
+    // a quarter of the block's values per workgroup (blockIdx.y), 4 elements per unit
+    const int e_end = (blockIdx.y + 1) * (kBlock * kDim / 16);
+    for (int e = blockIdx.y * (kBlock * kDim / 16) + threadIdx.x; e < e_end; e += 256) {
         f32x4 ak = {0.0f, 0.0f, 0.0f, 0.0f}, av = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int it = i0; it < i1; ++it) {
             ak += *(const f32x4*)(dkv_part + (size_t)it * 2 * part + e * 4);
@@ -553,7 +555,7 @@ hipError_t launch_bwd_dq_sum(const int32_t* block_idx, void* dq, const BwdWs& ws
 
 hipError_t launch_bwd_dkdv_reduce(void* dk, void* dv, const BwdWs& ws, const Dims& d, hipStream_t stream) {
     const int n = d.B * d.Hkv * d.nblk;
-    hipLaunchKernelGGL(k_bwd_dkdv_reduce, dim3(n), dim3(256), 0, stream, ws.dkv_part, ws.plan.item_off,
+    hipLaunchKernelGGL(k_bwd_dkdv_reduce, dim3(n, 4), dim3(256), 0, stream, ws.dkv_part, ws.plan.item_off,
                        (__bf16*)dk, (__bf16*)dv, d.N, d.Hkv, d.nblk);
     return hipGetLastError();
 }
