@@ -13,13 +13,13 @@ namespace msa {
 
 constexpr int kTopkRegVals = 16;
 
+// Unconditional loads (index clamped into the row, so no branch per load); entries at or
+// past cl are masked by the caller.
 __device__ __forceinline__ void topk_load_row(const float* __restrict__ src, int cl, int lane,
                                               float (&v)[kTopkRegVals]) {
+    const int last = cl - 1;
 #pragma unroll
-    for (int i = 0; i < kTopkRegVals; ++i) {
-        const int c = lane + 64 * i;
-        v[i] = c < cl ? src[c] : 0.0f;
-    }
+    for (int i = 0; i < kTopkRegVals; ++i) v[i] = src[min(lane + 64 * i, last)];
 }
 
 // Rank of `mine` among list[0..n4): how many listed keys are larger. n4 is a multiple
@@ -99,10 +99,12 @@ __device__ __forceinline__ void topk_row_from_regs(const float (&cur)[kTopkRegVa
     for (int i = 0; i < kTopkRegVals; ++i) {
         const bool take = k32[i] >= T;
         const uint64_t mask = __ballot(take);
-        if (take)
-            list[n + __popcll(mask & ((1ull << lane) - 1ull))] =
-                ((uint64_t)k32[i] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * i));
-        n += __popcll(mask);
+        if (mask != 0ull) {  // wave-uniform: most groups hold no candidate
+            if (take)
+                list[n + __popcll(mask & ((1ull << lane) - 1ull))] =
+                    ((uint64_t)k32[i] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * i));
+            n += __popcll(mask);
+        }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
