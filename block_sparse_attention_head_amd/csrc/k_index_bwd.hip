@@ -306,6 +306,151 @@ __global__ __launch_bounds__(256, 2) void k_kl_dz(
     }
 }
 
+// The same result for G >= 4 with the proxy logits computed once per position
+// instead of once per head row: per half of the keys, the lane of head 0 of each
+// position puts the averaged main probabilities in LDS, then waves 0 and 1 compute
+// Z^T for the tile's (at most 32) positions, one 32-key tile each, and write dZ.
+constexpr int kKlSharedPos = 32;  // positions of a 128-row tile when G >= 4
+
+__global__ __launch_bounds__(256, 2) void k_kl_dz_shared(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ q_idx,
+    const __bf16* __restrict__ k_idx, const float* __restrict__ lse, const float* __restrict__ lse_px,
+    const int32_t* __restrict__ off, const int32_t* __restrict__ item_off, const int32_t* __restrict__ entries,
+    __bf16* __restrict__ dz, int N, int Hq, int Hkv, int gshift, int nblk, int n_tiles, float c_main,
+    float c_idx, float dz_scale) {
+    __shared__ __attribute__((aligned(16))) __bf16 ks[kBlock * kDim];
+    __shared__ __attribute__((aligned(16))) __bf16 kis[kBlock * kDim];
+    __shared__ int32_t ent[kRowTilesPerItem * kKlSharedPos];
+    __shared__ __attribute__((aligned(16))) float pbar[kKlSharedPos][64 + 4];  // [position][key of the half]
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const int G = 1 << gshift;
+    const int P = kBlock >> gshift;  // <= 32
+    const int r = wave * 32 + l32;
+    const int pslot = r >> gshift, hh = r & (G - 1);
+    const float log2e = 1.4426950408889634f, invG = 1.0f / (float)G;
+    const bool zwave = wave < 2;  // waves 0, 1 compute the proxy logits, lane l32 = position
+    const int total_items = item_off[n_tiles];
+
+    for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
+        const int tile = kl_item_tile(item_off, n_tiles, item);
+        const int c = tile % nblk, bg = tile / nblk, g = bg % Hkv, b = bg / Hkv;
+        const int e0 = off[tile], npos = off[tile + 1] - e0;
+        const int n_rt = (npos + P - 1) / P;
+        const int rt0 = (item - item_off[tile]) * kRowTilesPerItem;
+        const int rt1 = min(rt0 + kRowTilesPerItem, n_rt);
+        const int ne = min(rt1 * P, npos) - rt0 * P;
+        const int ebase = e0 + rt0 * P;
+
+        __syncthreads();
+        for (int i = tid; i < ne; i += 256) ent[i] = entries[ebase + i];
+        kl_stage_rows(k + (((size_t)b * N + (size_t)c * kBlock) * Hkv + g) * kDim, Hkv * kDim, ks, tid);
+        kl_stage_rows(k_idx + ((size_t)b * N + (size_t)c * kBlock) * kDim, kDim, kis, tid);
+        __syncthreads();
+
+        const int head = g * G + hh;
+        auto load_rows = [&](const __bf16* base, size_t row, bf16x8 (&buf)[8]) {
+            const __bf16* p = base + row * kDim + 8 * h;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) buf[kk] = *(const bf16x8*)(p + kk * 16);
+        };
+        // this lane's head row (S) and, on waves 0-1, the proxy row of position l32 (Z)
+        auto row_of = [&](int rt, int slot, bool& valid) {
+            const int li = (rt - rt0) * P + slot;
+            valid = slot < P && li < ne;
+            return ent[valid ? li : 0] >> 8;
+        };
+        bool svalid, zvalid;
+        int ts = row_of(rt0, pslot, svalid), tz = row_of(rt0, l32, zvalid);
+        bf16x8 qf[8], qif[8];
+        load_rows(q, ((size_t)b * N + ts) * Hq + head, qf);
+        if (zwave) load_rows(q_idx, ((size_t)b * N + tz) * Hkv + g, qif);
+        for (int rt = rt0; rt < rt1; ++rt) {
+            bool nsv = false, nzv = false;
+            const int tsn = rt + 1 < rt1 ? row_of(rt + 1, pslot, nsv) : ts;
+            const int tzn = rt + 1 < rt1 ? row_of(rt + 1, l32, nzv) : tz;
+            const float lm = lse[((size_t)b * Hq + head) * N + ts] * log2e;
+            const int lims = ((ts >> 7) == c ? ts - c * kBlock : kBlock - 1);
+            const float lp = zwave ? lse_px[((size_t)b * Hkv + g) * N + tz] * log2e : 0.0f;
+            const int limz = ((tz >> 7) == c ? tz - c * kBlock : kBlock - 1);
+#pragma unroll 1
+            for (int mh = 0; mh < 2; ++mh) {
+                asm volatile("" ::: "memory");
+                f32x16 sacc[2];
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sacc[m2][i] = 0.0f;
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                    for (int m2 = 0; m2 < 2; ++m2) {
+                        const bf16x8 a = *(const bf16x8*)(ks + swz_chunk_offset((2 * mh + m2) * 32 + l32, 2 * kk + h));
+                        sacc[m2] = mfma32(a, qf[kk], sacc[m2]);
+                    }
+                if (mh == 1 && rt + 1 < rt1) load_rows(q, ((size_t)b * N + tsn) * Hq + head, qf);
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = (2 * mh + m2) * 32 + mfma32_row(i, h);
+                        sacc[m2][i] =
+                            key <= lims ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[m2][i], c_main, -lm)) : 0.0f;
+                    }
+                for (int sft = 1; sft < G; sft <<= 1)
+#pragma unroll
+                    for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) sacc[m2][i] += __shfl_xor(sacc[m2][i], sft, 64);
+                if (hh == 0 && pslot < P) {
+#pragma unroll
+                    for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                        for (int i0 = 0; i0 < 16; i0 += 4)
+                            *(f32x4*)&pbar[pslot][m2 * 32 + mfma32_row(i0, h)] =
+                                (f32x4){sacc[m2][i0] * invG, sacc[m2][i0 + 1] * invG, sacc[m2][i0 + 2] * invG,
+                                        sacc[m2][i0 + 3] * invG};
+                }
+                __syncthreads();  // the half's averaged probabilities are in LDS
+                if (zwave) {
+                    const int m2 = wave;
+                    f32x16 zacc;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) zacc[i] = 0.0f;
+#pragma unroll
+                    for (int kk = 0; kk < 8; ++kk) {
+                        const bf16x8 a = *(const bf16x8*)(kis + swz_chunk_offset((2 * mh + m2) * 32 + l32, 2 * kk + h));
+                        zacc = mfma32(a, qif[kk], zacc);
+                    }
+                    if (zvalid) {
+                        __bf16* dst = dz + (size_t)(ebase + (rt - rt0) * P + l32) * kBlock;
+#pragma unroll
+                        for (int i0 = 0; i0 < 16; i0 += 4) {
+                            const int k0 = (2 * mh + m2) * 32 + mfma32_row(i0, h);
+                            const f32x4 pb = *(const f32x4*)&pbar[l32][m2 * 32 + mfma32_row(i0, h)];
+                            bf16x4 w;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const float px = k0 + j <= limz
+                                                     ? __builtin_amdgcn_exp2f(__builtin_fmaf(zacc[i0 + j], c_idx, -lp))
+                                                     : 0.0f;
+                                w[j] = (__bf16)(dz_scale * (px - pb[j]));
+                            }
+                            *(bf16x4*)(dst + k0) = w;
+                        }
+                    }
+                    if (mh == 1 && rt + 1 < rt1) load_rows(q_idx, ((size_t)b * N + tzn) * Hkv + g, qif);
+                }
+                __syncthreads();  // pbar is read before the next half overwrites it
+            }
+            ts = tsn;
+            svalid = nsv;
+            tz = tzn;
+            zvalid = nzv;
+        }
+    }
+}
+
 __global__ __launch_bounds__(256, 2) void k_kl_grad(
     const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx, const __bf16* __restrict__ dz,
     const int32_t* __restrict__ off, const int32_t* __restrict__ item_off, const int32_t* __restrict__ entries,
@@ -482,7 +627,8 @@ hipError_t launch_kl_dz(const void* q, const void* k, const void* q_idx, const v
                         const Dims& d, hipStream_t stream) {
     const int n = d.B * d.Hkv * d.nblk;
     const float log2e = 1.4426950408889634f;
-    hipLaunchKernelGGL(k_kl_dz, dim3(2 * device_cu_count()), dim3(256), 0, stream, (const __bf16*)q,
+    auto kernel = d.G >= 4 ? k_kl_dz_shared : k_kl_dz;  // G >= 4: proxy logits once per position
+    hipLaunchKernelGGL(kernel, dim3(2 * device_cu_count()), dim3(256), 0, stream, (const __bf16*)q,
                        (const __bf16*)k, (const __bf16*)q_idx, (const __bf16*)k_idx, lse, lse_px, plan.off,
                        plan.item_off, plan.entries, (__bf16*)dz, d.N, d.Hq, d.Hkv, d.gshift, d.nblk, n,
                        d.scale * log2e, index_scale * log2e, kl_weight * index_scale);
