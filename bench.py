@@ -12,8 +12,9 @@ by HIP events on the stream the library launches on.
 Prints ONE JSON line (rank 0): the contract fields, the roofline of the
 dominant kernel, per-stage figures, the CPU oracle baseline, (unless
 --no-backward) a "backward" object: msa_sparse_attn_bwd timed at the
-64K-token training shape, and (unless --no-decode) a "decode" object: one
-decode step (msa_decode's three stages) for 128 sequences of 64K-128K tokens.
+64K-token training shape, (unless --no-decode) a "decode" object: one
+decode step (msa_decode's three stages) for 128 sequences of 64K-128K tokens,
+and (unless --no-long-context) a "long_context" object: msa_fwd at 2^20 tokens.
 
     python bench.py [--steps K] [--warmup W] [--workload n128k] [--gpus 1]
 """
@@ -228,6 +229,58 @@ def decode_report(w, steps: int, warmup: int):
             "stages": stages}
 
 
+def long_context_report(w, steps: int, warmup: int):
+    """msa_fwd at 2^20 tokens (inputs drawn on the GPU), timed with HIP events. The per-slot
+    partials of one pass would not fit in HBM, so the library runs the sparse attention in
+    query chunks inside its workspace."""
+    import torch
+
+    from block_sparse_attention_head_amd import msa
+    from block_sparse_attention_head_amd import perfmodel as P
+    from synth.msa_inputs import make_inputs
+
+    print(f"[bench] long context: generating {w.name} inputs on the GPU", file=sys.stderr, flush=True)
+    xg = make_inputs(w, device="cuda:0")
+    B, N, Hq, Hkv, K = w.batch, w.seqlen, w.h_q, w.h_kv, w.top_k
+    dev = xg["q"].device
+    shape = msa.make_shape(B, N, Hq, Hkv, K, w.softmax_scale)
+    ws = msa.alloc_workspace(shape, msa.OP_FWD, dev)
+    small = msa.make_shape(B, 1 << 17, Hq, Hkv, K, w.softmax_scale)
+    block_idx = torch.empty((B, Hkv, N, K), dtype=torch.int32, device=dev)
+    o = torch.empty_like(xg["q"])
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+
+    def fwd():
+        msa.msa_fwd(xg["q_idx"], xg["k_idx"], xg["q"], xg["k"], xg["v"], K, w.softmax_scale, block_idx, o, lse,
+                    workspace=ws)
+
+    for _ in range(warmup):
+        fwd()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fwd()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    finite = bool(torch.isfinite(o[:, ::4097].float()).all()) and bool(torch.isfinite(lse[:, :, ::4097]).all())
+    # rows with at least top_k visible blocks end with their own block (shorter rows are padded)
+    t_full = (K - 1) * 128
+    local = bool((block_idx[:, :, t_full:, -1] == (torch.arange(t_full, N, device=dev) // 128)).all())
+    s = P.Shape(B, N, Hq, Hkv, K)
+    flop = P.index_flops(s) + P.main_flops(s)
+    per_pos = msa.workspace_size(small, msa.OP_SPARSE_ATTN_FWD) / (1 << 17)
+    del xg, ws, block_idx, o, lse
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "config": {"batch": B, "seqlen": N, "h_q": Hq, "h_kv": Hkv, "top_k": K},
+            "what": "msa_fwd (single-pass selection, chunked sparse attention)", "ms": round(ms, 2),
+            "tokens_s": round(B * N / (ms / 1e3), 1), "tflops": round(flop / 1e12 / (ms / 1e3), 2),
+            "workspace_GB": round(msa.workspace_size(shape, msa.OP_FWD) / 1e9, 2),
+            "one_pass_workspace_GB": round(per_pos * N / 1e9, 1),
+            "outputs_finite": finite, "local_block_last": local}
+
+
 def two_kernel_selection(msa, xg, w, block_idx_single, steps: int, warmup: int):
     """msa_index_scores (pooled scores to HBM) then msa_block_topk, on the step's inputs,
     timed with HIP events per kernel; the indices must equal the single pass's."""
@@ -271,6 +324,7 @@ def main(argv=None) -> int:
     ap.add_argument("--backward-only", action="store_true",
                     help="only the backward measurement (a JSON line with the backward object), for profiling")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
+    ap.add_argument("--no-long-context", action="store_true", help="skip the 2^20-token forward")
     ap.add_argument("--decode-workload", default="dec_b128_n128k")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode measurement (a JSON line with the decode object), for profiling")
@@ -424,6 +478,11 @@ def main(argv=None) -> int:
         out["backward"] = backward_report(WORKLOADS[a.backward_workload], a.steps, a.warmup)
     if not a.no_decode:
         out["decode"] = decode_report(DECODE_WORKLOADS[a.decode_workload], a.steps, a.warmup)
+    if not a.no_long_context:
+        try:  # a failure here must not cost the main line
+            out["long_context"] = long_context_report(WORKLOADS["n1m"], min(a.steps, 2), min(a.warmup, 1))
+        except Exception as exc:  # pragma: no cover
+            out["long_context"] = {"error": f"{type(exc).__name__}: {exc}"}
     if not a.no_cpu_baseline:
         print(f"[bench] CPU oracle baseline (~{a.cpu_budget:.0f} s)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, x, a.cpu_budget)

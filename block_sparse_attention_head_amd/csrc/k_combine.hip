@@ -10,7 +10,7 @@
 
 namespace msa {
 
-// Partial O layout: [(b*N + t)*top_k + slot][chunk c][head][8], where chunk
+// Partial O layout: [(b*Nc + t - p0)*top_k + slot][chunk c][head][8], where chunk
 // c = hf*8 + dt*2 + i0/8 holds dims 32*dt + 8*(i/4) + 4*hf + i%4 for
 // i = i0 .. i0+7 (the order the MFMA result registers are in).
 //
@@ -28,8 +28,8 @@ constexpr int kCombineFastSlots = 16;
 
 __global__ __launch_bounds__(256, 6) void k_combine(const __bf16* __restrict__ part_o, const float* __restrict__ part_lse,
                                                  const int32_t* __restrict__ block_idx, __bf16* __restrict__ o,
-                                                 float* __restrict__ lse, int N, int Hq, int Hkv, int gshift,
-                                                 int top_k) {
+                                                 float* __restrict__ lse, int N, int p0, int Nc, int Hq, int Hkv,
+                                                 int gshift, int top_k) {
     // dynamic LDS: orow [Hq][128] bf16 | wts [top_k][Hq] fp32 | inv_l [Hq] fp32 | sel [Hkv][top_k] int32
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __bf16* orow = (__bf16*)smem;
@@ -37,10 +37,10 @@ __global__ __launch_bounds__(256, 6) void k_combine(const __bf16* __restrict__ p
     float* inv_l = wts + (size_t)top_k * Hq;
     int32_t* sel = (int32_t*)(inv_l + Hq);
     const int tid = threadIdx.x;
-    const int bt = blockIdx.x;
-    const int b = bt / N, t = bt - b * N;
+    const int bt = blockIdx.x;  // (b, t - p0) inside the chunk
+    const int b = bt / Nc, t = p0 + (bt - b * Nc);
     const int cl = t >> 7;
-    const size_t rec0 = (size_t)bt * top_k;  // first record of this position: (b*N + t) * top_k
+    const size_t rec0 = (size_t)bt * top_k;  // first record of this position
 
     // 0. selection rows and slot LSEs into LDS
     for (int i = tid; i < Hkv * top_k; i += 256) {
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256, 6) void k_combine(const __bf16* __restrict__ p
     __syncthreads();
 
     // 3. the position's output row is contiguous in O: write it in 16-byte pieces
-    uint4* dst = (uint4*)(o + (size_t)bt * Hq * kDim);
+    uint4* dst = (uint4*)(o + ((size_t)b * N + t) * Hq * kDim);
     const uint4* srcl = (const uint4*)orow;
     for (int j = tid; j < Hq * 16; j += 256) dst[j] = srcl[j];
 }
@@ -130,8 +130,8 @@ size_t combine_lds_bytes(const Dims& d) {
 
 hipError_t launch_sparse_combine(const int32_t* block_idx, void* o, float* lse, const SparseWs& ws, const Dims& d,
                                  hipStream_t stream) {
-    hipLaunchKernelGGL(k_combine, dim3(d.B * d.N), dim3(256), combine_lds_bytes(d), stream, (const __bf16*)ws.part_o,
-                       ws.part_lse, block_idx, (__bf16*)o, lse, d.N, d.Hq, d.Hkv, d.gshift, d.top_k);
+    hipLaunchKernelGGL(k_combine, dim3(d.B * d.Nc), dim3(256), combine_lds_bytes(d), stream, (const __bf16*)ws.part_o,
+                       ws.part_lse, block_idx, (__bf16*)o, lse, d.N, d.p0, d.Nc, d.Hq, d.Hkv, d.gshift, d.top_k);
     return hipGetLastError();
 }
 

@@ -48,10 +48,10 @@ int rev_groups(int N) { return (N + rev_positions_per_group(N) - 1) / rev_positi
 // wgcnt[(bg*nwg + w)*nblk + c] = entries of range w selecting tile c; cnt[bg*nblk + c] += the same.
 __global__ __launch_bounds__(kRevThreads) void k_rev_count(const int32_t* __restrict__ block_idx,
                                                            int32_t* __restrict__ cnt, int32_t* __restrict__ wgcnt,
-                                                           int N, int nblk, int top_k, int ppw) {
+                                                           int N, int p0, int Nc, int nblk, int top_k, int ppw) {
     __shared__ int32_t hist[kRevLdsBins];
     const int bg = blockIdx.y, w = blockIdx.x, nwg = gridDim.x;
-    const int t0 = w * ppw, t1 = min(N, t0 + ppw);
+    const int t0 = p0 + w * ppw, t1 = min(p0 + Nc, t0 + ppw);
     int32_t* mine = wgcnt + ((size_t)bg * nwg + w) * nblk;
     for (int c0 = 0; c0 < nblk; c0 += kRevLdsBins) {
         const int nb = min(kRevLdsBins, nblk - c0);
@@ -138,13 +138,13 @@ __global__ __launch_bounds__(256) void k_rev_wgoff(const int32_t* __restrict__ o
 // and slot that selected the same tile.
 __global__ __launch_bounds__(kRevThreads) void k_rev_scatter(const int32_t* __restrict__ block_idx,
                                                              const int32_t* __restrict__ wgoff,
-                                                             int32_t* __restrict__ entries, int N, int nblk,
-                                                             int top_k, int ppw) {
+                                                             int32_t* __restrict__ entries, int N, int p0, int Nc,
+                                                             int nblk, int top_k, int ppw) {
     __shared__ int32_t bins[kRevLdsBins];
     __shared__ __attribute__((aligned(16))) int32_t keys[kRevThreads];
     const int tid = threadIdx.x;
     const int bg = blockIdx.y, w = blockIdx.x, nwg = gridDim.x;
-    const int t0 = w * ppw, t1 = min(N, t0 + ppw);
+    const int t0 = p0 + w * ppw, t1 = min(p0 + Nc, t0 + ppw);
     const int32_t* base_off = wgoff + ((size_t)bg * nwg + w) * nblk;
     for (int c0 = 0; c0 < nblk; c0 += kRevLdsBins) {
         const int nb = min(kRevLdsBins, nblk - c0);
@@ -179,12 +179,12 @@ __global__ __launch_bounds__(kRevThreads) void k_rev_scatter(const int32_t* __re
 // Unordered scatter (forward): places inside a tile come from atomics.
 __global__ __launch_bounds__(kRevThreads) void k_rev_scatter_any(const int32_t* __restrict__ block_idx,
                                                                  int32_t* __restrict__ cursor,
-                                                                 int32_t* __restrict__ entries, int N, int nblk,
-                                                                 int top_k, int ppw) {
+                                                                 int32_t* __restrict__ entries, int N, int p0,
+                                                                 int Nc, int nblk, int top_k, int ppw) {
     __shared__ int32_t bins[kRevLdsBins];
     const bool use_lds = nblk <= kRevLdsBins;
     const int bg = blockIdx.y, w = blockIdx.x;
-    const int t0 = w * ppw, t1 = min(N, t0 + ppw);
+    const int t0 = p0 + w * ppw, t1 = min(p0 + Nc, t0 + ppw);
     int32_t* cur = cursor + (size_t)bg * nblk;
     if (use_lds) {
         for (int i = threadIdx.x; i < nblk; i += kRevThreads) bins[i] = 0;
@@ -217,21 +217,21 @@ __global__ __launch_bounds__(kRevThreads) void k_rev_scatter_any(const int32_t* 
 hipError_t launch_sparse_plan(const int32_t* block_idx, const SparseWs& ws, const Dims& d, bool canonical,
                               hipStream_t stream) {
     const int n = d.B * d.Hkv * d.nblk;
-    const int ppw = rev_positions_per_group(d.N), nwg = rev_groups(d.N);
+    const int ppw = rev_positions_per_group(d.Nc), nwg = rev_groups(d.Nc);
     hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, stream, ws.cnt, 0, (long long)n);
     const dim3 rgrid(nwg, d.B * d.Hkv);
-    hipLaunchKernelGGL(k_rev_count, rgrid, dim3(kRevThreads), 0, stream, block_idx, ws.cnt, ws.wgoff, d.N, d.nblk,
-                       d.top_k, ppw);
+    hipLaunchKernelGGL(k_rev_count, rgrid, dim3(kRevThreads), 0, stream, block_idx, ws.cnt, ws.wgoff, d.N, d.p0, d.Nc,
+                       d.nblk, d.top_k, ppw);
     hipLaunchKernelGGL(k_rev_scan, dim3(1), dim3(1024), 0, stream, ws.cnt, ws.off, ws.item_off, ws.cursor, n,
                        kBlock >> d.gshift);
     if (canonical) {
         hipLaunchKernelGGL(k_rev_wgoff, dim3((n + 255) / 256), dim3(256), 0, stream, ws.off, ws.wgoff, n, d.nblk,
                            nwg);
         hipLaunchKernelGGL(k_rev_scatter, rgrid, dim3(kRevThreads), 0, stream, block_idx, ws.wgoff, ws.entries, d.N,
-                           d.nblk, d.top_k, ppw);
+                           d.p0, d.Nc, d.nblk, d.top_k, ppw);
     } else {
         hipLaunchKernelGGL(k_rev_scatter_any, rgrid, dim3(kRevThreads), 0, stream, block_idx, ws.cursor, ws.entries,
-                           d.N, d.nblk, d.top_k, ppw);
+                           d.N, d.p0, d.Nc, d.nblk, d.top_k, ppw);
     }
     return hipGetLastError();
 }

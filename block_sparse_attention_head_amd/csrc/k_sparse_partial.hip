@@ -38,7 +38,8 @@ struct RowInfo {
 __global__ __launch_bounds__(256, 2) void k_sparse_partial(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ off, const int32_t* __restrict__ item_off, const int32_t* __restrict__ entries,
-    __bf16* __restrict__ part_o, float* __restrict__ part_lse, int N, int Hq, int Hkv, int gshift, int nblk,
+    __bf16* __restrict__ part_o, float* __restrict__ part_lse, int N, int p0, int Nc, int Hq, int Hkv, int gshift,
+    int nblk,
     int top_k, int n_tiles, float scale_log2) {
     __shared__ __attribute__((aligned(16))) __bf16 ks[kBlock * kDim];   // K[key][dim], swizzled
     __shared__ __attribute__((aligned(16))) __bf16 vts[kDim * kBlock];  // V^T[dim][vt_pos(key)], swizzled
@@ -172,8 +173,8 @@ __global__ __launch_bounds__(256, 2) void k_sparse_partial(
                     }
             l += __shfl_xor(l, 32, 64);
             const float inv = 1.0f / l;
-            // partial O record layout: [(b*N + t)*top_k + slot][chunk][head][8 dims], chunk = h*8 + dt*2 + i0/8
-            const size_t rec2 = ((size_t)b * N + cur.t) * top_k + cur.slot;
+            // partial O record layout: [(b*Nc + t - p0)*top_k + slot][chunk][head][8 dims], chunk = h*8 + dt*2 + i0/8
+            const size_t rec2 = ((size_t)b * Nc + (cur.t - p0)) * top_k + cur.slot;
             __bf16* dst = part_o + ((rec2 * 16 + h * 8) * Hq + qhead) * 8;
             const size_t chunk_stride = (size_t)Hq * 8;
 
@@ -221,7 +222,8 @@ hipError_t launch_sparse_partial(const void* q, const void* k, const void* v, co
     const int grid = 2 * device_cu_count();
     const float log2e = 1.4426950408889634f;
     hipLaunchKernelGGL(k_sparse_partial, dim3(grid), dim3(256), 0, stream, (const __bf16*)q, (const __bf16*)k,
-                       (const __bf16*)v, ws.off, ws.item_off, ws.entries, (__bf16*)ws.part_o, ws.part_lse, d.N, d.Hq,
+                       (const __bf16*)v, ws.off, ws.item_off, ws.entries, (__bf16*)ws.part_o, ws.part_lse, d.N, d.p0,
+                       d.Nc, d.Hq,
                        d.Hkv, d.gshift, d.nblk, d.top_k, n, d.scale * log2e);
     return hipGetLastError();
 }

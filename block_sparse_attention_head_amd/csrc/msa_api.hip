@@ -54,6 +54,8 @@ msa_status check_shape(const msa_shape* s, Dims* d) {
     d->nblk = s->seqlen / kBlock;
     d->top_k = s->top_k;
     d->scale = s->softmax_scale;
+    d->p0 = 0;
+    d->Nc = s->seqlen;
     return MSA_OK;
 }
 
@@ -84,6 +86,8 @@ msa_status check_decode_shape(const msa_shape* s, Dims* d) {
     d->nblk = s->seqlen / kBlock;
     d->top_k = s->top_k;
     d->scale = s->softmax_scale;
+    d->p0 = 0;
+    d->Nc = s->seqlen;
     return MSA_OK;
 }
 
@@ -102,8 +106,8 @@ size_t plan_ws_bytes(const Dims& d) {
     s += align_up((n + 1) * 4, 256);                              // off
     s += align_up((n + 1) * 4, 256);                              // item_off
     s += align_up(n * 4, 256);                                    // cursor
-    s += align_up(n * rev_groups(d.N) * 4, 256);                  // wgoff
-    s += align_up((size_t)d.B * d.Hkv * d.N * d.top_k * 4, 256);  // entries
+    s += align_up(n * rev_groups(d.Nc) * 4, 256);                  // wgoff
+    s += align_up((size_t)d.B * d.Hkv * d.Nc * d.top_k * 4, 256);  // entries
     return s;
 }
 
@@ -115,7 +119,7 @@ SparseWs carve_plan_ws(void* base, const Dims& d) {
     w.off = (int32_t*)p;      p += align_up((n + 1) * 4, 256);
     w.item_off = (int32_t*)p; p += align_up((n + 1) * 4, 256);
     w.cursor = (int32_t*)p;   p += align_up(n * 4, 256);
-    w.wgoff = (int32_t*)p;    p += align_up(n * rev_groups(d.N) * 4, 256);
+    w.wgoff = (int32_t*)p;    p += align_up(n * rev_groups(d.Nc) * 4, 256);
     w.entries = (int32_t*)p;
     w.part_o = nullptr;
     w.part_lse = nullptr;
@@ -126,16 +130,40 @@ SparseWs carve_plan_ws(void* base, const Dims& d) {
 
 size_t sparse_ws_bytes(const Dims& d) {
     size_t s = plan_ws_bytes(d);
-    s += align_up((size_t)d.B * d.N * d.top_k * d.Hq * kDim * 2, 256);  // part_o
-    s += align_up((size_t)d.B * d.N * d.top_k * d.Hq * 4, 256);         // part_lse
+    s += align_up((size_t)d.B * d.Nc * d.top_k * d.Hq * kDim * 2, 256);  // part_o
+    s += align_up((size_t)d.B * d.Nc * d.top_k * d.Hq * 4, 256);         // part_lse
     return s;
+}
+
+// The largest chunk of query positions (a multiple of 128, at most N) whose sparse
+// attention workspace fits in `bytes`; 0 if not even 128 positions fit.
+int fwd_chunk(const Dims& d, size_t bytes) {
+    Dims c = d;
+    int lo = 0, hi = d.N / kBlock;  // in units of 128 positions
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        c.Nc = mid * kBlock;
+        if (sparse_ws_bytes(c) <= bytes) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo * kBlock;
+}
+
+// Workspace the library asks for: the whole sequence in one pass when that needs at
+// most this much, else the chunk that fits it (the per-slot partials grow with N).
+constexpr size_t kFwdWsBudget = (size_t)64 << 30;
+
+Dims fwd_chunk_dims(const Dims& d, size_t bytes) {
+    Dims c = d;
+    c.Nc = fwd_chunk(d, bytes);
+    return c;
 }
 
 SparseWs carve_sparse_ws(void* base, const Dims& d) {
     SparseWs w = carve_plan_ws(base, d);
     char* p = (char*)base + plan_ws_bytes(d);
     w.part_o = (void*)p;
-    p += align_up((size_t)d.B * d.N * d.top_k * d.Hq * kDim * 2, 256);
+    p += align_up((size_t)d.B * d.Nc * d.top_k * d.Hq * kDim * 2, 256);
     w.part_lse = (float*)p;
     return w;
 }
@@ -173,8 +201,8 @@ size_t ws_bytes(const Dims& d, msa_op op) {
     switch (op) {
         case MSA_OP_INDEX_SCORES: return 0;
         case MSA_OP_BLOCK_TOPK: return 0;
-        case MSA_OP_SPARSE_ATTN_FWD: return sparse_ws_bytes(d);
-        case MSA_OP_FWD: return index_topk_ws_bytes(d) + sparse_ws_bytes(d);
+        case MSA_OP_SPARSE_ATTN_FWD: return sparse_ws_bytes(fwd_chunk_dims(d, kFwdWsBudget));
+        case MSA_OP_FWD: return index_topk_ws_bytes(d) + sparse_ws_bytes(fwd_chunk_dims(d, kFwdWsBudget));
         case MSA_OP_SPARSE_ATTN_BWD: return bwd_ws_bytes(d);
         case MSA_OP_INDEX_TOPK: return index_topk_ws_bytes(d);
         case MSA_OP_DECODE: return dec_ws_bytes(d);
@@ -222,6 +250,25 @@ hipError_t run_index_topk(const void* q_idx, const void* k_idx, int32_t* block_i
 }
 
 msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
+
+// Sparse attention over every query position, in chunks of `chunk` positions that
+// reuse one workspace (plan, partials); each chunk's rows only read K/V and the block
+// indices, so the chunks are independent.
+hipError_t run_sparse_attn(const void* q, const void* k, const void* v, const int32_t* block_idx, void* o, float* lse,
+                           void* workspace, const Dims& d, int chunk, hipStream_t stream) {
+    Dims c = d;
+    c.Nc = chunk;
+    const SparseWs ws = carve_sparse_ws(workspace, c);
+    hipError_t e = hipSuccess;
+    for (int p0 = 0; p0 < d.N && e == hipSuccess; p0 += chunk) {
+        c.p0 = p0;
+        c.Nc = d.N - p0 < chunk ? d.N - p0 : chunk;
+        e = launch_sparse_plan(block_idx, ws, c, false, stream);
+        if (e == hipSuccess) e = launch_sparse_partial(q, k, v, ws, c, stream);
+        if (e == hipSuccess) e = launch_sparse_combine(block_idx, o, lse, ws, c, stream);
+    }
+    return e;
+}
 
 }  // namespace
 
@@ -291,14 +338,10 @@ msa_status msa_sparse_attn_fwd(const msa_shape* shape, const void* q, const void
     const msa_status st = check_shape(shape, &d);
     if (st != MSA_OK) return st;
     if (!q || !k || !v || !block_idx || !o || !lse) return MSA_ERR_INVALID_ARG;
-    const size_t need = ws_bytes(d, MSA_OP_SPARSE_ATTN_FWD);
-    if (!workspace || workspace_bytes < need) return MSA_ERR_WORKSPACE;
+    const int chunk = workspace ? fwd_chunk(d, workspace_bytes) : 0;
+    if (chunk == 0) return MSA_ERR_WORKSPACE;
     (void)hipGetLastError();
-    const SparseWs ws = carve_sparse_ws(workspace, d);
-    hipError_t e = launch_sparse_plan(block_idx, ws, d, false, stream);
-    if (e == hipSuccess) e = launch_sparse_partial(q, k, v, ws, d, stream);
-    if (e == hipSuccess) e = launch_sparse_combine(block_idx, o, lse, ws, d, stream);
-    return hip_status(e);
+    return hip_status(run_sparse_attn(q, k, v, block_idx, o, lse, workspace, d, chunk, stream));
 }
 
 msa_status msa_sparse_attn_plan(const msa_shape* shape, const int32_t* block_idx, void* workspace,
@@ -307,7 +350,7 @@ msa_status msa_sparse_attn_plan(const msa_shape* shape, const int32_t* block_idx
     const msa_status st = check_shape(shape, &d);
     if (st != MSA_OK) return st;
     if (!block_idx) return MSA_ERR_INVALID_ARG;
-    if (!workspace || workspace_bytes < ws_bytes(d, MSA_OP_SPARSE_ATTN_FWD)) return MSA_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < sparse_ws_bytes(d)) return MSA_ERR_WORKSPACE;
     (void)hipGetLastError();
     return hip_status(launch_sparse_plan(block_idx, carve_sparse_ws(workspace, d), d, false, stream));
 }
@@ -318,7 +361,7 @@ msa_status msa_sparse_attn_partial(const msa_shape* shape, const void* q, const 
     const msa_status st = check_shape(shape, &d);
     if (st != MSA_OK) return st;
     if (!q || !k || !v) return MSA_ERR_INVALID_ARG;
-    if (!workspace || workspace_bytes < ws_bytes(d, MSA_OP_SPARSE_ATTN_FWD)) return MSA_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < sparse_ws_bytes(d)) return MSA_ERR_WORKSPACE;
     (void)hipGetLastError();
     return hip_status(launch_sparse_partial(q, k, v, carve_sparse_ws(workspace, d), d, stream));
 }
@@ -329,7 +372,7 @@ msa_status msa_sparse_attn_combine(const msa_shape* shape, const int32_t* block_
     const msa_status st = check_shape(shape, &d);
     if (st != MSA_OK) return st;
     if (!block_idx || !o || !lse) return MSA_ERR_INVALID_ARG;
-    if (!workspace || workspace_bytes < ws_bytes(d, MSA_OP_SPARSE_ATTN_FWD)) return MSA_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < sparse_ws_bytes(d)) return MSA_ERR_WORKSPACE;
     (void)hipGetLastError();
     return hip_status(launch_sparse_combine(block_idx, o, lse, carve_sparse_ws(workspace, d), d, stream));
 }
@@ -342,17 +385,14 @@ msa_status msa_fwd(const msa_shape* shape, const void* q_idx, const void* k_idx,
     if (st != MSA_OK) return st;
     if (!q_idx || !k_idx || !q || !k || !v || !block_idx || !o || !lse) return MSA_ERR_INVALID_ARG;
     if (!index_topk_fusable(d) && !topk_supported(d.nblk, d.top_k)) return MSA_ERR_UNSUPPORTED;
-    const size_t need = ws_bytes(d, MSA_OP_FWD);
-    if (!workspace || workspace_bytes < need) return MSA_ERR_WORKSPACE;
+    const size_t sel_bytes = index_topk_ws_bytes(d);
+    if (!workspace || workspace_bytes < sel_bytes) return MSA_ERR_WORKSPACE;
+    const int chunk = fwd_chunk(d, workspace_bytes - sel_bytes);
+    if (chunk == 0) return MSA_ERR_WORKSPACE;
     (void)hipGetLastError();
-    void* rest = (char*)workspace + index_topk_ws_bytes(d);
     hipError_t e = run_index_topk(q_idx, k_idx, block_idx, workspace, d, stream);
     if (e != hipSuccess) return MSA_ERR_HIP;
-    const SparseWs ws = carve_sparse_ws(rest, d);
-    e = launch_sparse_plan(block_idx, ws, d, false, stream);
-    if (e == hipSuccess) e = launch_sparse_partial(q, k, v, ws, d, stream);
-    if (e == hipSuccess) e = launch_sparse_combine(block_idx, o, lse, ws, d, stream);
-    return hip_status(e);
+    return hip_status(run_sparse_attn(q, k, v, block_idx, o, lse, (char*)workspace + sel_bytes, d, chunk, stream));
 }
 
 msa_status msa_index_topk(const msa_shape* shape, const void* q_idx, const void* k_idx, int32_t* block_idx,

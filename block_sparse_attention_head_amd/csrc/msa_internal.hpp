@@ -15,6 +15,9 @@ constexpr int kRowTilesPerItem = 16;  // 128-row query tiles per sparse-attentio
 struct Dims {
     int B, N, Hq, Hkv, G, gshift, nblk, top_k;
     float scale;
+    // query positions [p0, p0 + Nc) handled by one pass of the sparse attention (plan,
+    // partial, combine) and sized in its workspace; the whole sequence unless chunked
+    int p0 = 0, Nc = 0;
 };
 
 // Index scores + causal block max-pool. Writes pooled[b,g,t,c] for c <= t/128;

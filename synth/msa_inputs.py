@@ -83,29 +83,35 @@ WORKLOADS: Dict[str, Workload] = {
     # 131072 tokens (1024 blocks), 64 query heads on 4 KV heads (the 109B model's
     # attention shape), top-16.
     "n128k": Workload("n128k", batch=1, seqlen=131072, h_q=64, h_kv=4, h_idx=4, top_k=16, seed=3),
+    # 2^20 tokens (8192 blocks) on the 128K workload's heads: the context length of the pages'
+    # prefill figure (inputs drawn on the GPU)
+    "n1m": Workload("n1m", batch=1, seqlen=1 << 20, h_q=64, h_kv=4, h_idx=4, top_k=16, seed=9),
     # main-branch training step: 65536 tokens, 32 query heads on 8 KV heads, top-16.
     "n64k_train": Workload("n64k_train", batch=1, seqlen=65536, h_q=32, h_kv=8, h_idx=8, top_k=16,
                            seed=4, with_grad=True),
 }
 
 
-def make_inputs(w: Workload, generator_seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
-    """Draw the workload's inputs on the CPU as contiguous bfloat16 tensors.
+def make_inputs(w: Workload, generator_seed: Optional[int] = None, device: str = "cpu") -> Dict[str, torch.Tensor]:
+    """Draw the workload's inputs as contiguous bfloat16 tensors, on the CPU by default
+    (a GPU generator draws a different, equally seeded stream: for sizes the CPU
+    would take minutes over).
 
     Returns a dict with q, k, v, q_idx, k_idx (and d_o when ``w.with_grad``).
     """
-    g = torch.Generator(device="cpu")
+    g = torch.Generator(device=device)
     g.manual_seed(w.seed if generator_seed is None else generator_seed)
     B, N = w.batch, w.seqlen
     f32 = torch.float32
-    q = torch.randn((B, N, w.h_q, w.head_dim), generator=g, dtype=f32)
-    k = torch.randn((B, N, w.h_kv, w.head_dim), generator=g, dtype=f32)
-    v = torch.randn((B, N, w.h_kv, w.head_dim), generator=g, dtype=f32)
-    q_idx = torch.randn((B, N, w.h_idx, w.idx_dim), generator=g, dtype=f32)
-    k_idx = torch.randn((B, N, w.idx_dim), generator=g, dtype=f32)
-    u = torch.randn((B, w.nblk, w.idx_dim), generator=g, dtype=f32)
+    q = torch.randn((B, N, w.h_q, w.head_dim), generator=g, dtype=f32, device=device)
+    q = q.to(torch.bfloat16) if device != "cpu" else q
+    k = torch.randn((B, N, w.h_kv, w.head_dim), generator=g, dtype=f32, device=device)
+    v = torch.randn((B, N, w.h_kv, w.head_dim), generator=g, dtype=f32, device=device)
+    q_idx = torch.randn((B, N, w.h_idx, w.idx_dim), generator=g, dtype=f32, device=device)
+    k_idx = torch.randn((B, N, w.idx_dim), generator=g, dtype=f32, device=device)
+    u = torch.randn((B, w.nblk, w.idx_dim), generator=g, dtype=f32, device=device)
     u = u / u.norm(dim=-1, keepdim=True)
-    block_of = torch.arange(N) // w.block_size
+    block_of = torch.arange(N, device=device) // w.block_size
     k_idx += w.offset_scale * u[:, block_of, :]
     out = {
         "q": q.to(torch.bfloat16),
@@ -116,7 +122,7 @@ def make_inputs(w: Workload, generator_seed: Optional[int] = None) -> Dict[str, 
     }
     del q, k, v, q_idx, k_idx
     if w.with_grad:
-        out["d_o"] = torch.randn((B, N, w.h_q, w.head_dim), generator=g, dtype=f32).to(torch.bfloat16)
+        out["d_o"] = torch.randn((B, N, w.h_q, w.head_dim), generator=g, dtype=f32, device=device).to(torch.bfloat16)
     return out
 
 

@@ -202,3 +202,20 @@ def test_index_bwd_validation(m):
     assert call(s, 0.1, float("nan"), one, 1 << 40) == 1
     assert call(s, 0.1, 1.0, one, 8) == 3
     assert call(m.make_shape(1, 1024, 128, 2, 4, 0.1), 0.1, 1.0, one, 1 << 40) == 2  # 64 heads per group
+
+
+def test_forward_workspace_is_bounded_by_chunking(m):
+    # 1M tokens, 64 query heads, top-16: one pass would need 2^20 * 16 * 64 * 260 B of per-slot
+    # partials (about 280 GB); the library asks for one chunk's worth under its 64 GiB budget
+    s = m.make_shape(1, 1 << 20, 64, 4, 16, 0.1)
+    n = ctypes.c_size_t(0)
+    assert m.lib().msa_workspace_size(ctypes.byref(s), m.OP_FWD, ctypes.byref(n)) == 0
+    assert (32 << 30) < n.value <= (64 << 30)
+    small = m.make_shape(1, 128 * 1024, 64, 4, 16, 0.1)
+    n2 = ctypes.c_size_t(0)
+    assert m.lib().msa_workspace_size(ctypes.byref(small), m.OP_FWD, ctypes.byref(n2)) == 0
+    assert n2.value < n.value  # 128K tokens fit in one pass
+    P = ctypes.c_void_p
+    one = P(16)
+    # a workspace below one chunk of 128 positions is refused before any launch
+    assert m.lib().msa_fwd(ctypes.byref(s), one, one, one, one, one, one, one, one, one, 4096, P(0)) == 3

@@ -141,6 +141,33 @@ def test_fused_index_topk_ties_take_lower_blocks(msa):
     assert (zero_rows == want[None]).all()
 
 
+@pytest.mark.parametrize("N,hq,hkv,k,chunk", [(4096, 8, 2, 4, 1024), (1024, 4, 1, 3, 384), (2048, 64, 4, 16, 128)])
+def test_forward_in_position_chunks_matches_one_pass(msa, N, hq, hkv, k, chunk):
+    # a workspace for `chunk` query positions runs the sparse attention chunk by chunk
+    # (the last one ragged); every (t, slot) record and every combine reads only its own
+    # row's inputs, so the result is identical bit for bit
+    w = small_workload(N, hq, hkv, k, seed=700 + N + chunk)
+    xg = {kk: v.to(DEV) for kk, v in make_inputs(w).items()}
+    _say(w.name, f"forward in chunks of {chunk} positions")
+    shape = msa.make_shape(1, N, hq, hkv, k, w.softmax_scale)
+    bi1, o1, l1 = msa.msa_fwd(xg["q_idx"], xg["k_idx"], xg["q"], xg["k"], xg["v"], k, w.softmax_scale)
+    small = msa.make_shape(1, chunk, hq, hkv, k, w.softmax_scale)
+    # the chunked workspace: the forward's for `chunk` positions, plus the plan's per-tile arrays of all N
+    n_ws = msa.workspace_size(small, msa.OP_SPARSE_ATTN_FWD) + msa.workspace_size(shape, msa.OP_INDEX_TOPK) + \
+        16 * 4 * (N // 128) * hkv + (1 << 16)
+    assert n_ws < msa.workspace_size(shape, msa.OP_FWD)
+    ws = torch.empty(n_ws, dtype=torch.uint8, device=DEV)
+    bi2, o2, l2 = msa.msa_fwd(xg["q_idx"], xg["k_idx"], xg["q"], xg["k"], xg["v"], k, w.softmax_scale, workspace=ws)
+    o3, l3 = msa.sparse_attn_fwd(xg["q"], xg["k"], xg["v"], bi1, w.softmax_scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(bi1, bi2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    with pytest.raises(msa.MsaError) as e:  # the stage-wise calls need the whole sequence in one pass
+        msa.sparse_attn_plan(shape, bi1, ws)
+    assert e.value.status == 3
+
+
 def test_dense_reduction_on_gpu(msa):
     # top_k covering every block: the GPU path must equal dense causal GQA attention
     w = small_workload(1024, 8, 2, 8, seed=21)
