@@ -95,7 +95,11 @@ typedef enum msa_op {
 
 /* Bytes of device workspace `op` needs for `shape` (0 is a valid answer).
  * The workspace is scratch owned by the caller, needs no initialisation, and
- * must not be used by anything else while the call's work runs. */
+ * must not be used by anything else while the call's work runs.
+ * MSA_OP_SPARSE_ATTN_FWD and MSA_OP_FWD: the per-slot partial results grow with
+ * seqlen * top_k * h_q, so the answer is the size for one pass over all query
+ * positions when that is at most 64 GiB, and otherwise the size for the largest
+ * chunk of positions (a multiple of 128) that fits in 64 GiB. */
 msa_status msa_workspace_size(const msa_shape* shape, msa_op op, size_t* bytes);
 
 /* Index scores with causal block max-pool ([MSA summary] "Architecture";
@@ -141,15 +145,20 @@ msa_status msa_index_topk(const msa_shape* shape, const void* q_idx, const void*
  * with no valid entry gives o = 0 and lse = -inf. Runs KV-outer: each
  * (key block, KV head) tile gathers the queries that selected it ([MSA summary]
  * "GPU kernel co-design"), writes per-slot partial results into the workspace,
- * and a combine pass merges them. Deterministic (no floating-point atomics). */
+ * and a combine pass merges them. Deterministic (no floating-point atomics).
+ * Any workspace that holds the partials of at least 128 query positions is
+ * accepted: the positions are then processed in as many chunks as it takes
+ * (each chunk reads only its rows' block indices; all K/V stay where they are),
+ * with results identical to one pass. */
 msa_status msa_sparse_attn_fwd(const msa_shape* shape, const void* q, const void* k, const void* v,
                                const int32_t* block_idx, void* o, float* lse,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* The three phases of msa_sparse_attn_fwd, for callers that schedule or time
- * them separately. All three take the workspace sized for
- * MSA_OP_SPARSE_ATTN_FWD and must be enqueued in this order on one stream with
- * the same shape and workspace:
+ * them separately. They process the whole sequence in one pass, so all three
+ * need the one-pass workspace (MSA_ERR_WORKSPACE otherwise; msa_workspace_size
+ * gives it whenever it is at most 64 GiB), and must be enqueued in this order
+ * on one stream with the same shape and workspace:
  *   plan:    reverse sparse index ([Flash-MSA] "Backward": the map from
  *            (query, slot) to key block is inverted into key block -> queries;
  *            [MSA summary] "GPU kernel co-design": reverse sparse indexing)
@@ -167,7 +176,9 @@ msa_status msa_sparse_attn_combine(const msa_shape* shape, const int32_t* block_
 
 /* The whole forward: msa_index_topk into `block_idx`, then msa_sparse_attn_fwd
  * into `o` and `lse` ([Flash-MSA] "Forward": index branch
- * first, then sparse main attention; block indices and LSE are kept). */
+ * first, then sparse main attention; block indices and LSE are kept). The
+ * workspace holds msa_index_topk's (0 bytes for top_k <= 17) followed by the
+ * sparse attention's, which may be a chunk's (see msa_sparse_attn_fwd). */
 msa_status msa_fwd(const msa_shape* shape, const void* q_idx, const void* k_idx, const void* q,
                    const void* k, const void* v, int32_t* block_idx, void* o, float* lse,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
