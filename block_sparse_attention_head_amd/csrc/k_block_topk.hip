@@ -20,7 +20,9 @@
 //      `need` are the selection;
 //   5. the chosen blocks are put in ascending order, the local block last.
 // Rows of up to 1025 blocks keep their scores in registers and work on 32-bit
-// score keys first (msa_topk.hpp); longer rows use k_block_topk below.
+// score keys first (msa_topk.hpp), with a 128-entry candidate list (rows with
+// more candidates, from many equal scores, take an exact list-free path), so
+// six waves fit per SIMD; longer rows use k_block_topk below.
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 #include "msa_topk.hpp"
@@ -108,42 +110,27 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
 }
 
 // Rows of at most 64 * kTopkRegVals non-local blocks: each wave walks a strided
-// sequence of rows, keeps the current row's scores in registers (one load per
-// score) and issues the next row's loads before ranking the current one. The
-// threshold works on 32-bit score keys: the need-th largest lane maximum of the
-// score keys, T32, is the high word of the need-th largest 64-bit lane maximum,
-// so every key of the exact selection has a score key >= T32. Only those
-// candidates get 64-bit (score, block) keys and are ranked exactly.
-__global__ __launch_bounds__(256) void k_block_topk_reg(const float* __restrict__ pooled,
-                                                        int32_t* __restrict__ block_idx, int N, int nblk, int top_k,
-                                                        long long rows) {
-    __shared__ __attribute__((aligned(16))) uint64_t cand[kTopkWaves][64 * kTopkRegVals + 4];
+// sequence of rows and keeps the current row's scores in registers (one load
+// per score). The threshold works on 32-bit score keys: the need-th largest
+// lane maximum of the score keys, T32, is the high word of the need-th largest
+// 64-bit lane maximum, so every key of the exact selection has a score key
+// >= T32. Only those candidates get 64-bit (score, block) keys and are ranked
+// exactly. No row is prefetched: the registers that would take go to
+// occupancy (six waves per SIMD), which hides the loads better. The grid holds
+// as many workgroups as are resident at once.
+__global__ __launch_bounds__(256) void k_block_topk_reg(
+    const float* __restrict__ pooled, int32_t* __restrict__ block_idx, int N, int nblk, int top_k, long long rows) {
+    __shared__ __attribute__((aligned(16))) uint64_t cand[kTopkWaves][kTopkListCap + 4];
     __shared__ __attribute__((aligned(16))) int32_t chosen[kTopkWaves][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const long long stride = (long long)gridDim.x * kTopkWaves;
     const int need = top_k - 1;
     uint64_t* list = cand[wave];
-
-    long long row = (long long)blockIdx.x * kTopkWaves + wave;
-    float v[kTopkRegVals];
-    if (row < rows) {
-        const int cl = (int)(row % N) >> 7;
-        if (cl + 1 > top_k) topk_load_row(pooled + row * nblk, cl, lane, v);
-    }
-    for (; row < rows; row += stride) {
+    for (long long row = (long long)blockIdx.x * kTopkWaves + wave; row < rows; row += stride) {
         const int t = (int)(row % N);
         const int cl = t >> 7;
         int32_t* dst = block_idx + row * top_k;
-        const bool rank_row = cl + 1 > top_k;
-        float cur[kTopkRegVals];
-#pragma unroll
-        for (int i = 0; i < kTopkRegVals; ++i) cur[i] = v[i];
-        const long long nrow = row + stride;  // prefetch the next row's scores
-        if (nrow < rows) {
-            const int ncl = (int)(nrow % N) >> 7;
-            if (ncl + 1 > top_k) topk_load_row(pooled + nrow * nblk, ncl, lane, v);
-        }
-        if (!rank_row) {  // every visible block
+        if (cl + 1 <= top_k) {  // every visible block
             for (int s = lane; s < top_k; s += 64) dst[s] = s <= cl ? s : -1;
             continue;
         }
@@ -151,8 +138,9 @@ __global__ __launch_bounds__(256) void k_block_topk_reg(const float* __restrict_
             if (lane == 0) dst[0] = cl;
             continue;
         }
+        float cur[kTopkRegVals];
+        topk_load_row(pooled + row * nblk, cl, lane, cur);
         topk_row_from_regs(cur, cl, need, list, chosen[wave], dst, lane);
-        // the next row reuses this wave's LDS lists
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");

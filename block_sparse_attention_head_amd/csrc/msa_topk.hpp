@@ -67,16 +67,52 @@ __device__ __forceinline__ void rank_and_emit(uint64_t* list, int32_t* chosen, i
     if (lane == 0) dst[need] = cl;
 }
 
+// A row with more candidates than the list holds (many equal scores): exact
+// without a list. T = the need-th largest score key of the row, counted with
+// multiplicity, found bit by bit; every key above T is chosen (fewer than
+// `need`), then the lowest blocks among the keys equal to T fill the rest
+// (equal scores go to the lower block). Blocks are lane + 64 i, so ascending
+// block order is (i, lane) order and ballot prefix counts place each one.
+__device__ __forceinline__ void topk_row_ties(const uint32_t (&k32)[kTopkRegVals], int cl, int need,
+                                              int32_t* __restrict__ dst, int lane) {
+    const uint64_t lt = (1ull << lane) - 1ull;
+    uint32_t T = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand_t = T | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < kTopkRegVals; ++i) cnt += __popcll(__ballot(k32[i] >= cand_t));
+        if (cnt >= need) T = cand_t;
+    }
+    int above = 0;
+#pragma unroll
+    for (int i = 0; i < kTopkRegVals; ++i) above += __popcll(__ballot(k32[i] > T));
+    const int rem = need - above;  // >= 1 keys equal to T are taken, lowest blocks first
+    int eq_before = 0, base = 0;
+#pragma unroll
+    for (int i = 0; i < kTopkRegVals; ++i) {
+        const uint64_t eq = __ballot(k32[i] == T);
+        const bool take = k32[i] > T || (k32[i] == T && eq_before + __popcll(eq & lt) < rem);
+        eq_before += __popcll(eq);
+        const uint64_t tm = __ballot(take);
+        if (take) dst[base + __popcll(tm & lt)] = lane + 64 * i;
+        base += __popcll(tm);
+    }
+    if (lane == 0) dst[need] = cl;
+}
+
 // Steps 1-5 for one row whose non-local scores (blocks lane + 64 i < cl) are in
 // registers: the threshold works on 32-bit score keys. The need-th largest lane
 // maximum of the score keys, T32, is the high word of the need-th largest
 // 64-bit lane maximum, so every key of the exact selection has a score key
-// >= T32. Only those candidates get 64-bit (score, block) keys, ranked exactly.
-// `list` holds 64 * kTopkRegVals + 4 keys, `chosen` 64 ints; both per wave.
+// >= T32. Only those candidates get 64-bit (score, block) keys, ranked exactly;
+// more than kTopkListCap of them (ties) take topk_row_ties instead.
+// `list` holds kTopkListCap + 4 keys, `chosen` 64 ints; both per wave.
+constexpr int kTopkListCap = 128;
+
 __device__ __forceinline__ void topk_row_from_regs(const float (&cur)[kTopkRegVals], int cl, int need,
                                                    uint64_t* list, int32_t* chosen, int32_t* __restrict__ dst,
                                                    int lane) {
-    // 1. 32-bit score keys (0 for blocks outside the row) and their lane maximum
     uint32_t k32[kTopkRegVals];
     uint32_t lmax = 0u;
 #pragma unroll
@@ -84,32 +120,36 @@ __device__ __forceinline__ void topk_row_from_regs(const float (&cur)[kTopkRegVa
         k32[i] = lane + 64 * i < cl ? order_key(cur[i]) : 0u;
         lmax = k32[i] > lmax ? k32[i] : lmax;
     }
-    // 2. T32 = the need-th largest lane maximum (a real key: at least need + 1 lanes hold a
-    // block, since cl >= top_k), bit by bit from the top: keep a bit when at least `need`
-    // lane maxima are >= the value with it set
     uint32_t T = 0u;
 #pragma unroll
     for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand_t = T | (1u << bit);
         if (__popcll(__ballot(lmax >= cand_t)) >= need) T = cand_t;
     }
-    // 3. candidates: score key >= T, as 64-bit (score, block) keys
+    uint64_t masks[kTopkRegVals];
     int n = 0;
 #pragma unroll
     for (int i = 0; i < kTopkRegVals; ++i) {
-        const bool take = k32[i] >= T;
-        const uint64_t mask = __ballot(take);
-        if (mask != 0ull) {  // wave-uniform: most groups hold no candidate
-            if (take)
-                list[n + __popcll(mask & ((1ull << lane) - 1ull))] =
+        masks[i] = __ballot(k32[i] >= T);
+        n += __popcll(masks[i]);
+    }
+    if (n > kTopkListCap) {
+        topk_row_ties(k32, cl, need, dst, lane);
+        return;
+    }
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < kTopkRegVals; ++i) {
+        if (masks[i] != 0ull) {
+            if (k32[i] >= T)
+                list[base + __popcll(masks[i] & ((1ull << lane) - 1ull))] =
                     ((uint64_t)k32[i] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * i));
-            n += __popcll(mask);
+            base += __popcll(masks[i]);
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // 4, 5. exact rank among the candidates; ascending output, local block last
     rank_and_emit(list, chosen, n, need, cl, dst, lane);
 }
 
