@@ -14,7 +14,8 @@ dominant kernel, per-stage figures, the CPU oracle baseline, (unless
 --no-backward) a "backward" object: msa_sparse_attn_bwd timed at the
 64K-token training shape, (unless --no-decode) a "decode" object: one
 decode step (msa_decode's three stages) for 128 sequences of 64K-128K tokens,
-and (unless --no-long-context) a "long_context" object: msa_fwd at 2^20 tokens.
+and (unless --no-long-context) a "long_context" object: msa_fwd at 2^20 tokens,
+and a "long_training" object: forward and both backward passes at 2^20 tokens.
 
     python bench.py [--steps K] [--warmup W] [--workload n128k] [--gpus 1]
 """
@@ -281,6 +282,64 @@ def long_context_report(w, steps: int, warmup: int):
             "outputs_finite": finite, "local_block_last": local}
 
 
+def long_training_report(w, steps: int, warmup: int):
+    """One training step of the attention at 2^20 tokens: msa_fwd, msa_sparse_attn_bwd and
+    msa_index_bwd, each timed with HIP events; each workspace is allocated for its phase and
+    freed after it (the three do not fit in HBM at once)."""
+    import torch
+
+    from block_sparse_attention_head_amd import msa
+    from block_sparse_attention_head_amd import perfmodel as P
+    from synth.msa_inputs import make_inputs
+
+    print(f"[bench] long training: generating {w.name} inputs on the GPU", file=sys.stderr, flush=True)
+    xg = make_inputs(w, device="cuda:0")
+    B, N, Hq, Hkv, K = w.batch, w.seqlen, w.h_q, w.h_kv, w.top_k
+    dev = xg["q"].device
+    shape = msa.make_shape(B, N, Hq, Hkv, K, w.softmax_scale)
+    block_idx = torch.empty((B, Hkv, N, K), dtype=torch.int32, device=dev)
+    o = torch.empty_like(xg["q"])
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(xg["q"]), torch.empty_like(xg["k"]), torch.empty_like(xg["v"])
+    dqi, dki = torch.empty_like(xg["q_idx"]), torch.empty_like(xg["k_idx"])
+    res, gb = {}, {}
+
+    def timed(name, op, fn):
+        ws = msa.alloc_workspace(shape, op, dev)
+        gb[name] = round(ws.numel() / 1e9, 1)
+        for _ in range(warmup):
+            fn(ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn(ws)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps
+        del ws
+        torch.cuda.empty_cache()
+
+    timed("fwd", msa.OP_FWD, lambda ws: msa.msa_fwd(xg["q_idx"], xg["k_idx"], xg["q"], xg["k"], xg["v"], K,
+                                                    w.softmax_scale, block_idx, o, lse, workspace=ws))
+    timed("bwd", msa.OP_SPARSE_ATTN_BWD, lambda ws: msa.sparse_attn_bwd(
+        xg["q"], xg["k"], xg["v"], o, lse, xg["d_o"], block_idx, w.softmax_scale, dq, dk, dv, ws))
+    timed("index_bwd", msa.OP_INDEX_BWD, lambda ws: msa.index_bwd(
+        xg["q_idx"], xg["k_idx"], xg["q"], xg["k"], lse, block_idx, w.softmax_scale, dq_idx=dqi, dk_idx=dki,
+        workspace=ws))
+    finite = all(bool(torch.isfinite(t[:, ::4099].float()).all()) for t in (o, dq, dk, dv, dqi, dki))
+    s = P.Shape(B, N, Hq, Hkv, K)
+    flop = P.index_flops(s) + P.main_flops(s) + P.bwd_flops(s) + P.index_bwd_flops(s)
+    step = res["fwd"] + res["bwd"] + res["index_bwd"]
+    del xg, block_idx, o, lse, dq, dk, dv, dqi, dki
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "config": {"batch": B, "seqlen": N, "h_q": Hq, "h_kv": Hkv, "h_idx": w.h_idx,
+                                           "top_k": K},
+            "what": "msa_fwd + msa_sparse_attn_bwd + msa_index_bwd", "ms": {k: round(v, 2) for k, v in res.items()},
+            "step_ms": round(step, 2), "tokens_s": round(B * N / (step / 1e3), 1),
+            "tflops": round(flop / 1e12 / (step / 1e3), 2), "workspace_GB": gb, "outputs_finite": finite}
+
+
 def two_kernel_selection(msa, xg, w, block_idx_single, steps: int, warmup: int):
     """msa_index_scores (pooled scores to HBM) then msa_block_topk, on the step's inputs,
     timed with HIP events per kernel; the indices must equal the single pass's."""
@@ -324,7 +383,8 @@ def main(argv=None) -> int:
     ap.add_argument("--backward-only", action="store_true",
                     help="only the backward measurement (a JSON line with the backward object), for profiling")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
-    ap.add_argument("--no-long-context", action="store_true", help="skip the 2^20-token forward")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="skip the 2^20-token forward and the 2^20-token training step")
     ap.add_argument("--decode-workload", default="dec_b128_n128k")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode measurement (a JSON line with the decode object), for profiling")
@@ -483,6 +543,10 @@ def main(argv=None) -> int:
             out["long_context"] = long_context_report(WORKLOADS["n1m"], min(a.steps, 2), min(a.warmup, 1))
         except Exception as exc:  # pragma: no cover
             out["long_context"] = {"error": f"{type(exc).__name__}: {exc}"}
+        try:
+            out["long_training"] = long_training_report(WORKLOADS["n1m_train"], 1, 1)
+        except Exception as exc:  # pragma: no cover
+            out["long_training"] = {"error": f"{type(exc).__name__}: {exc}"}
     if not a.no_cpu_baseline:
         print(f"[bench] CPU oracle baseline (~{a.cpu_budget:.0f} s)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, x, a.cpu_budget)

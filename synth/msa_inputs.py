@@ -86,6 +86,10 @@ WORKLOADS: Dict[str, Workload] = {
     # 2^20 tokens (8192 blocks) on the 128K workload's heads: the context length of the pages'
     # prefill figure (inputs drawn on the GPU)
     "n1m": Workload("n1m", batch=1, seqlen=1 << 20, h_q=64, h_kv=4, h_idx=4, top_k=16, seed=9),
+    # the training step's heads at 2^20 tokens: the length of the training pages' title
+    # (inputs drawn on the GPU)
+    "n1m_train": Workload("n1m_train", batch=1, seqlen=1 << 20, h_q=32, h_kv=8, h_idx=8, top_k=16, seed=10,
+                          with_grad=True),
     # main-branch training step: 65536 tokens, 32 query heads on 8 KV heads, top-16.
     "n64k_train": Workload("n64k_train", batch=1, seqlen=65536, h_q=32, h_kv=8, h_idx=8, top_k=16,
                            seed=4, with_grad=True),
