@@ -41,10 +41,12 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-# Per-source extra flags. The index max-pool never needs NaN quieting, so its
-# fmaxf chains compile to plain v_max_f32 instead of canonicalise + max.
+# Per-source extra flags. The index max-pool and the selection's lane maxima
+# never need NaN quieting, so their fmaxf chains compile to plain v_max_f32
+# instead of canonicalise + max.
 EXTRA_FLAGS = {
     "k_index_pool.hip": ["-fno-honor-nans"],
+    "k_block_topk.hip": ["-fno-honor-nans"],
 }
 
 

@@ -19,10 +19,11 @@
 //   4. each listed key is ranked by counting larger listed keys; ranks below
 //      `need` are the selection;
 //   5. the chosen blocks are put in ascending order, the local block last.
-// Rows of up to 1025 blocks keep their scores in registers and work on 32-bit
-// score keys first (msa_topk.hpp), with a 128-entry candidate list (rows with
-// more candidates, from many equal scores, take an exact list-free path), so
-// six waves fit per SIMD; longer rows use k_block_topk below.
+// Rows of up to 1025 blocks keep their scores in registers (msa_topk.hpp):
+// four 16-byte buffer loads per lane, a 16-bit bound on the lane maxima, a
+// 128-entry candidate list in ascending block order and ballot-placed output;
+// rows it cannot take (bound not above zero, or many equal scores) are
+// selected exactly from memory. Longer rows use k_block_topk below.
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 #include "msa_topk.hpp"
@@ -44,7 +45,6 @@ bool topk_supported(int nblk, int top_k) {
 __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ pooled, int32_t* __restrict__ block_idx,
                                                     int N, int nblk, int top_k, long long rows) {
     __shared__ __attribute__((aligned(16))) uint64_t cand[kTopkWaves][kTopkCap + 4];
-    __shared__ __attribute__((aligned(16))) int32_t chosen[kTopkWaves][64];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const long long row = (long long)blockIdx.x * kTopkWaves + wave;
@@ -106,28 +106,26 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // 4, 5. rank the listed keys; ascending output, local block last
-    rank_and_emit(list, chosen[wave], n, need, cl, dst, lane);
+    rank_and_emit(list, n, need, cl, dst, lane);
 }
 
-// Rows of at most 64 * kTopkRegVals non-local blocks: each wave walks a strided
-// sequence of rows and keeps the current row's scores in registers (one load
-// per score). The threshold works on 32-bit score keys: the need-th largest
-// lane maximum of the score keys, T32, is the high word of the need-th largest
-// 64-bit lane maximum, so every key of the exact selection has a score key
-// >= T32. Only those candidates get 64-bit (score, block) keys and are ranked
-// exactly. No row is prefetched: the registers that would take go to
-// occupancy (six waves per SIMD), which hides the loads better. The grid holds
-// as many workgroups as are resident at once.
+// Rows of at most kTopkRowMax non-local blocks: each wave walks a strided
+// sequence of rows (the row index is wave-uniform, so the row's scalars and
+// branches stay scalar) and selects each with topk_row_quads. No row is
+// prefetched: 68 registers give seven waves per SIMD, which hide the loads.
+// The grid holds as many workgroups as are resident at once.
 __global__ __launch_bounds__(256) void k_block_topk_reg(
     const float* __restrict__ pooled, int32_t* __restrict__ block_idx, int N, int nblk, int top_k, long long rows) {
     __shared__ __attribute__((aligned(16))) uint64_t cand[kTopkWaves][kTopkListCap + 4];
-    __shared__ __attribute__((aligned(16))) int32_t chosen[kTopkWaves][64];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const long long stride = (long long)gridDim.x * kTopkWaves;
     const int need = top_k - 1;
     uint64_t* list = cand[wave];
-    for (long long row = (long long)blockIdx.x * kTopkWaves + wave; row < rows; row += stride) {
-        const int t = (int)(row % N);
+    const long long row0 = (long long)blockIdx.x * kTopkWaves + wave;
+    // the query position row % N is stepped along with the row: no division per row
+    const int dt = (int)(stride % N);
+    int t = (int)(row0 % N);
+    for (long long row = row0; row < rows; row += stride, t = t + dt >= N ? t + dt - N : t + dt) {
         const int cl = t >> 7;
         int32_t* dst = block_idx + row * top_k;
         if (cl + 1 <= top_k) {  // every visible block
@@ -138,9 +136,7 @@ __global__ __launch_bounds__(256) void k_block_topk_reg(
             if (lane == 0) dst[0] = cl;
             continue;
         }
-        float cur[kTopkRegVals];
-        topk_load_row(pooled + row * nblk, cl, lane, cur);
-        topk_row_from_regs(cur, cl, need, list, chosen[wave], dst, lane);
+        topk_row_quads(pooled + row * nblk, cl, need, list, dst, lane);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -149,7 +145,7 @@ __global__ __launch_bounds__(256) void k_block_topk_reg(
 
 hipError_t launch_block_topk(const float* pooled, int32_t* block_idx, const Dims& d, hipStream_t stream) {
     const long long rows = (long long)d.B * d.Hkv * d.N;
-    if (d.nblk - 1 <= 64 * kTopkRegVals && d.top_k <= 65) {
+    if (d.nblk - 1 <= kTopkRowMax && d.top_k <= 65) {
         // as many workgroups as are resident at once: each wave then walks its rows with
         // no second round of workgroups waiting for a slot
         static int per_cu = 0;

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void k_dec_index(const __bf16* __restrict__ q_
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_dec_topk(const float* __restrict__ pooled, const int32_t* __restrict__ seqlens,
                                                  int32_t* __restrict__ block_idx, int C, int H, int nblk, int top_k) {
-    extern __shared__ __attribute__((aligned(16))) uint64_t dec_list[];  // nblk + 4 keys, then 64 ints
+    extern __shared__ __attribute__((aligned(16))) uint64_t dec_list[];  // nblk + 4 keys
     const int row = blockIdx.x, b = row / H;
     const int lane = threadIdx.x;
     const int L = dec_len(seqlens, b, C);
@@ -139,7 +139,6 @@ __global__ __launch_bounds__(64) void k_dec_topk(const float* __restrict__ poole
         if (__popcll(__ballot(lmax >= cand_t)) >= need) T = cand_t;
     }
     uint64_t* list = dec_list;
-    int32_t* chosen = (int32_t*)(dec_list + nblk + 4);
     int n = 0;
     for (int c0 = 0; c0 < cl; c0 += 64) {
         const int c = c0 + lane;
@@ -154,7 +153,7 @@ __global__ __launch_bounds__(64) void k_dec_topk(const float* __restrict__ poole
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    rank_and_emit(list, chosen, n, need, cl, dst, lane);
+    rank_and_emit(list, n, need, cl, dst, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -327,7 +326,7 @@ __global__ __launch_bounds__(256) void k_dec_attn(const __bf16* __restrict__ q, 
 }
 
 // ---------------------------------------------------------------------------
-size_t dec_topk_lds_bytes(const Dims& d) { return ((size_t)d.nblk + 4) * 8 + 64 * 4; }
+size_t dec_topk_lds_bytes(const Dims& d) { return ((size_t)d.nblk + 4) * 8; }
 
 hipError_t launch_dec_index(const void* q_idx, const void* k_idx, const int32_t* seqlens, float* pooled, const Dims& d,
                             hipStream_t stream) {

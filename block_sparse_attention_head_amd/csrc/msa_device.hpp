@@ -42,9 +42,12 @@ __device__ __forceinline__ int swz_chunk_offset(int row, int ch) {
 // Total order on fp32 scores as unsigned integers (larger float -> larger key),
 // with -0.0 folded onto +0.0 so that equal scores compare equal.
 __device__ __forceinline__ uint32_t order_key(float x) {
-    uint32_t u = __float_as_uint(x);
-    if (u == 0x80000000u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t u = __float_as_uint(x + 0.0f);  // -0 + 0 = +0 under round-to-nearest
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);  // negative: all bits flip; else the sign bit
+}
+// The score whose key is k (the inverse of order_key on +0 and the non-NaN floats).
+__device__ __forceinline__ float key_score(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
 // 64-bit selection key: score first, then the LOWER block index wins ties.

@@ -254,6 +254,39 @@ def test_duplicate_block_exact_tie_lower_index_wins(msa):
     assert any(2 in gi[0, 0, t] and 5 not in gi[0, 0, t] for t in rows)
 
 
+def test_block_topk_full_length_rows_every_path(msa):
+    """msa_block_topk on 1024-block rows (N = 131072) against the oracle, bit-exact, on five
+    kinds of row, each sampled at every local block from 16 to 1023: normal scores; every score
+    negative; five positive scores among negative ones; scores on three levels (ties, more
+    candidates than the kernel's list); and constant rows of +0 and -0 (equal scores)."""
+    N, nblk, k = 131072, 1024, 16
+    g = torch.Generator(device=DEV).manual_seed(77)
+    _say("block_topk 1024-block rows", "drawing")
+    p = torch.randn(1, 1, N, nblk, device=DEV, generator=g)
+    kind = ((torch.arange(N, device=DEV) // 7) % 5).view(1, 1, N, 1)
+    neg = -p.abs() - 0.5
+    few = torch.where(torch.rand(1, 1, N, nblk, device=DEV, generator=g) < 5.0 / 1024, p.abs() + 1.0, neg)
+    levels = p.round().clamp(-1.0, 1.0)
+    zeros = torch.where(torch.rand(1, 1, N, nblk, device=DEV, generator=g) < 0.5, -0.0, 0.0)
+    p = torch.where(kind == 1, neg, p)
+    p = torch.where(kind == 2, few, p)
+    p = torch.where(kind == 3, levels, p)
+    p = torch.where(kind == 4, zeros, p)
+    del neg, few, levels, zeros
+    _say("block_topk 1024-block rows", "select")
+    bi = msa.block_topk(p, k)
+    torch.cuda.synchronize()
+    rows = np.array([cl * 128 + 7 * c for cl in range(16, nblk) for c in range(5)])
+    sample = p[:, :, torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    got = to_np(bi)[:, :, rows]
+    del p, bi
+    torch.cuda.empty_cache()
+    kinds = (rows // 7) % 5
+    assert all(np.sum(kinds == c) >= 900 for c in range(5))
+    _say("block_topk 1024-block rows", f"oracle on {len(rows)} rows")
+    np.testing.assert_array_equal(got, O.block_topk(sample.astype(np.float64), k, positions=rows))
+
+
 def test_one_hot_value_probe(msa):
     w = WORKLOADS["tiny_n1k"]
     x = make_inputs(w)
