@@ -24,6 +24,8 @@
 // 128-entry candidate list in ascending block order and ballot-placed output;
 // rows it cannot take (bound not above zero, or many equal scores) are
 // selected exactly from memory. Longer rows use k_block_topk below.
+#include <atomic>
+
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 #include "msa_topk.hpp"
@@ -148,12 +150,16 @@ hipError_t launch_block_topk(const float* pooled, int32_t* block_idx, const Dims
     if (d.nblk - 1 <= kTopkRowMax && d.top_k <= 65) {
         // as many workgroups as are resident at once: each wave then walks its rows with
         // no second round of workgroups waiting for a slot
-        static int per_cu = 0;
+        // resident workgroups per CU: a property of the kernel, the same on every device of this build;
+        // computed once (a racing first call computes the same value)
+        static std::atomic<int> cached_per_cu{0};
+        int per_cu = cached_per_cu.load(std::memory_order_relaxed);
         if (per_cu <= 0) {
             int n = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_block_topk_reg, 256, 0) != hipSuccess || n <= 0)
                 n = 2;
             per_cu = n;
+            cached_per_cu.store(n, std::memory_order_relaxed);
         }
         const long long want = (rows + kTopkWaves - 1) / kTopkWaves;
         const long long cap = (long long)per_cu * device_cu_count();
