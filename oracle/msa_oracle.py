@@ -199,9 +199,11 @@ def sparse_attention(q, k, v, block_idx, softmax_scale: float, block_size: int =
     rows for the P requested positions. Returns O float64 [B, P, H_q, D] and
     LSE float64 [B, H_q, P]. A row with no attended key gives O = 0, LSE = -inf (R9).
     """
-    qq, kk, vv = _f64(q), _f64(k), _f64(v)
+    # q is widened one requested row at a time: at long lengths the whole of it
+    # in float64 would not fit in host memory, and only the requested rows are read
+    kk, vv = _f64(k), _f64(v)
     bi = np.asarray(block_idx)
-    B, N, Hq, D = qq.shape
+    B, N, Hq, D = q.shape
     Hkv = kk.shape[2]
     if Hq % Hkv:
         raise ValueError("H_q must be a multiple of H_kv")
@@ -214,13 +216,14 @@ def sparse_attention(q, k, v, block_idx, softmax_scale: float, block_size: int =
     for b in range(B):
         for i, t in enumerate(pos):
             t = int(t)
+            qt = _f64(q[b, t])                                 # [H_q, D]
             for g in range(Hkv):
                 keys = attended_keys(bi[b, g, i], t, block_size)
                 if keys.size == 0:  # R9: nothing to attend to
                     O[b, i, g * G:(g + 1) * G] = 0.0
                     LSE[b, g * G:(g + 1) * G, i] = -np.inf
                     continue
-                qg = qq[b, t, g * G:(g + 1) * G]            # [G, D]
+                qg = qt[g * G:(g + 1) * G]                     # [G, D]
                 z = softmax_scale * (qg @ kk[b, keys, g].T)  # [G, n]
                 m = z.max(axis=-1, keepdims=True)
                 p = np.exp(z - m)

@@ -222,6 +222,44 @@ def test_full_size_sampled_rows(msa, name):
     assert np.all(np.isfinite(to_np(lse)))
 
 
+def test_long_context_sampled_rows(msa):
+    # 2^20 tokens with the 128K workload's heads, as the benchmark's long-context line runs it:
+    # the one-pass selection over rows of up to 8192 blocks and the sparse attention in query
+    # chunks inside the library's own workspace; sampled positions against the oracle
+    w = WORKLOADS["n1m"]
+    _say(w.name, "generating inputs on the GPU")
+    xg = make_inputs(w, device=DEV)
+    _say(w.name, "msa_fwd")
+    bi, o, lse = msa.msa_fwd(xg["q_idx"], xg["k_idx"], xg["q"], xg["k"], xg["v"], w.top_k, w.softmax_scale)
+    torch.cuda.synchronize()
+    pos = sample_positions(w.seqlen, 12, seed=w.seed)
+    pos_t = torch.from_numpy(pos).to(DEV)
+    gi = to_np(bi[:, :, pos_t])
+    go, gl = to_np(o[:, pos_t]), to_np(lse[:, :, pos_t])
+    bic = bi.cpu().numpy().astype(np.int64)
+    lse_finite = bool(torch.isfinite(lse).all())
+    del bi, o, lse
+    x = {name: t.cpu() for name, t in xg.items()}  # host copies for the oracle
+    del xg
+    torch.cuda.empty_cache()
+    _say(w.name, f"oracle on {len(pos)} sampled positions")
+    ref_pooled = O.index_scores(x["q_idx"], x["k_idx"], positions=pos)
+    ref_idx = O.block_topk(ref_pooled, w.top_k, positions=pos)
+    n_mis, n_tie, not_tie = O.near_tie_rows(ref_pooled, gi, ref_idx, w.top_k, positions=pos)
+    assert not not_tie, f"{w.name}: {len(not_tie)} mismatching rows are not near-ties, e.g. {not_tie[:5]}"
+    _say(w.name, f"sampled index rows differing from the oracle: {n_mis} (near-ties: {n_tie})")
+    ro, rl = O.sparse_attention(x["q"], x["k"], x["v"], gi, w.softmax_scale, positions=pos)
+    do, dl = check_attn(go, gl, ro, rl, w.name)
+    _say(w.name, f"max|dO|={do:.2e} max|dLSE|={dl:.2e}")
+    # every row: local block last, min(top_k, c_loc + 1) ascending entries
+    cl = np.arange(w.seqlen) // 128
+    valid = bic >= 0
+    assert np.all(valid.sum(-1) == np.minimum(w.top_k, cl + 1)[None, None])
+    assert np.all(np.take_along_axis(bic, (valid.sum(-1, keepdims=True) - 1), -1)[..., 0] == cl[None, None])
+    assert np.all(np.where(valid[..., 1:], np.diff(bic, axis=-1) > 0, True))
+    assert lse_finite
+
+
 def test_zero_index_queries_tie_to_lowest_blocks(msa):
     w = small_workload(2048, 4, 1, 5, seed=3)
     x = make_inputs(w)
