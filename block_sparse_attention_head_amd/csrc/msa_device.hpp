@@ -12,6 +12,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // v_mfma_f32_32x32x16_bf16. Operand layouts (checked on the device):
 //   A (32 x 16): lane l holds A[l % 32][8 * (l / 32) + e], e = 0..7
