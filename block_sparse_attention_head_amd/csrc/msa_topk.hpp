@@ -125,7 +125,9 @@ __device__ __forceinline__ void topk_row_exact(const float* __restrict__ src, in
 //    order it.
 //  - Steps 2-3: the scores >= T are compacted into the wave's list per 256-block
 //    chunk in (lane, slot) order, which is ascending block order, each lane's
-//    first slot placed by the mbcnt of the chunk's four ballots.
+//    first slot placed by the mbcnt of the chunk's four ballots. The stores are
+//    unconditional (no exec-mask branch per value): a value below T is written
+//    to slot kTopkListCap + 3, past every slot the ranking reads.
 //  - Steps 4-5: rank_and_emit.
 // A bound not above zero, or more than kTopkListCap candidates, takes
 // topk_row_exact.
@@ -186,10 +188,10 @@ __device__ __forceinline__ void topk_row_quads(const float* __restrict__ src, in
             const uint32_t blk = 256u * j + 4u * lane;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                if (v[j][e] >= tf) {
-                    list[pos] = positive_key(v[j][e], blk + e);
-                    ++pos;
-                }
+                // branch-free: a value below the bound goes to a slot past the list that is never read
+                const bool take = v[j][e] >= tf;
+                list[take ? pos : (uint32_t)(kTopkListCap + 3)] = positive_key(v[j][e], blk + e);
+                pos += take ? 1u : 0u;
             }
             base += __popcll(mk[j][0]) + __popcll(mk[j][1]) + __popcll(mk[j][2]) + __popcll(mk[j][3]);
         }
