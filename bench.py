@@ -394,8 +394,8 @@ def main(argv=None) -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: the MSA forward here is a single-GPU build "
-              "(how it would shard across GPUs is described in DESIGN.md); use --gpus 1.", file=sys.stderr)
+        print("bench.py runs on one GPU only: this MSA build has no multi-GPU path (it would shard by "
+              "MSA group, one KV head and its query heads per GPU); use --gpus 1.", file=sys.stderr)
         return 2
 
     import torch
