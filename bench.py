@@ -538,6 +538,12 @@ def main(argv=None) -> int:
         out["backward"] = backward_report(WORKLOADS[a.backward_workload], a.steps, a.warmup)
     if not a.no_decode:
         out["decode"] = decode_report(DECODE_WORKLOADS[a.decode_workload], a.steps, a.warmup)
+    if not a.no_decode and not a.no_long_context:
+        # decode at the pages' long context: 16 sequences of 768K-1M cached tokens
+        try:
+            out["decode_long"] = decode_report(DECODE_WORKLOADS["dec_b16_n1m"], a.steps, a.warmup)
+        except Exception as exc:  # pragma: no cover
+            out["decode_long"] = {"error": f"{type(exc).__name__}: {exc}"}
     if not a.no_long_context:
         try:  # a failure here must not cost the main line
             out["long_context"] = long_context_report(WORKLOADS["n1m"], min(a.steps, 2), min(a.warmup, 1))

@@ -28,7 +28,7 @@ typedef __attribute__((address_space(3))) bf16x4* lds_bf16x4_ptr;
     } while (0)
 
 constexpr int kDecIdxWaves = 4;   // key blocks per index workgroup (one per wave)
-constexpr int kDecAttnWaves = 4;  // 32 keys of every selected block per wave
+constexpr int kDecAttnSlices = 4;  // 32-key slices of a block, one per wave of a slot group
 
 // Sequence length as the kernels use it: clamped to the cache capacity; <= 0 is empty.
 __device__ __forceinline__ int dec_len(const int32_t* __restrict__ seqlens, int b, int C) {
@@ -98,68 +98,123 @@ __global__ __launch_bounds__(256) void k_dec_index(const __bf16* __restrict__ q_
 }
 
 // ---------------------------------------------------------------------------
-// Selection per (sequence, index head) row, one wave each: the same steps as the
-// forward's selection kernel on a row of any length. The lane maxima of the
-// 32-bit score keys give T, the (top_k-1)-th largest; every key of the exact
-// selection is >= T; candidates >= T go to an LDS list of 64-bit (score, block)
-// keys (sized for the whole row, so any tie pattern fits) and are ranked exactly.
+// Selection per (sequence, index head) row, one workgroup of four waves each:
+// the forward selection kernel's steps on a row of any length, spread over 256
+// threads. Thread i takes blocks i, i + 256, ... (so wave w holds the blocks
+// with (c / 64) % 4 == w).
+//   1. each thread takes the max of its 32-bit score keys;
+//   2. each wave finds T_w, the (top_k-1)-th largest of its 64 thread maxima,
+//      bit by bit (0 when fewer lanes hold a block). At least top_k-1 keys of the
+//      row are >= T_w, so T = max_w T_w is at most the row's (top_k-1)-th
+//      largest key and every key of the exact selection is >= T;
+//   3. each wave puts its keys >= T, as 64-bit (score, block) keys, in its own
+//      LDS segment in ascending block order (sized for all its blocks, so any
+//      tie pattern fits);
+//   4. each candidate is ranked by counting larger candidates in all segments;
+//      ranks below top_k-1 are the selection (the keys are unique);
+//   5. the chosen blocks are written in ascending order, the local block last.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k_dec_topk(const float* __restrict__ pooled, const int32_t* __restrict__ seqlens,
-                                                 int32_t* __restrict__ block_idx, int C, int H, int nblk, int top_k) {
-    extern __shared__ __attribute__((aligned(16))) uint64_t dec_list[];  // nblk + 4 keys
+constexpr int kDecTopkWaves = 4;
+constexpr int kDecTopkThreads = 64 * kDecTopkWaves;
+
+__device__ __forceinline__ int dec_topk_segment(int nblk) {
+    return (nblk + kDecTopkThreads - 1) / kDecTopkThreads * 64;  // blocks one wave can hold
+}
+
+__global__ __launch_bounds__(kDecTopkThreads) void k_dec_topk(const float* __restrict__ pooled,
+                                                              const int32_t* __restrict__ seqlens,
+                                                              int32_t* __restrict__ block_idx, int C, int H, int nblk,
+                                                              int top_k) {
+    extern __shared__ __attribute__((aligned(16))) uint64_t dec_list[];  // kDecTopkWaves segments
+    __shared__ uint32_t wave_t[kDecTopkWaves];
+    __shared__ int wave_n[kDecTopkWaves];
+    __shared__ int32_t chosen[64];  // by rank; top_k <= 65
     const int row = blockIdx.x, b = row / H;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int L = dec_len(seqlens, b, C);
     int32_t* dst = block_idx + (size_t)row * top_k;
+    // the early exits depend on the row alone, so the whole workgroup takes them
     if (L <= 0) {
-        for (int s = lane; s < top_k; s += 64) dst[s] = -1;
+        for (int s = tid; s < top_k; s += kDecTopkThreads) dst[s] = -1;
         return;
     }
     const int cl = (L - 1) / kBlock;
     if (cl + 1 <= top_k) {  // every visible block
-        for (int s = lane; s < top_k; s += 64) dst[s] = s <= cl ? s : -1;
+        for (int s = tid; s < top_k; s += kDecTopkThreads) dst[s] = s <= cl ? s : -1;
         return;
     }
     const int need = top_k - 1;
     if (need == 0) {
-        if (lane == 0) dst[0] = cl;
+        if (tid == 0) dst[0] = cl;
         return;
     }
     const float* src = pooled + (size_t)row * nblk;
-    uint32_t lmax = 0u;
-    for (int c = lane; c < cl; c += 64) {
+
+    // 1, 2. thread maxima, then each wave's bound
+    uint32_t tmax = 0u;  // below every real key
+    for (int c = tid; c < cl; c += kDecTopkThreads) {
         const uint32_t k = order_key(src[c]);
-        lmax = k > lmax ? k : lmax;
+        tmax = k > tmax ? k : tmax;
     }
-    // need <= 64 and cl >= need + 1, so at least `need` lanes hold a block
     uint32_t T = 0u;
 #pragma unroll
     for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand_t = T | (1u << bit);
-        if (__popcll(__ballot(lmax >= cand_t)) >= need) T = cand_t;
+        if (__popcll(__ballot(tmax >= cand_t)) >= need) T = cand_t;
     }
-    uint64_t* list = dec_list;
+    if (lane == 0) wave_t[wave] = T;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kDecTopkWaves; ++w) T = wave_t[w] > T ? wave_t[w] : T;
+
+    // 3. this wave's candidates, ascending block order
+    const int seg = dec_topk_segment(nblk);
+    uint64_t* list = dec_list + (size_t)wave * seg;
+    const uint64_t lt = (1ull << lane) - 1ull;
     int n = 0;
-    for (int c0 = 0; c0 < cl; c0 += 64) {
+    for (int c0 = 64 * wave; c0 < cl; c0 += kDecTopkThreads) {
         const int c = c0 + lane;
         const uint32_t k = c < cl ? order_key(src[c]) : 0u;
         const bool take = c < cl && k >= T;
         const uint64_t mask = __ballot(take);
-        if (take)
-            list[n + __popcll(mask & ((1ull << lane) - 1ull))] =
-                ((uint64_t)k << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)c);
+        if (take) list[n + __popcll(mask & lt)] = ((uint64_t)k << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)c);
         n += __popcll(mask);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    rank_and_emit(list, n, need, cl, dst, lane);
+    if (lane == 0) wave_n[wave] = n;
+    __syncthreads();
+
+    // 4. rank every candidate against all of them
+    for (int w = 0; w < kDecTopkWaves; ++w) {
+        const int nw = wave_n[w];
+        for (int i = tid; i < nw; i += kDecTopkThreads) {
+            const uint64_t mine = dec_list[(size_t)w * seg + i];
+            int r = 0;
+            for (int w2 = 0; w2 < kDecTopkWaves; ++w2) {
+                const uint64_t* l2 = dec_list + (size_t)w2 * seg;
+                const int n2 = wave_n[w2];
+                for (int j = 0; j < n2; ++j) r += l2[j] > mine ? 1 : 0;
+            }
+            if (r < need) chosen[r] = key_block(mine);
+        }
+    }
+    __syncthreads();
+
+    // 5. ascending output: a chosen block's place is the number of smaller chosen blocks
+    if (tid < need) {
+        const int blk = chosen[tid];
+        int slot = 0;
+        for (int j = 0; j < need; ++j) slot += chosen[j] < blk ? 1 : 0;
+        dst[slot] = blk;
+    }
+    if (tid == 0) dst[need] = cl;
 }
 
 // ---------------------------------------------------------------------------
 // Attention over the selected blocks. A workgroup owns (sequence b, KV head g,
-// a tile of up to 16 of the group's query heads); wave w takes keys
-// 32w .. 32w+31 of every selected block and keeps an online softmax over them.
+// a tile of up to 16 of the group's query heads). Its NW waves form NW / 4 slot
+// groups: wave w takes keys 32(w % 4) .. +31 of the selected blocks in slots
+// w / 4, w / 4 + NW / 4, ... and keeps an online softmax over them (NW = 4 when
+// the grid fills the chip, 16 when there are fewer groups than CUs).
 //   S^T = K Q^T: K rows are the A operand, read from memory (rows past t clamped
 //   to t and masked), Q the B operand; lane l holds keys 16mt + 4(l/16) + i of
 //   head l % 16.
@@ -168,14 +223,15 @@ __global__ __launch_bounds__(64) void k_dec_topk(const float* __restrict__ poole
 //   16(e/4) + 4(l/16) + e%4); the V rows of the same keys come from the wave's
 //   LDS tile (filled by global->LDS loads) through ds_read_b64_tr_b16, which
 //   hands each lane one dim of 4 consecutive keys.
-// The four waves' (m, l, O) are merged in LDS at the end.
+// The waves' (m, l, O) are merged in LDS at the end.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bf16x4 dec_tr_rows4(const __bf16* tile, int r0, int c0, int li) {
     const int row = r0 + (li >> 2), col = c0 + 4 * (li & 3);
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(tile + row * kDim + col));
 }
 
-__global__ __launch_bounds__(256) void k_dec_attn(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void k_dec_attn(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                   const __bf16* __restrict__ v, const int32_t* __restrict__ seqlens,
                                                   const int32_t* __restrict__ block_idx, __bf16* __restrict__ o,
                                                   float* __restrict__ lse, int C, int Hq, int Hkv, int G, int top_k,
@@ -188,8 +244,8 @@ __global__ __launch_bounds__(256) void k_dec_attn(const __bf16* __restrict__ q, 
     const int h0 = g * G + ht * 16;
     const int hn = min(16, G - ht * 16);
 
-    __shared__ __attribute__((aligned(16))) __bf16 vs[kDecAttnWaves][32 * kDim];  // 8 KB of V rows per wave
-    __shared__ float sm[kDecAttnWaves][16], sl[kDecAttnWaves][16];
+    __shared__ __attribute__((aligned(16))) __bf16 vs[NW][32 * kDim];  // 8 KB of V rows per wave
+    __shared__ float sm[NW][16], sl[NW][16];
     __bf16* vw = vs[wave];
 
     bf16x8 qf[4];
@@ -211,10 +267,11 @@ __global__ __launch_bounds__(256) void k_dec_attn(const __bf16* __restrict__ q, 
     const size_t kv_row = (size_t)Hkv * kDim;  // elements between consecutive cache rows
     const __bf16* kseq = k + ((size_t)b * C * Hkv + g) * kDim;
     const __bf16* vseq = v + ((size_t)b * C * Hkv + g) * kDim;
-    for (int s = 0; s < top_k; ++s) {
+    // wave w takes slice w % 4 of the slots w / 4, w / 4 + NW / 4, ...
+    for (int s = wave / kDecAttnSlices; s < top_k; s += NW / kDecAttnSlices) {
         const int c = sel[s];
         if (c < 0 || c > cl) continue;  // padding or not visible
-        const int kbase = c * kBlock + 32 * wave;
+        const int kbase = c * kBlock + 32 * (wave % kDecAttnSlices);
         const int rmax = t - kbase;  // last valid key of this wave's 32
         if (rmax < 0) continue;      // the whole slice lies after t
         // V rows kbase .. kbase+31 (clamped to t) into LDS, row-major: instruction i
@@ -285,9 +342,9 @@ __global__ __launch_bounds__(256) void k_dec_attn(const __bf16* __restrict__ q, 
         }
     }
 
-    // merge the four waves: weights 2^(m_w - M) per head, O and l summed
+    // merge the waves: weights 2^(m_w - M) per head, O and l summed
     __syncthreads();  // every wave is done with its V tile; the tiles become the merge buffer
-    float* red = (float*)&vs[0][0];  // [wave][16 heads][128 dims] fp32, 32 KB
+    float* red = (float*)&vs[0][0];  // [wave][16 heads][128 dims] fp32, 8 KB per wave
     if (q4 == 0) {
         sm[wave][n] = m_run;
         sl[wave][n] = l_run;
@@ -298,7 +355,7 @@ __global__ __launch_bounds__(256) void k_dec_attn(const __bf16* __restrict__ q, 
         const int h = 4 * q4 + i;
         float M = sm[0][h];
 #pragma unroll
-        for (int w = 1; w < kDecAttnWaves; ++w) M = fmaxf(M, sm[w][h]);
+        for (int w = 1; w < NW; ++w) M = fmaxf(M, sm[w][h]);
         const float mw = sm[wave][h];
         const float wt = mw == -INFINITY ? 0.0f : exp2f(mw - M);
 #pragma unroll
@@ -309,17 +366,17 @@ __global__ __launch_bounds__(256) void k_dec_attn(const __bf16* __restrict__ q, 
     if (h >= hn) return;
     float M = sm[0][h];
 #pragma unroll
-    for (int w = 1; w < kDecAttnWaves; ++w) M = fmaxf(M, sm[w][h]);
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm[w][h]);
     float Lsum = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kDecAttnWaves; ++w) Lsum += sm[w][h] == -INFINITY ? 0.0f : exp2f(sm[w][h] - M) * sl[w][h];
+    for (int w = 0; w < NW; ++w) Lsum += sm[w][h] == -INFINITY ? 0.0f : exp2f(sm[w][h] - M) * sl[w][h];
     const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
     bf16x8 out;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         float acc = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kDecAttnWaves; ++w) acc += red[(w * 16 + h) * kDim + d0 + e];
+        for (int w = 0; w < NW; ++w) acc += red[(w * 16 + h) * kDim + d0 + e];
         out[e] = (__bf16)(acc * inv);
     }
     *(bf16x8*)(o + ((size_t)b * Hq + h0 + h) * kDim + d0) = out;
@@ -328,7 +385,9 @@ __global__ __launch_bounds__(256) void k_dec_attn(const __bf16* __restrict__ q, 
 }
 
 // ---------------------------------------------------------------------------
-size_t dec_topk_lds_bytes(const Dims& d) { return ((size_t)d.nblk + 4) * 8; }
+size_t dec_topk_lds_bytes(const Dims& d) {
+    return (size_t)kDecTopkWaves * ((d.nblk + kDecTopkThreads - 1) / kDecTopkThreads * 64) * 8;
+}
 
 hipError_t launch_dec_index(const void* q_idx, const void* k_idx, const int32_t* seqlens, float* pooled, const Dims& d,
                             hipStream_t stream) {
@@ -346,7 +405,7 @@ hipError_t launch_dec_topk(const float* pooled, const int32_t* seqlens, int32_t*
                                                  (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_dec_topk, dim3((unsigned)(d.B * d.Hkv)), dim3(64), lds, stream, pooled, seqlens, block_idx,
+    hipLaunchKernelGGL(k_dec_topk, dim3((unsigned)(d.B * d.Hkv)), dim3(kDecTopkThreads), lds, stream, pooled, seqlens, block_idx,
                        d.N, d.Hkv, d.nblk, d.top_k);
     return hipGetLastError();
 }
@@ -354,9 +413,18 @@ hipError_t launch_dec_topk(const float* pooled, const int32_t* seqlens, int32_t*
 hipError_t launch_dec_attn(const void* q, const void* k, const void* v, const int32_t* seqlens,
                            const int32_t* block_idx, void* o, float* lse, const Dims& d, hipStream_t stream) {
     dim3 grid((unsigned)((d.G + 15) / 16), (unsigned)d.Hkv, (unsigned)d.B);
-    hipLaunchKernelGGL(k_dec_attn, grid, dim3(64 * kDecAttnWaves), 0, stream, (const __bf16*)q, (const __bf16*)k,
-                       (const __bf16*)v, seqlens, block_idx, (__bf16*)o, lse, d.N, d.Hq, d.Hkv, d.G, d.top_k,
-                       d.scale * 1.4426950408889634f);
+    const float sl2 = d.scale * 1.4426950408889634f;
+    // Few (sequence, KV head, head tile) groups would leave most CUs idle: then four slot
+    // groups of four waves share a group's selected blocks (16 waves, 130 KB of LDS).
+    if ((long long)grid.x * grid.y * grid.z < device_cu_count()) {
+        hipLaunchKernelGGL(k_dec_attn<4 * kDecAttnSlices>, grid, dim3(64 * 4 * kDecAttnSlices), 0, stream,
+                           (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, seqlens, block_idx, (__bf16*)o, lse,
+                           d.N, d.Hq, d.Hkv, d.G, d.top_k, sl2);
+    } else {
+        hipLaunchKernelGGL(k_dec_attn<kDecAttnSlices>, grid, dim3(64 * kDecAttnSlices), 0, stream, (const __bf16*)q,
+                           (const __bf16*)k, (const __bf16*)v, seqlens, block_idx, (__bf16*)o, lse, d.N, d.Hq, d.Hkv,
+                           d.G, d.top_k, sl2);
+    }
     return hipGetLastError();
 }
 
