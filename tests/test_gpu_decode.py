@@ -127,6 +127,47 @@ def test_decode_lengths_past_capacity_read_as_capacity(msa):
     assert (c[0] == -1).all() and (c[1] == 0).all() and torch.isneginf(c[2]).all()
 
 
+def test_decode_ties_take_lower_blocks(msa):
+    # closed form: with zero index queries every pooled score is exactly 0, so each row keeps
+    # blocks 0 .. top_k-2 and its own block; rows of 1024 and 8192 blocks run the four-wave
+    # selection with every block a candidate. A copy of block 2's index keys in block 5 ties
+    # the two exactly; the lower block must win.
+    for C, lengths in ((131072, [131072, 70001, 2000]), (1 << 20, [1 << 20, 600000])):
+        w = small_decode_workload(C, 8, 2, 16, seed=77, batch=len(lengths))
+        x = make_decode_inputs(w, lengths=lengths)
+        x["q_idx"] = torch.zeros_like(x["q_idx"])
+        xg = _gpu(x)
+        _say(w.name, f"decode all-tied selection, rows of {C // 128} blocks")
+        bi, _, _ = msa.decode(xg["q_idx"], xg["k_idx"], xg["q"], xg["k"], xg["v"], xg["seqlens"], 16,
+                              w.softmax_scale)
+        torch.cuda.synchronize()
+        got = to_np(bi)
+        for b, L in enumerate(lengths):
+            cl = (L - 1) // 128
+            want = list(range(15)) + [cl]
+            assert (got[b] == np.array(want)[None, :]).all(), (C, b, got[b])
+    # an exact tie at the selection boundary: blocks 7 and 9 (keys x8) lead, blocks 2 and 5
+    # (the same keys x4, an exact copy) tie for the last of the top_k - 1 = 3 places, and the
+    # lower block must win; scaling by a power of two is exact in bf16
+    w = small_decode_workload(131072, 8, 2, 4, seed=78, batch=1)
+    x = make_decode_inputs(w, lengths=[131072])
+    ki = x["k_idx"][0]
+    for c, f in ((7, 8.0), (9, 8.0), (2, 4.0)):
+        ki[c * 128:(c + 1) * 128] = ki[c * 128:(c + 1) * 128] * f
+    ki[5 * 128:6 * 128] = ki[2 * 128:3 * 128]
+    xg = _gpu(x)
+    _say(w.name, "decode tie at the selection boundary")
+    pooled = msa.decode_index_scores(xg["q_idx"], xg["k_idx"], xg["seqlens"])
+    bi = msa.decode_topk(pooled, xg["seqlens"], 4, 131072)
+    torch.cuda.synchronize()
+    gp, gi = to_np(pooled), to_np(bi)
+    for h in range(w.h_kv):
+        assert gp[0, h, 5] == gp[0, h, 2]  # identical inputs, identical sums
+        order = sorted(range(1023), key=lambda c: (-float(gp[0, h, c]), c))
+        assert order[:4] in ([7, 9, 2, 5], [9, 7, 2, 5]), (h, order[:6])  # the case is exercised
+        assert list(gi[0, h]) == [2, 7, 9, 1023], (h, gi[0, h])
+
+
 def test_decode_attn_invalid_and_repeated_entries(msa):
     w = small_decode_workload(2048, 16, 2, 6, seed=6, batch=3)
     lengths = [2000, 300, 1025]
