@@ -127,9 +127,13 @@ __global__ __launch_bounds__(256) void k_block_topk_reg(
     // the query position row % N is stepped along with the row: no division per row
     const int dt = (int)(stride % N);
     int t = (int)(row0 % N);
-    for (long long row = row0; row < rows; row += stride, t = t + dt >= N ? t + dt - N : t + dt) {
+    // row offsets advance by fixed steps: no 64-bit multiply per row
+    long long src_off = row0 * nblk, dst_off = row0 * top_k;
+    const long long src_step = stride * nblk, dst_step = stride * top_k;
+    for (long long row = row0; row < rows;
+         row += stride, t = t + dt >= N ? t + dt - N : t + dt, src_off += src_step, dst_off += dst_step) {
         const int cl = t >> 7;
-        int32_t* dst = block_idx + row * top_k;
+        int32_t* dst = block_idx + dst_off;
         if (cl + 1 <= top_k) {  // every visible block
             for (int s = lane; s < top_k; s += 64) dst[s] = s <= cl ? s : -1;
             continue;
@@ -138,7 +142,7 @@ __global__ __launch_bounds__(256) void k_block_topk_reg(
             if (lane == 0) dst[0] = cl;
             continue;
         }
-        topk_row_quads(pooled + row * nblk, cl, need, list, dst, lane);
+        topk_row_quads(pooled + src_off, cl, need, list, dst, lane);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
