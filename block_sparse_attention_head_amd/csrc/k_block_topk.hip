@@ -127,13 +127,15 @@ __global__ __launch_bounds__(256) void k_block_topk_reg(
     // the query position row % N is stepped along with the row: no division per row
     const int dt = (int)(stride % N);
     int t = (int)(row0 % N);
-    // row offsets advance by fixed steps: no 64-bit multiply per row
-    long long src_off = row0 * nblk, dst_off = row0 * top_k;
+    // row pointers advance by a fixed stride: no 64-bit multiply per row (after the last
+    // row they point past the arrays and are not used). Advancing integer offsets instead
+    // measured 20% slower (0.396 against 0.327 ms at 128K), from the code layout alone.
+    const float* src = pooled + row0 * nblk;
+    int32_t* dst = block_idx + row0 * top_k;
     const long long src_step = stride * nblk, dst_step = stride * top_k;
     for (long long row = row0; row < rows;
-         row += stride, t = t + dt >= N ? t + dt - N : t + dt, src_off += src_step, dst_off += dst_step) {
+         row += stride, t = t + dt >= N ? t + dt - N : t + dt, src += src_step, dst += dst_step) {
         const int cl = t >> 7;
-        int32_t* dst = block_idx + dst_off;
         if (cl + 1 <= top_k) {  // every visible block
             for (int s = lane; s < top_k; s += 64) dst[s] = s <= cl ? s : -1;
             continue;
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(256) void k_block_topk_reg(
             if (lane == 0) dst[0] = cl;
             continue;
         }
-        topk_row_quads(pooled + src_off, cl, need, list, dst, lane);
+        topk_row_quads(src, cl, need, list, dst, lane);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
