@@ -361,6 +361,31 @@ def test_near_tie_classification():
     assert O.near_tie_rows(pooled, ref, ref, 4, positions=pos) == (0, 0, [])
 
 
+def test_near_tie_rejects_a_wrong_exact_tie_break():
+    # block 2 and block 3 score exactly 3.0; the lower block must win, so picking
+    # block 3 is a wrong tie-break, not a near-tie
+    pooled = np.array([[[[5.0, 4.0, 3.0, 3.0, 1.0, 9.0]]]])
+    pos = [5 * 128]
+    ref = O.block_topk(pooled, 4, positions=pos)
+    assert list(ref[0, 0, 0]) == [0, 1, 2, 5]
+    wrong = np.array([[[[0, 1, 3, 5]]]], dtype=np.int32)
+    assert O.near_tie_rows(pooled, wrong, ref, 4, positions=pos) == (1, 0, [(0, 0, 0)])
+    # with a third block just below the tied pair: trading a tied block for it is a
+    # near-tie, trading one tied block for the other is not
+    pooled = np.array([[[[5.0, 4.0, 3.0, 3.0, 2.999, 9.0]]]])
+    ref = O.block_topk(pooled, 4, positions=pos)
+    assert list(ref[0, 0, 0]) == [0, 1, 2, 5]
+    below = np.array([[[[0, 1, 4, 5]]]], dtype=np.int32)
+    assert O.near_tie_rows(pooled, below, ref, 4, positions=pos)[:2] == (1, 1)
+    assert O.near_tie_rows(pooled, wrong, ref, 4, positions=pos)[:2] == (1, 0)
+    # -0.0 and +0.0 are equal scores: a higher block over a lower one is no near-tie
+    pooled = np.array([[[[1.0, -0.0, 0.0, -2.0, 9.0]]]])
+    pos = [4 * 128]
+    ref = O.block_topk(pooled, 3, positions=pos)
+    assert list(ref[0, 0, 0]) == [0, 1, 4]
+    assert O.near_tie_rows(pooled, np.array([[[[0, 2, 4]]]], dtype=np.int32), ref, 3, positions=pos)[:2] == (1, 0)
+
+
 def test_empty_selection_gives_zero_output_and_minus_inf_lse():
     # R9: an empty sum of exp is 0, so LSE = log 0 = -inf; O is taken as 0.
     rng = np.random.default_rng(13)
