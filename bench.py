@@ -70,30 +70,61 @@ def _traffic(kernel: str, workload: str, src: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, x, budget_s: float, seed: int = 7):
-    """The CPU oracle, as it stands, on a bounded uniform sample of query positions."""
+def host_cpu():
+    """The host's CPU model and core counts, for the CPU-baseline record."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = None
+    return {"cpu_model": model, "host_cpus_affinity": len(os.sched_getaffinity(0)),
+            "host_cpus_total": os.cpu_count(), "blas_threads": blas}
+
+
+SAMPLE_SEED = 7
+PARITY_MAX_POSITIONS = 8192  # GPU rows kept for the parity check; the CPU leg samples fewer
+
+
+def sample_order(n: int, seed: int = SAMPLE_SEED):
+    import numpy as np
+
+    return np.random.default_rng(seed).permutation(n)
+
+
+def cpu_baseline(w, x, budget_s: float, seed: int = SAMPLE_SEED, max_positions: int = PARITY_MAX_POSITIONS):
+    """The CPU oracle, as it stands, on a bounded uniform sample of query positions
+    (until budget_s seconds of oracle time or max_positions positions).
+    Returns the report and the oracle's outputs at the sampled positions."""
     import numpy as np
 
     from oracle import msa_oracle as O
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+    host = host_cpu()
     x64 = {k: v.double().numpy() for k, v in x.items() if k in ("q", "k", "v", "q_idx", "k_idx")}
-    order = np.random.default_rng(seed).permutation(w.seqlen)
+    order = sample_order(w.seqlen, seed)
     done, t_total, chunk = 0, 0.0, 16
-    while done < w.seqlen and t_total < budget_s:
-        pos = np.sort(order[done:done + chunk])
+    outs = []
+    while done < min(w.seqlen, max_positions) and t_total < budget_s:
+        pos = np.sort(order[done:min(done + chunk, max_positions)])
         t0 = time.perf_counter()
-        O.msa_forward(x64["q_idx"], x64["k_idx"], x64["q"], x64["k"], x64["v"], w.top_k, w.softmax_scale,
-                      positions=pos)
+        r = O.msa_forward(x64["q_idx"], x64["k_idx"], x64["q"], x64["k"], x64["v"], w.top_k, w.softmax_scale,
+                          positions=pos)
         t_total += time.perf_counter() - t0
+        outs.append((pos, r))
         done += len(pos)
     del x64
-    return {
+    cores = host["blas_threads"] or host["host_cpus_affinity"]
+    report = {
         "value": w.batch * done / t_total,
         "unit": "tokens/s",
         "cores": cores,
@@ -102,7 +133,41 @@ def cpu_baseline(w, x, budget_s: float, seed: int = 7):
                    f"(batch {w.batch}, all {w.h_idx} index heads and {w.h_q} query heads), full forward per "
                    f"position (index scores over all visible keys, top-k, sparse attention); "
                    f"{t_total:.1f} s of float64 NumPy on the host; tokens/s = positions x batch / seconds"),
+        **host,
     }
+    return report, outs
+
+
+def parity_report(w, outs, gpu_rows):
+    """The GPU's block_idx, O and LSE at the CPU leg's sampled positions against the oracle's.
+    Index rows are compared exactly; rows that differ must be near-ties (pairwise rule of
+    the oracle's near_tie_rows). O and LSE are compared on positions whose selections agree."""
+    import numpy as np
+
+    from oracle import msa_oracle as O
+
+    where = {int(p): i for i, p in enumerate(gpu_rows["positions"])}
+    n_pos = n_mis = n_tie = n_bad = 0
+    max_o = max_l = 0.0
+    for pos, (bi_r, o_r, lse_r, pooled_r) in outs:
+        rows = np.array([where[int(p)] for p in pos])
+        bi_g = gpu_rows["block_idx"][:, :, rows]
+        mis, tie, bad = O.near_tie_rows(pooled_r, bi_g, bi_r, w.top_k, positions=pos)
+        n_pos += len(pos)
+        n_mis += mis
+        n_tie += tie
+        n_bad += len(bad)
+        same = np.all(bi_g == bi_r, axis=(0, 1, 3))          # positions whose every index row agrees
+        if same.any():
+            o_g = gpu_rows["o"][:, rows][:, same]
+            l_g = gpu_rows["lse"][:, :, rows][:, :, same]
+            max_o = max(max_o, float(np.abs(o_g - o_r[:, same]).max()))
+            max_l = max(max_l, float(np.abs(l_g - lse_r[:, :, same]).max()))
+    return {"positions": n_pos, "index_rows": n_pos * w.batch * w.h_idx, "index_mismatch": n_mis,
+            "near_ties": n_tie, "not_near_ties": n_bad, "max_abs_O": max_o, "max_abs_LSE": max_l,
+            "tolerance": {"O": 2e-2, "LSE": 1e-3},
+            "what": ("GPU msa_fwd outputs of the timed steps at the CPU baseline's sampled positions against "
+                     "the float64 oracle: index rows bit-exact except counted near-ties; O and LSE max-abs error")}
 
 
 def backward_report(w, steps: int, warmup: int):
@@ -463,7 +528,16 @@ def main(argv=None) -> int:
     t_end.record()
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / a.steps
+    per_step = sorted(e[0].elapsed_time(e[-1]) for e in evs)
+    ms_median = per_step[len(per_step) // 2] if len(per_step) % 2 else \
+        0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
     stage_ms = {s: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / a.steps for j, s in enumerate(stages)}
+    # the last timed step's outputs at the positions the CPU baseline will sample (a superset)
+    gpu_rows = None
+    if not a.no_cpu_baseline:
+        sp = torch.from_numpy(sample_order(N)[:PARITY_MAX_POSITIONS].copy()).to(dev)
+        gpu_rows = {"positions": sp.cpu().numpy(), "block_idx": block_idx[:, :, sp].cpu().numpy(),
+                    "o": o[:, sp].float().cpu().numpy(), "lse": lse[:, :, sp].cpu().numpy()}
     two_kernel = two_kernel_selection(msa, xg, w, block_idx, a.steps, a.warmup)
 
     if a.copy_calibration:
@@ -512,6 +586,7 @@ def main(argv=None) -> int:
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(ms_median, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -555,7 +630,8 @@ def main(argv=None) -> int:
             out["long_training"] = {"error": f"{type(exc).__name__}: {exc}"}
     if not a.no_cpu_baseline:
         print(f"[bench] CPU oracle baseline (~{a.cpu_budget:.0f} s)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, x, a.cpu_budget)
+        out["cpu_baseline"], outs = cpu_baseline(w, x, a.cpu_budget)
+        out["parity"] = parity_report(w, outs, gpu_rows)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -222,6 +222,95 @@ def test_full_size_sampled_rows(msa, name):
     assert np.all(np.isfinite(to_np(lse)))
 
 
+@pytest.mark.timeout(900)
+def test_full_rows_n32k_b2(msa):
+    """Every index row of the 32K two-batch workload (2 x 8 heads x 32768 positions): bit-exact
+    against the oracle's selection on the GPU's own pooled scores; against the oracle's float64
+    scores only near-ties may differ, and they are counted and printed. O and LSE on 640 positions."""
+    w = WORKLOADS["n32k_b2"]
+    _say(w.name, "generating inputs")
+    x = make_inputs(w)
+    xg = _gpu(x)
+    _say(w.name, "msa_fwd + index scores")
+    bi, o, lse = msa.msa_fwd(xg["q_idx"], xg["k_idx"], xg["q"], xg["k"], xg["v"], w.top_k, w.softmax_scale)
+    pooled = msa.index_scores(xg["q_idx"], xg["k_idx"], visible_only=True)
+    torch.cuda.synchronize()
+    gi = to_np(bi)
+    gp = pooled.cpu().numpy()
+    del pooled
+    torch.cuda.empty_cache()
+    _say(w.name, "oracle selection on the GPU's pooled scores, every row")
+    same = O.block_topk(gp.astype(np.float64), w.top_k)   # reads only the visible part
+    bad = np.argwhere(np.any(same != gi, axis=-1))
+    assert bad.size == 0, f"selection differs from the oracle on identical scores at rows {bad[:5].tolist()}"
+    del same
+    q64, k64 = x["q_idx"].double().numpy(), x["k_idx"].double().numpy()
+    n_mis = n_tie = 0
+    step = 4096
+    for b in range(w.batch):
+        for p0 in range(0, w.seqlen, step):
+            pos = np.arange(p0, p0 + step)
+            ref_pooled = O.index_scores(q64[b:b + 1], k64[b:b + 1], positions=pos)
+            ref_idx = O.block_topk(ref_pooled, w.top_k, positions=pos)
+            m, t, not_tie = O.near_tie_rows(ref_pooled, gi[b:b + 1, :, p0:p0 + step], ref_idx, w.top_k,
+                                            positions=pos)
+            assert not not_tie, f"batch {b}: {len(not_tie)} rows differ beyond near-ties, e.g. {not_tie[:5]}"
+            n_mis += m
+            n_tie += t
+            _say(w.name, f"batch {b} positions {p0}..{p0 + step - 1}: float64 rows differing {m} (near-ties {t})")
+    rows = w.batch * w.h_idx * w.seqlen
+    _say(w.name, f"index rows differing from the float64 oracle: {n_mis} of {rows} (all near-ties: {n_tie})")
+    pos = sample_positions(w.seqlen, 628, seed=w.seed + 1)
+    assert len(pos) >= 512
+    _say(w.name, f"attention oracle on {len(pos)} positions")
+    ro, rl = O.sparse_attention(x["q"], x["k"], x["v"], gi[:, :, pos], w.softmax_scale, positions=pos)
+    do, dl = check_attn(to_np(o[:, pos]), to_np(lse[:, :, pos]), ro, rl, w.name)
+    _say(w.name, f"max|dO|={do:.2e} max|dLSE|={dl:.2e}")
+
+
+def test_fused_index_topk_exact_integer_scores_long_rows(msa):
+    """Index queries and keys drawn from {-1, 0, 1}: every dot product is a small integer, exact
+    in fp32 and float64 alike, so the GPU's pooled scores equal the oracle's and the selection
+    must match bit for bit, with no near-tie allowance, on rows of up to 8192 blocks where exact
+    ties between blocks are everywhere (equal scores must go to the lower block)."""
+    N, H, K = 1 << 20, 4, 16
+    gen = torch.Generator(device=DEV).manual_seed(91)
+    _say("integer index scores 2^20", "drawing")
+    qi = torch.randint(-1, 2, (1, N, H, 128), generator=gen, device=DEV).to(torch.bfloat16)
+    ki = torch.randint(-1, 2, (1, N, 128), generator=gen, device=DEV).to(torch.bfloat16)
+    _say("integer index scores 2^20", "fused index top-k")
+    bi = msa.index_topk(qi, ki, K)
+    torch.cuda.synchronize()
+    pos = sample_positions(N, 28, seed=91)
+    pos_t = torch.from_numpy(pos).to(DEV)
+    got = to_np(bi[:, :, pos_t])
+    bic = to_np(bi).astype(np.int64)
+    q_h, k_h = qi.cpu(), ki.cpu()
+    del bi, qi, ki
+    torch.cuda.empty_cache()
+    _say("integer index scores 2^20", f"oracle on {len(pos)} positions")
+    ref_pooled = O.index_scores(q_h, k_h, positions=pos)
+    assert np.all(ref_pooled[np.isfinite(ref_pooled)] == np.round(ref_pooled[np.isfinite(ref_pooled)]))
+    ref = O.block_topk(ref_pooled, K, positions=pos)
+    # the case is exercised: many rows have a tie across the selection boundary
+    cl = pos // 128
+    ties = 0
+    for i, t in enumerate(pos):
+        if cl[i] >= K:
+            for h in range(H):
+                row = ref_pooled[0, h, i, :cl[i]]
+                chosen = row[ref[0, h, i, :K - 1]]
+                ties += int(np.sum(row == chosen.min()) > np.sum(chosen == chosen.min()))
+    _say("integer index scores 2^20", f"rows with an exact tie across the boundary: {ties}")
+    assert ties >= 20
+    np.testing.assert_array_equal(got, ref)
+    valid = bic >= 0
+    c_all = np.arange(N) // 128
+    assert np.all(valid.sum(-1) == np.minimum(K, c_all + 1)[None, None])
+    assert np.all(np.take_along_axis(bic, (valid.sum(-1, keepdims=True) - 1), -1)[..., 0] == c_all[None, None])
+    assert np.all(np.where(valid[..., 1:], np.diff(bic, axis=-1) > 0, True))
+
+
 def test_long_context_sampled_rows(msa):
     # 2^20 tokens with the 128K workload's heads, as the benchmark's long-context line runs it:
     # the one-pass selection over rows of up to 8192 blocks and the sparse attention in query
