@@ -40,7 +40,8 @@ __global__ __launch_bounds__(256) void k_fill_i32(int32_t* __restrict__ p, int32
 __device__ __forceinline__ bool valid_entry(int c, int t) { return c >= 0 && c <= (t >> 7); }
 
 int rev_positions_per_group(int N) {
-    const int units = (N + 1023) / 1024;  // 1024 positions per range, or more so that ranges <= 256
+    // 1024 positions per range, or more so that ranges <= 256 (at least one range)
+    const int units = N > 0 ? (N + 1023) / 1024 : 1;
     return 1024 * ((units + kRevMaxGroups - 1) / kRevMaxGroups);
 }
 int rev_groups(int N) { return (N + rev_positions_per_group(N) - 1) / rev_positions_per_group(N); }

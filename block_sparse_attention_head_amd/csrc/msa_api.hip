@@ -153,9 +153,12 @@ int fwd_chunk(const Dims& d, size_t bytes) {
 // most this much, else the chunk that fits it (the per-slot partials grow with N).
 constexpr size_t kFwdWsBudget = (size_t)64 << 30;
 
+// The chunk the library asks a workspace for: the largest that fits `bytes`, and never
+// fewer than 128 positions (the smallest chunk the forward runs, whatever its size).
 Dims fwd_chunk_dims(const Dims& d, size_t bytes) {
     Dims c = d;
-    c.Nc = fwd_chunk(d, bytes);
+    const int fit = fwd_chunk(d, bytes);
+    c.Nc = fit > 0 ? fit : kBlock;
     return c;
 }
 

@@ -6,8 +6,10 @@
  * allocates, frees or synchronises: all work is enqueued on `stream` and runs
  * asynchronously. Arguments are validated on the host before anything is
  * enqueued; on any error nothing is enqueued and no output is touched.
- * No C++ exception crosses this boundary. The library keeps no mutable global
- * state; calls from several host threads on different streams are safe.
+ * No C++ exception crosses this boundary. The only global state is a
+ * per-device cache of the compute-unit count (filled on first use; every
+ * thread writes the same value), so calls from several host threads on
+ * different streams are safe.
  *
  * The method (cited from the web pages that describe it, by title and section):
  *   [MSA summary] "MiniMax Sparse Attention (MSA): Turning Theoretical Sparse
@@ -52,7 +54,16 @@
 extern "C" {
 #endif
 
-typedef enum msa_status {
+/* In C++ the enums get a fixed 32-bit underlying type, so any int a C caller
+ * passes is a valid value (the checks below then reject it); C's enums are
+ * int-sized, so the layout is the same in both languages. */
+#ifdef __cplusplus
+#define MSA_ENUM_INT32 : int32_t
+#else
+#define MSA_ENUM_INT32
+#endif
+
+typedef enum msa_status MSA_ENUM_INT32 {
     MSA_OK = 0,
     MSA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, inconsistent heads, size overflow */
     MSA_ERR_UNSUPPORTED = 2, /* a valid shape this build does not handle (see msa_shape) */
@@ -82,7 +93,7 @@ typedef struct msa_shape {
     uint32_t flags;      /* MSA_CAUSAL must be set */
 } msa_shape;
 
-typedef enum msa_op {
+typedef enum msa_op MSA_ENUM_INT32 {
     MSA_OP_INDEX_SCORES = 0,
     MSA_OP_BLOCK_TOPK = 1,
     MSA_OP_SPARSE_ATTN_FWD = 2,
@@ -99,7 +110,8 @@ typedef enum msa_op {
  * MSA_OP_SPARSE_ATTN_FWD and MSA_OP_FWD: the per-slot partial results grow with
  * seqlen * top_k * h_q, so the answer is the size for one pass over all query
  * positions when that is at most 64 GiB, and otherwise the size for the largest
- * chunk of positions (a multiple of 128) that fits in 64 GiB. */
+ * chunk of positions (a multiple of 128) that fits in 64 GiB, or for 128
+ * positions when not even those fit (the smallest chunk the forward runs). */
 msa_status msa_workspace_size(const msa_shape* shape, msa_op op, size_t* bytes);
 
 /* Index scores with causal block max-pool ([MSA summary] "Architecture";
@@ -141,7 +153,8 @@ msa_status msa_index_topk(const msa_shape* shape, const void* q_idx, const void*
  *   z_j = softmax_scale * q[b,t,h] . k[b,j,g]  for j in a selected block, j <= t
  *   o[b,t,h] = sum_j softmax(z)_j v[b,j,g];   lse[b,h,t] = log sum_j exp(z_j)
  * block_idx entries outside [0, t/128] are ignored (treated as padding);
- * entries must not repeat within a row (a repeated block counts twice). A row
+ * a block listed twice in a row counts twice (the selections msa_fwd makes
+ * never repeat a block). A row
  * with no valid entry gives o = 0 and lse = -inf. Runs KV-outer: each
  * (key block, KV head) tile gathers the queries that selected it ([MSA summary]
  * "GPU kernel co-design"), writes per-slot partial results into the workspace,
