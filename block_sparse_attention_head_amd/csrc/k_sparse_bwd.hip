@@ -13,14 +13,19 @@
 //
 // Kernels:
 //   k_bwd_delta       per (b, t, h) row: D and LSE * log2(e).
-//   k_bwd_main        one persistent workgroup per work item (a chunk of the
-//                     rows gathered for one (key block, KV head) tile). Wave w
-//                     owns keys 32w .. 32w+31 of the block and keeps their K, V
-//                     as MFMA operands in registers. Per 32 gathered rows:
-//                       S = Q K^T, dP = dO V^T    (rows x own keys, one lane per key)
+//   k_bwd_main        one persistent workgroup of 8 waves per CU walks the
+//                     work items (a chunk of the rows gathered for one
+//                     (key block, KV head) tile). Wave w owns keys 16w .. 16w+15
+//                     of the block and keeps their K, V as MFMA operands in
+//                     registers (16x16x32 bf16 MFMA throughout). Per 32
+//                     gathered rows (a "step", staged row-major in an LDS ring
+//                     by global->LDS loads three steps ahead):
+//                       S = Q K^T, dP = dO V^T    (rows x own keys)
 //                       P, dS                      (bf16, dS also into LDS)
-//                       dV += P^T dO, dK += dS^T Q (Q, dO staged transposed in LDS)
-//                       dQ^T = K^T dS^T            (all 128 keys, own 32 dims)
+//                       dV += P^T dO, dK += dS^T Q (transposed operands read from
+//                                                   the row-major tiles with
+//                                                   ds_read_b64_tr_b16)
+//                       dQ^T = K^T dS^T            (all 128 keys, own 16 dims)
 //                     dQ rows go to bf16 per-(t, slot, head) partials (the
 //                     forward's chunk-major record layout); dK, dV to one fp32
 //                     partial per work item.
