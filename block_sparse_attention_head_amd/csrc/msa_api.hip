@@ -2,6 +2,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "msa.h"
 #include "msa_internal.hpp"
@@ -12,6 +13,31 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet; benign race (same value)
+
+// Scratch of msa_decode_noalloc: one copy of this array on every GPU the library
+// runs on, held until the process ends. In host code `scratch` names a host-side
+// stand-in, never a device address: the device address is looked up once per
+// device (hipGetSymbolAddress, with that device current) and only that address
+// is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[MSA_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch_dev[kMaxDevices];  // device address of `scratch`, per device
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array, or null on a HIP error.
+void* scratch_address(int dev) {
+    void* p = g_scratch_dev[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_dev[dev].load(std::memory_order_relaxed);
+    if (p) return p;
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    g_scratch_dev[dev].store(addr, std::memory_order_release);
+    return addr;
+}
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 int log2i(int x) {
@@ -254,6 +280,16 @@ hipError_t run_index_topk(const void* q_idx, const void* k_idx, int32_t* block_i
 
 msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
 
+// The decode step's three kernels with the pooled scores in `pooled` (dec_ws_bytes).
+hipError_t run_decode(const void* q_idx, const void* k_idx, const void* q, const void* k, const void* v,
+                      const int32_t* seqlens, int32_t* block_idx, void* o, float* lse, float* pooled, const Dims& d,
+                      hipStream_t stream) {
+    hipError_t e = launch_dec_index(q_idx, k_idx, seqlens, pooled, d, stream);
+    if (e == hipSuccess) e = launch_dec_topk(pooled, seqlens, block_idx, d, stream);
+    if (e == hipSuccess) e = launch_dec_attn(q, k, v, seqlens, block_idx, o, lse, d, stream);
+    return e;
+}
+
 // Sparse attention over every query position, in chunks of `chunk` positions that
 // reuse one workspace (plan, partials); each chunk's rows only read K/V and the block
 // indices, so the chunks are independent.
@@ -451,11 +487,28 @@ msa_status msa_decode(const msa_shape* shape, const void* q_idx, const void* k_i
     if (!q_idx || !k_idx || !q || !k || !v || !seqlens || !block_idx || !o || !lse) return MSA_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < dec_ws_bytes(d)) return MSA_ERR_WORKSPACE;
     (void)hipGetLastError();
-    float* pooled = (float*)workspace;
-    hipError_t e = launch_dec_index(q_idx, k_idx, seqlens, pooled, d, stream);
-    if (e == hipSuccess) e = launch_dec_topk(pooled, seqlens, block_idx, d, stream);
-    if (e == hipSuccess) e = launch_dec_attn(q, k, v, seqlens, block_idx, o, lse, d, stream);
-    return hip_status(e);
+    return hip_status(run_decode(q_idx, k_idx, q, k, v, seqlens, block_idx, o, lse, (float*)workspace, d, stream));
+}
+
+msa_status msa_decode_noalloc(const msa_shape* shape, const void* q_idx, const void* k_idx, const void* q,
+                              const void* k, const void* v, const int32_t* seqlens, int32_t* block_idx, void* o,
+                              float* lse, hipStream_t stream) {
+    Dims d;
+    const msa_status st = check_decode_shape(shape, &d);
+    if (st != MSA_OK) return st;
+    if (!q_idx || !k_idx || !q || !k || !v || !seqlens || !block_idx || !o || !lse) return MSA_ERR_INVALID_ARG;
+    if (dec_ws_bytes(d) > (size_t)MSA_NOALLOC_SCRATCH_BYTES) return MSA_ERR_WORKSPACE;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return MSA_ERR_HIP;
+    }
+    void* ws = scratch_address(dev);
+    if (!ws) return MSA_ERR_HIP;
+    (void)hipGetLastError();
+    // every pooled entry the selection reads is written by the index kernel of this
+    // call, so the scratch needs no clearing between calls
+    return hip_status(run_decode(q_idx, k_idx, q, k, v, seqlens, block_idx, o, lse, (float*)ws, d, stream));
 }
 
 msa_status msa_sparse_attn_bwd(const msa_shape* shape, const void* q, const void* k, const void* v, const void* o,

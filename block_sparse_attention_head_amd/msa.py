@@ -66,6 +66,7 @@ _SIGNATURES = {
     "msa_decode_topk": [_S, _P, _P, _P, _P],
     "msa_decode_attn": [_S, _P, _P, _P, _P, _P, _P, _P, _P],
     "msa_decode": [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "msa_decode_noalloc": [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "msa_index_bwd": [_S, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P],
 }
 
@@ -384,4 +385,23 @@ def decode(q_idx, k_idx, q, k, v, seqlens, top_k: int, softmax_scale: float, blo
     _check("msa_decode", lib().msa_decode(ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k), _ptr(v),
                                           _ptr(seqlens), _ptr(block_idx), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
                                           _stream(q.device)))
+    return block_idx, o, lse
+
+
+def decode_noalloc(q_idx, k_idx, q, k, v, seqlens, top_k: int, softmax_scale: float, block_idx=None, o=None,
+                   lse=None):
+    """msa_decode_noalloc: the decode step with the library's static scratch (no workspace).
+    Outputs are allocated here only when not given; pass them to keep the call allocation-free."""
+    shape = _decode_shape(q_idx, k_idx, q, k, v, seqlens, top_k, softmax_scale)
+    B, H, _ = q_idx.shape
+    Hq = q.shape[1]
+    block_idx = torch.empty((B, H, top_k), dtype=torch.int32, device=q.device) if block_idx is None else block_idx
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(block_idx, "block_idx", torch.int32, (B, H, top_k))
+    _need(o, "o", torch.bfloat16, q.shape)
+    _need(lse, "lse", torch.float32, (B, Hq))
+    _check("msa_decode_noalloc", lib().msa_decode_noalloc(
+        ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens), _ptr(block_idx),
+        _ptr(o), _ptr(lse), _stream(q.device)))
     return block_idx, o, lse

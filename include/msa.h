@@ -288,6 +288,23 @@ msa_status msa_decode(const msa_shape* shape, const void* q_idx, const void* k_i
                       const void* k, const void* v, const int32_t* seqlens, int32_t* block_idx,
                       void* o, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* msa_decode without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops and harnesses that forbid
+ * hipMalloc). The step's scratch (the pooled block scores, B * H_idx * C/128 * 4
+ * bytes rounded up to 256) lives in a static device array of
+ * MSA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on, from
+ * the first call on that GPU until the process ends; this call allocates nothing.
+ * A step that needs more scratch than that returns MSA_ERR_WORKSPACE (nothing is
+ * enqueued; use msa_decode). All calls on one GPU share its array: calls whose
+ * work overlaps in time on the same GPU (other streams, other host threads) race
+ * and must be ordered by the caller. Same arguments, outputs and results as
+ * msa_decode (bit for bit); the first call on each device looks up the array's
+ * device address (MSA_ERR_HIP if that fails). */
+#define MSA_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)
+msa_status msa_decode_noalloc(const msa_shape* shape, const void* q_idx, const void* k_idx, const void* q,
+                              const void* k, const void* v, const int32_t* seqlens, int32_t* block_idx,
+                              void* o, float* lse, hipStream_t stream);
+
 /* Static, never-NULL description of a status code. */
 const char* msa_status_string(msa_status status);
 

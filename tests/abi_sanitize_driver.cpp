@@ -182,6 +182,12 @@ int main() {
     dec_bad.seqlen = 4000;
     EXPECT_EQ(msa_decode(&dec_bad, P, P, P, P, P, PI, PI, P, PF, P, dec_ws, S), MSA_ERR_UNSUPPORTED);
 
+    // the allocation-free decode: rejected before it looks anything up on a device
+    EXPECT_EQ(msa_decode_noalloc(&dec, P, P, P, P, P, PI, PI, P, nullptr, S), MSA_ERR_INVALID_ARG);
+    EXPECT_EQ(msa_decode_noalloc(&dec_bad, P, P, P, P, P, PI, PI, P, PF, S), MSA_ERR_UNSUPPORTED);
+    msa_shape dec_big = make(64, 1 << 21, 8, 8, 16);  // 64 * 8 * 16384 * 4 B = 32 MiB of pooled scores
+    EXPECT_EQ(msa_decode_noalloc(&dec_big, P, P, P, P, P, PI, PI, P, PF, S), MSA_ERR_WORKSPACE);
+
     // status strings: never NULL, also for values outside the enum
     for (int st = -3; st <= 8; ++st) {
         ++g_checks;
