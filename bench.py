@@ -246,6 +246,9 @@ def decode_report(w, steps: int, warmup: int):
     bi = torch.empty((B, Hkv, K), dtype=torch.int32, device=dev)
     o = torch.empty_like(x["q"])
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    # the attention's workspace: as in msa_decode, few sequences spread a group's blocks over
+    # several workgroups whose records a second kernel merges
+    ws = msa.alloc_workspace(msa.make_shape(B, C, Hq, Hkv, K, w.softmax_scale), msa.OP_DECODE, dev)
 
     def step(ev=None):
         if ev is not None:
@@ -256,7 +259,7 @@ def decode_report(w, steps: int, warmup: int):
         msa.decode_topk(pooled, x["seqlens"], K, C, bi)
         if ev is not None:
             ev[2].record()
-        msa.decode_attn(x["q"], x["k"], x["v"], x["seqlens"], bi, w.softmax_scale, o, lse)
+        msa.decode_attn(x["q"], x["k"], x["v"], x["seqlens"], bi, w.softmax_scale, o, lse, workspace=ws)
         if ev is not None:
             ev[3].record()
 
@@ -281,7 +284,7 @@ def decode_report(w, steps: int, warmup: int):
         stages[name] = {"ms": round(ms, 4), "algorithmic_GB": round(nbytes[name] / 1e9, 4), "achieved": round(gbs, 1),
                         "unit": "GB/s", "frac": round(gbs / P.PEAK_HBM_GBS, 4), "kernel": kern,
                         "traffic": _traffic(kern, w.name, src)}
-    del x, pooled, bi, o, lse
+    del x, pooled, bi, o, lse, ws
     torch.cuda.empty_cache()
     total = sum(nbytes.values())
     return {"workload": w.name,

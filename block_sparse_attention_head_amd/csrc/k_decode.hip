@@ -224,6 +224,13 @@ __global__ __launch_bounds__(kDecTopkThreads) void k_dec_topk(const float* __res
 //   LDS tile (filled by global->LDS loads) through ds_read_b64_tr_b16, which
 //   hands each lane one dim of 4 consecutive keys.
 // The waves' (m, l, O) are merged in LDS at the end.
+//
+// Split mode (splits > 1; blockIdx.z = b * splits + split): when there are few
+// (sequence, KV head) groups, the selected slots of one group are dealt over
+// `splits` workgroups, so more CUs stream the blocks at once. Each workgroup
+// then writes its heads' (M, L) and unnormalised O (relative to M, log2 units)
+// to a record [b, head, split] instead of O and LSE, and k_dec_merge combines
+// the records: M* = max M_s, L* = sum L_s 2^(M_s - M*), O = sum O_s 2^(M_s - M*) / L*.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bf16x4 dec_tr_rows4(const __bf16* tile, int r0, int c0, int li) {
     const int row = r0 + (li >> 2), col = c0 + 4 * (li & 3);
@@ -235,8 +242,9 @@ __global__ __launch_bounds__(64 * NW) void k_dec_attn(const __bf16* __restrict__
                                                   const __bf16* __restrict__ v, const int32_t* __restrict__ seqlens,
                                                   const int32_t* __restrict__ block_idx, __bf16* __restrict__ o,
                                                   float* __restrict__ lse, int C, int Hq, int Hkv, int G, int top_k,
-                                                  float scale_log2) {
-    const int ht = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+                                                  float scale_log2, int splits, float2* __restrict__ rec_ml,
+                                                  float* __restrict__ rec_o) {
+    const int ht = blockIdx.x, g = blockIdx.y, b = blockIdx.z / splits, split = blockIdx.z - b * splits;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q4 = lane >> 4, n = lane & 15;
     const int L = dec_len(seqlens, b, C);
     const int t = L - 1;
@@ -267,8 +275,10 @@ __global__ __launch_bounds__(64 * NW) void k_dec_attn(const __bf16* __restrict__
     const size_t kv_row = (size_t)Hkv * kDim;  // elements between consecutive cache rows
     const __bf16* kseq = k + ((size_t)b * C * Hkv + g) * kDim;
     const __bf16* vseq = v + ((size_t)b * C * Hkv + g) * kDim;
-    // wave w takes slice w % 4 of the slots w / 4, w / 4 + NW / 4, ...
-    for (int s = wave / kDecAttnSlices; s < top_k; s += NW / kDecAttnSlices) {
+    // wave w takes slice w % 4 of its slot group's slots: group split * NW/4 + w/4 of
+    // the splits * NW/4 groups, slots group, group + splits * NW/4, ...
+    constexpr int kGroups = NW / kDecAttnSlices;
+    for (int s = split * kGroups + wave / kDecAttnSlices; s < top_k; s += splits * kGroups) {
         const int c = sel[s];
         if (c < 0 || c > cl) continue;  // padding or not visible
         const int kbase = c * kBlock + 32 * (wave % kDecAttnSlices);
@@ -370,18 +380,81 @@ __global__ __launch_bounds__(64 * NW) void k_dec_attn(const __bf16* __restrict__
     float Lsum = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) Lsum += sm[w][h] == -INFINITY ? 0.0f : exp2f(sm[w][h] - M) * sl[w][h];
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        acc[e] = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) acc[e] += red[(w * 16 + h) * kDim + d0 + e];
+    }
+    if (splits > 1) {  // this split's record; M = -inf, L = 0, O = 0 when it saw no key
+        const size_t rr = ((size_t)b * Hq + h0 + h) * splits + split;
+        float4* dst = (float4*)(rec_o + rr * kDim + d0);
+        dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        if ((tid & 15) == 0) rec_ml[rr] = make_float2(M, Lsum);
+        return;
+    }
     const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
     bf16x8 out;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) acc += red[(w * 16 + h) * kDim + d0 + e];
-        out[e] = (__bf16)(acc * inv);
-    }
+    for (int e = 0; e < 8; ++e) out[e] = (__bf16)(acc[e] * inv);
     *(bf16x8*)(o + ((size_t)b * Hq + h0 + h) * kDim + d0) = out;
     if ((tid & 15) == 0)
         lse[(size_t)b * Hq + h0 + h] = Lsum > 0.0f ? (M + log2f(Lsum)) * 0.69314718055994531f : -INFINITY;
+}
+
+// Merge of the split records, 16 threads (8 dims each) per (sequence, query head) row.
+// Every split writes its record (zeros and M = -inf when it saw no key), so all
+// records are loaded at once, with no load behind a data-dependent branch.
+constexpr int kDecMaxSplits = 16;
+
+__global__ __launch_bounds__(256) void k_dec_merge(const float2* __restrict__ rec_ml, const float* __restrict__ rec_o,
+                                                   __bf16* __restrict__ o, float* __restrict__ lse, int rows,
+                                                   int splits) {
+    const int r = blockIdx.x * 16 + (threadIdx.x >> 4), d0 = (threadIdx.x & 15) * 8;
+    if (r >= rows) return;
+    const float2* ml = rec_ml + (size_t)r * splits;
+    float2 x[kDecMaxSplits];
+    float4 a[kDecMaxSplits], c[kDecMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kDecMaxSplits; ++s) {
+        if (s < splits) {
+            x[s] = ml[s];
+            const float4* src = (const float4*)(rec_o + ((size_t)r * splits + s) * kDim + d0);
+            a[s] = src[0];
+            c[s] = src[1];
+        }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kDecMaxSplits; ++s)
+        if (s < splits) M = fmaxf(M, x[s].x);
+    float L = 0.0f, acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kDecMaxSplits; ++s) {
+        // a split that saw no key has M = -inf: weight 0 (its O is 0)
+        const float w = (s < splits && x[s].x != -INFINITY) ? exp2f(x[s].x - M) : 0.0f;
+        if (s < splits) {
+            L += w * x[s].y;
+            acc[0] += w * a[s].x;
+            acc[1] += w * a[s].y;
+            acc[2] += w * a[s].z;
+            acc[3] += w * a[s].w;
+            acc[4] += w * c[s].x;
+            acc[5] += w * c[s].y;
+            acc[6] += w * c[s].z;
+            acc[7] += w * c[s].w;
+        }
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    bf16x8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (__bf16)(acc[e] * inv);
+    *(bf16x8*)(o + (size_t)r * kDim + d0) = out;
+    if ((threadIdx.x & 15) == 0) lse[r] = L > 0.0f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -410,20 +483,59 @@ hipError_t launch_dec_topk(const float* pooled, const int32_t* seqlens, int32_t*
     return hipGetLastError();
 }
 
+// Workgroups the attention wants in flight before it spreads a group's slots over
+// several of them: four per CU of a 256-CU part. A constant (not the device's CU
+// count) so that the split, and so the rounding of the result, depends on the shape
+// alone.
+constexpr long long kDecAttnWantGroups = 1024;
+
+int dec_splits(const Dims& d) {
+    const long long base = (long long)((d.G + 15) / 16) * d.Hkv * d.B;
+    if (base * 2 >= kDecAttnWantGroups) return 1;
+    long long s = (kDecAttnWantGroups + base - 1) / base;
+    if (s > d.top_k) s = d.top_k;
+    return (int)(s < kDecMaxSplits ? s : kDecMaxSplits);
+}
+
+size_t dec_rec_bytes(const Dims& d) {
+    const int S = dec_splits(d);
+    if (S <= 1) return 0;
+    const size_t recs = (size_t)d.B * d.Hq * S;
+    return align_up(recs * sizeof(float2), 256) + align_up(recs * kDim * sizeof(float), 256);
+}
+
 hipError_t launch_dec_attn(const void* q, const void* k, const void* v, const int32_t* seqlens,
-                           const int32_t* block_idx, void* o, float* lse, const Dims& d, hipStream_t stream) {
-    dim3 grid((unsigned)((d.G + 15) / 16), (unsigned)d.Hkv, (unsigned)d.B);
+                           const int32_t* block_idx, void* o, float* lse, void* records, const Dims& d,
+                           hipStream_t stream) {
     const float sl2 = d.scale * 1.4426950408889634f;
+    const int S = records ? dec_splits(d) : 1;
+    if (S > 1) {
+        // split mode: four-wave workgroups, the group's slots dealt over S of them, then the merge
+        const size_t recs = (size_t)d.B * d.Hq * S;
+        float2* rec_ml = (float2*)records;
+        float* rec_o = (float*)((char*)records + align_up(recs * sizeof(float2), 256));
+        dim3 grid((unsigned)((d.G + 15) / 16), (unsigned)d.Hkv, (unsigned)(d.B * S));
+        hipLaunchKernelGGL(k_dec_attn<kDecAttnSlices>, grid, dim3(64 * kDecAttnSlices), 0, stream, (const __bf16*)q,
+                           (const __bf16*)k, (const __bf16*)v, seqlens, block_idx, (__bf16*)o, lse, d.N, d.Hq, d.Hkv,
+                           d.G, d.top_k, sl2, S, rec_ml, rec_o);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int rows = d.B * d.Hq;
+        hipLaunchKernelGGL(k_dec_merge, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, rec_ml, rec_o,
+                           (__bf16*)o, lse, rows, S);
+        return hipGetLastError();
+    }
+    dim3 grid((unsigned)((d.G + 15) / 16), (unsigned)d.Hkv, (unsigned)d.B);
     // Few (sequence, KV head, head tile) groups would leave most CUs idle: then four slot
     // groups of four waves share a group's selected blocks (16 waves, 130 KB of LDS).
     if ((long long)grid.x * grid.y * grid.z < device_cu_count()) {
         hipLaunchKernelGGL(k_dec_attn<4 * kDecAttnSlices>, grid, dim3(64 * 4 * kDecAttnSlices), 0, stream,
                            (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, seqlens, block_idx, (__bf16*)o, lse,
-                           d.N, d.Hq, d.Hkv, d.G, d.top_k, sl2);
+                           d.N, d.Hq, d.Hkv, d.G, d.top_k, sl2, 1, (float2*)nullptr, (float*)nullptr);
     } else {
         hipLaunchKernelGGL(k_dec_attn<kDecAttnSlices>, grid, dim3(64 * kDecAttnSlices), 0, stream, (const __bf16*)q,
                            (const __bf16*)k, (const __bf16*)v, seqlens, block_idx, (__bf16*)o, lse, d.N, d.Hq, d.Hkv,
-                           d.G, d.top_k, sl2);
+                           d.G, d.top_k, sl2, 1, (float2*)nullptr, (float*)nullptr);
     }
     return hipGetLastError();
 }

@@ -117,7 +117,9 @@ msa_status check_decode_shape(const msa_shape* s, Dims* d) {
     return MSA_OK;
 }
 
-size_t dec_ws_bytes(const Dims& d) { return align_up((size_t)d.B * d.Hkv * d.nblk * sizeof(float), 256); }
+// Decode workspace: the pooled scores, then the attention's split records (if any).
+size_t dec_pooled_bytes(const Dims& d) { return align_up((size_t)d.B * d.Hkv * d.nblk * sizeof(float), 256); }
+size_t dec_ws_bytes(const Dims& d) { return dec_pooled_bytes(d) + dec_rec_bytes(d); }
 
 }  // namespace
 
@@ -280,13 +282,16 @@ hipError_t run_index_topk(const void* q_idx, const void* k_idx, int32_t* block_i
 
 msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
 
-// The decode step's three kernels with the pooled scores in `pooled` (dec_ws_bytes).
+// The decode step's kernels in a workspace of dec_ws_bytes(d): pooled scores first,
+// then the attention's split records.
 hipError_t run_decode(const void* q_idx, const void* k_idx, const void* q, const void* k, const void* v,
-                      const int32_t* seqlens, int32_t* block_idx, void* o, float* lse, float* pooled, const Dims& d,
+                      const int32_t* seqlens, int32_t* block_idx, void* o, float* lse, void* ws, const Dims& d,
                       hipStream_t stream) {
+    float* pooled = (float*)ws;
+    void* records = dec_rec_bytes(d) ? (char*)ws + dec_pooled_bytes(d) : nullptr;
     hipError_t e = launch_dec_index(q_idx, k_idx, seqlens, pooled, d, stream);
     if (e == hipSuccess) e = launch_dec_topk(pooled, seqlens, block_idx, d, stream);
-    if (e == hipSuccess) e = launch_dec_attn(q, k, v, seqlens, block_idx, o, lse, d, stream);
+    if (e == hipSuccess) e = launch_dec_attn(q, k, v, seqlens, block_idx, o, lse, records, d, stream);
     return e;
 }
 
@@ -469,13 +474,16 @@ msa_status msa_decode_topk(const msa_shape* shape, const float* pooled, const in
 
 msa_status msa_decode_attn(const msa_shape* shape, const void* q, const void* k, const void* v,
                            const int32_t* seqlens, const int32_t* block_idx, void* o, float* lse,
-                           hipStream_t stream) {
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
     Dims d;
     const msa_status st = check_decode_shape(shape, &d);
     if (st != MSA_OK) return st;
     if (!q || !k || !v || !seqlens || !block_idx || !o || !lse) return MSA_ERR_INVALID_ARG;
+    const size_t rec = dec_rec_bytes(d);
+    if (workspace && workspace_bytes < rec) return MSA_ERR_WORKSPACE;
     (void)hipGetLastError();
-    return hip_status(launch_dec_attn(q, k, v, seqlens, block_idx, o, lse, d, stream));
+    return hip_status(launch_dec_attn(q, k, v, seqlens, block_idx, o, lse, workspace && rec ? workspace : nullptr, d,
+                                      stream));
 }
 
 msa_status msa_decode(const msa_shape* shape, const void* q_idx, const void* k_idx, const void* q, const void* k,
@@ -487,7 +495,7 @@ msa_status msa_decode(const msa_shape* shape, const void* q_idx, const void* k_i
     if (!q_idx || !k_idx || !q || !k || !v || !seqlens || !block_idx || !o || !lse) return MSA_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < dec_ws_bytes(d)) return MSA_ERR_WORKSPACE;
     (void)hipGetLastError();
-    return hip_status(run_decode(q_idx, k_idx, q, k, v, seqlens, block_idx, o, lse, (float*)workspace, d, stream));
+    return hip_status(run_decode(q_idx, k_idx, q, k, v, seqlens, block_idx, o, lse, workspace, d, stream));
 }
 
 msa_status msa_decode_noalloc(const msa_shape* shape, const void* q_idx, const void* k_idx, const void* q,
@@ -506,9 +514,9 @@ msa_status msa_decode_noalloc(const msa_shape* shape, const void* q_idx, const v
     void* ws = scratch_address(dev);
     if (!ws) return MSA_ERR_HIP;
     (void)hipGetLastError();
-    // every pooled entry the selection reads is written by the index kernel of this
-    // call, so the scratch needs no clearing between calls
-    return hip_status(run_decode(q_idx, k_idx, q, k, v, seqlens, block_idx, o, lse, (float*)ws, d, stream));
+    // every pooled entry the selection reads, and every split record the merge reads, is
+    // written by this call's kernels first, so the scratch needs no clearing between calls
+    return hip_status(run_decode(q_idx, k_idx, q, k, v, seqlens, block_idx, o, lse, ws, d, stream));
 }
 
 msa_status msa_sparse_attn_bwd(const msa_shape* shape, const void* q, const void* k, const void* v, const void* o,

@@ -34,8 +34,15 @@ hipError_t launch_dec_index(const void* q_idx, const void* k_idx, const int32_t*
                             hipStream_t stream);
 hipError_t launch_dec_topk(const float* pooled, const int32_t* seqlens, int32_t* block_idx, const Dims& d,
                            hipStream_t stream);
+// Attention over the selected blocks. With `records` (dec_rec_bytes(d) bytes, non-null
+// only when that is nonzero) a group's slots are spread over dec_splits(d) workgroups
+// whose (m, l, O) records a second kernel merges; with records == null one workgroup
+// per (sequence, KV head, head tile) does all its slots.
+int dec_splits(const Dims& d);
+size_t dec_rec_bytes(const Dims& d);
 hipError_t launch_dec_attn(const void* q, const void* k, const void* v, const int32_t* seqlens,
-                           const int32_t* block_idx, void* o, float* lse, const Dims& d, hipStream_t stream);
+                           const int32_t* block_idx, void* o, float* lse, void* records, const Dims& d,
+                           hipStream_t stream);
 
 // Index scores + block max-pool + top-k selection in one pass with no pooled
 // scores in memory and no scratch; needs index_topk_fusable(d) (top_k <= 17).

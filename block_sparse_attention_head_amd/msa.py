@@ -64,7 +64,7 @@ _SIGNATURES = {
     "msa_index_topk": [_S, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "msa_decode_index_scores": [_S, _P, _P, _P, _P, _P],
     "msa_decode_topk": [_S, _P, _P, _P, _P],
-    "msa_decode_attn": [_S, _P, _P, _P, _P, _P, _P, _P, _P],
+    "msa_decode_attn": [_S, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "msa_decode": [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "msa_decode_noalloc": [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "msa_index_bwd": [_S, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P],
@@ -349,8 +349,10 @@ def decode_topk(pooled, seqlens, top_k: int, capacity: int, block_idx=None) -> t
     return block_idx
 
 
-def decode_attn(q, k, v, seqlens, block_idx, softmax_scale: float, o=None, lse=None):
-    """(O bf16 [B, H_q, 128], LSE fp32 [B, H_q]) over the selected blocks (see msa_decode_attn)."""
+def decode_attn(q, k, v, seqlens, block_idx, softmax_scale: float, o=None, lse=None, workspace=None):
+    """(O bf16 [B, H_q, 128], LSE fp32 [B, H_q]) over the selected blocks (see msa_decode_attn).
+    With a workspace (uint8, msa_workspace_size(MSA_OP_DECODE) bytes) a step with few sequences
+    spreads each group's blocks over several workgroups, as msa_decode does."""
     B, Hq, D = q.shape
     C, Hkv = k.shape[1], k.shape[2]
     top_k = block_idx.shape[-1]
@@ -364,8 +366,12 @@ def decode_attn(q, k, v, seqlens, block_idx, softmax_scale: float, o=None, lse=N
     _need(o, "o", torch.bfloat16, (B, Hq, D))
     _need(lse, "lse", torch.float32, (B, Hq))
     shape = make_shape(B, C, Hq, Hkv, top_k, softmax_scale)
-    _check("msa_decode_attn", lib().msa_decode_attn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens),
-                                                    _ptr(block_idx), _ptr(o), _ptr(lse), _stream(q.device)))
+    if workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_contiguous()
+                                  or workspace.device != q.device):
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    _check("msa_decode_attn", lib().msa_decode_attn(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens), _ptr(block_idx), _ptr(o), _ptr(lse),
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(q.device)))
     return o, lse
 
 

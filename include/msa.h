@@ -278,12 +278,19 @@ msa_status msa_decode_topk(const msa_shape* shape, const float* pooled, const in
                            int32_t* block_idx, hipStream_t stream);
 
 /* Softmax attention of each query head over its group's selected blocks (entries
- * outside [0, t/128] ignored; a repeated entry counts twice, as in the forward). */
+ * outside [0, t/128] ignored; a repeated entry counts twice, as in the forward).
+ * workspace may be NULL: then one workgroup per (sequence, KV head, 16 query
+ * heads) walks all of its group's blocks. With a workspace of at least
+ * msa_workspace_size(MSA_OP_DECODE) bytes (MSA_ERR_WORKSPACE if smaller), a step
+ * with few sequences spreads each group's blocks over several workgroups, whose
+ * per-split (max, sum, output) records a second kernel merges; the results agree
+ * within rounding. msa_decode always passes its workspace. */
 msa_status msa_decode_attn(const msa_shape* shape, const void* q, const void* k, const void* v,
                            const int32_t* seqlens, const int32_t* block_idx, void* o, float* lse,
-                           hipStream_t stream);
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* The three steps in turn; the pooled scores live in the workspace (MSA_OP_DECODE). */
+/* The three steps in turn; the pooled scores and the attention's split records
+ * live in the workspace (MSA_OP_DECODE). */
 msa_status msa_decode(const msa_shape* shape, const void* q_idx, const void* k_idx, const void* q,
                       const void* k, const void* v, const int32_t* seqlens, int32_t* block_idx,
                       void* o, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -291,7 +298,8 @@ msa_status msa_decode(const msa_shape* shape, const void* q_idx, const void* k_i
 /* msa_decode without a workspace, for callers that cannot allocate device memory
  * (code under HIP graph capture, serving loops and harnesses that forbid
  * hipMalloc). The step's scratch (the pooled block scores, B * H_idx * C/128 * 4
- * bytes rounded up to 256) lives in a static device array of
+ * bytes, and with few sequences the attention's split records: the size
+ * msa_workspace_size(MSA_OP_DECODE) gives) lives in a static device array of
  * MSA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on, from
  * the first call on that GPU until the process ends; this call allocates nothing.
  * A step that needs more scratch than that returns MSA_ERR_WORKSPACE (nothing is
@@ -300,7 +308,7 @@ msa_status msa_decode(const msa_shape* shape, const void* q_idx, const void* k_i
  * and must be ordered by the caller. Same arguments, outputs and results as
  * msa_decode (bit for bit); the first call on each device looks up the array's
  * device address (MSA_ERR_HIP if that fails). */
-#define MSA_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)
+#define MSA_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
 msa_status msa_decode_noalloc(const msa_shape* shape, const void* q_idx, const void* k_idx, const void* q,
                               const void* k, const void* v, const int32_t* seqlens, int32_t* block_idx,
                               void* o, float* lse, hipStream_t stream);

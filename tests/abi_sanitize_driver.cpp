@@ -175,7 +175,8 @@ int main() {
     const size_t dec_ws = bytes;
     EXPECT_EQ(msa_decode_index_scores(&dec, P, P, nullptr, PF, S), MSA_ERR_INVALID_ARG);
     EXPECT_EQ(msa_decode_topk(&dec, PF, PI, nullptr, S), MSA_ERR_INVALID_ARG);
-    EXPECT_EQ(msa_decode_attn(&dec, P, P, P, PI, PI, nullptr, PF, S), MSA_ERR_INVALID_ARG);
+    EXPECT_EQ(msa_decode_attn(&dec, P, P, P, PI, PI, nullptr, PF, nullptr, 0, S), MSA_ERR_INVALID_ARG);
+    EXPECT_EQ(msa_decode_attn(&dec, P, P, P, PI, PI, P, PF, P, 16, S), MSA_ERR_WORKSPACE);  // split records
     EXPECT_EQ(msa_decode(&dec, P, P, P, P, P, PI, PI, P, PF, nullptr, dec_ws, S), MSA_ERR_WORKSPACE);
     EXPECT_EQ(msa_decode(&dec, P, P, P, P, P, PI, PI, P, PF, P, dec_ws - 1, S), MSA_ERR_WORKSPACE);
     msa_shape dec_bad = dec;
@@ -185,7 +186,7 @@ int main() {
     // the allocation-free decode: rejected before it looks anything up on a device
     EXPECT_EQ(msa_decode_noalloc(&dec, P, P, P, P, P, PI, PI, P, nullptr, S), MSA_ERR_INVALID_ARG);
     EXPECT_EQ(msa_decode_noalloc(&dec_bad, P, P, P, P, P, PI, PI, P, PF, S), MSA_ERR_UNSUPPORTED);
-    msa_shape dec_big = make(64, 1 << 21, 8, 8, 16);  // 64 * 8 * 16384 * 4 B = 32 MiB of pooled scores
+    msa_shape dec_big = make(128, 1 << 21, 8, 8, 16);  // 128 * 8 * 16384 * 4 B = 64 MiB of pooled scores
     EXPECT_EQ(msa_decode_noalloc(&dec_big, P, P, P, P, P, PI, PI, P, PF, S), MSA_ERR_WORKSPACE);
 
     // status strings: never NULL, also for values outside the enum

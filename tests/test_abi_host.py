@@ -178,7 +178,10 @@ def test_decode_shape_validation_and_workspace(m):
     assert lib.msa_decode(ctypes.byref(s), *args, one, 8, P(0)) == 3
     assert lib.msa_decode(ctypes.byref(s), *args, P(0), 1 << 40, P(0)) == 3
     assert lib.msa_decode_index_scores(ctypes.byref(s), one, one, P(0), one, P(0)) == 1
-    assert lib.msa_decode_attn(ctypes.byref(s), one, one, one, one, one, one, P(0), P(0)) == 1
+    assert lib.msa_decode_attn(ctypes.byref(s), one, one, one, one, one, one, P(0), P(0), 0, P(0)) == 1
+    # 8 sequences x 4 KV heads leave CUs idle: a workspace given to the attention must hold
+    # its split records (NULL runs one workgroup per group and needs none)
+    assert lib.msa_decode_attn(ctypes.byref(s), one, one, one, one, one, one, one, one, 8, P(0)) == 3
 
 
 def test_index_bwd_validation(m):

@@ -63,7 +63,12 @@ def _parity(msa, w, x, tag):
     _say(tag, "stages")
     pooled = msa.decode_index_scores(xg["q_idx"], xg["k_idx"], xg["seqlens"])
     sel = msa.decode_topk(pooled, xg["seqlens"], K, C)
-    o, lse = msa.decode_attn(xg["q"], xg["k"], xg["v"], xg["seqlens"], sel, w.softmax_scale)
+    # with a workspace the attention spreads each group's blocks over several workgroups
+    # when there are few sequences (as msa_decode does); without, one workgroup per group
+    ws = msa.alloc_workspace(msa.make_shape(w.batch, C, w.h_q, w.h_kv, K, w.softmax_scale), msa.OP_DECODE,
+                             xg["q"].device)
+    o, lse = msa.decode_attn(xg["q"], xg["k"], xg["v"], xg["seqlens"], sel, w.softmax_scale, workspace=ws)
+    o1, lse1 = msa.decode_attn(xg["q"], xg["k"], xg["v"], xg["seqlens"], sel, w.softmax_scale)
     _say(tag, "msa_decode")
     bi, o2, lse2 = msa.decode(xg["q_idx"], xg["k_idx"], xg["q"], xg["k"], xg["v"], xg["seqlens"], K,
                               w.softmax_scale)
@@ -82,6 +87,7 @@ def _parity(msa, w, x, tag):
     _, o_r, lse_r, _ = O.msa_decode(cpu["q_idx"], cpu["k_idx"], cpu["q"], cpu["k"], cpu["v"], cpu["seqlens"], K,
                                     w.softmax_scale, block_idx=sg)
     do, dl = check_attn(og, lg, o_r, lse_r, tag)
+    check_attn(to_np(o1), to_np(lse1), o_r, lse_r, tag + "/one-workgroup-per-group")
     assert np.isfinite(og).all()
     _say(tag, f"O err {do:.2e} LSE err {dl:.2e} selection mismatches/near-ties {mis}")
     return sg, og, lg
@@ -177,15 +183,19 @@ def test_decode_attn_invalid_and_repeated_entries(msa):
     given[0, 0] = [4, 4, 4, 15, -1, 20]
     given[1, 1] = [3, 9, -1, -2, 17, 5]  # nothing visible for L = 300
     xg = _gpu(x)
-    _say(w.name, "caller's selection")
-    o, lse = msa.decode_attn(xg["q"], xg["k"], xg["v"], xg["seqlens"], torch.from_numpy(given).to(DEV),
-                             w.softmax_scale)
-    torch.cuda.synchronize()
     _, o_r, lse_r, _ = O.msa_decode(x["q_idx"], x["k_idx"], x["q"], x["k"], x["v"], x["seqlens"], 6,
                                     w.softmax_scale, block_idx=given)
-    og, lg = to_np(o), to_np(lse)
-    check_attn(og, lg, o_r, lse_r, w.name)
-    assert not og[1, 8:].any() and np.isneginf(lg[1, 8:]).all()
+    ws = msa.alloc_workspace(msa.make_shape(3, 2048, 16, 2, 6, w.softmax_scale), msa.OP_DECODE, xg["q"].device)
+    # without a workspace (one workgroup per group), then with one (the group's slots split over
+    # several workgroups, some of which see no valid entry)
+    for label, wsp in (("one workgroup", None), ("split", ws)):
+        _say(w.name, f"caller's selection, {label}")
+        o, lse = msa.decode_attn(xg["q"], xg["k"], xg["v"], xg["seqlens"], torch.from_numpy(given).to(DEV),
+                                 w.softmax_scale, workspace=wsp)
+        torch.cuda.synchronize()
+        og, lg = to_np(o), to_np(lse)
+        check_attn(og, lg, o_r, lse_r, f"{w.name}/{label}")
+        assert not og[1, 8:].any() and np.isneginf(lg[1, 8:]).all()
 
 
 def test_decode_deterministic(msa):

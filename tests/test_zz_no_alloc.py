@@ -54,12 +54,12 @@ def test_decode_noalloc_matches_decode_on_two_calls(msa):
 
 
 def test_decode_noalloc_rejects_steps_past_its_scratch(msa):
-    # 64 sequences x 8 index heads x 16384 blocks x 4 B = 32 MiB of pooled scores > 16 MiB:
+    # 128 sequences x 8 index heads x 16384 blocks x 4 B = 64 MiB of pooled scores > 32 MiB:
     # the C ABI rejects the shape on the host, before any launch (the small buffers
     # passed here are never read)
     import ctypes
 
-    shape = msa.make_shape(64, 1 << 21, 8, 8, 16, 128 ** -0.5)
+    shape = msa.make_shape(128, 1 << 21, 8, 8, 16, 128 ** -0.5)
     buf = torch.zeros(1024, dtype=torch.float32, device=DEV)
     p = ctypes.c_void_p(buf.data_ptr())
     st = msa.lib().msa_decode_noalloc(ctypes.byref(shape), p, p, p, p, p, p, p, p, p,
