@@ -30,6 +30,46 @@
 
 namespace msa {
 
+// One step of the xor butterfly that sums x over aligned groups of lanes, through
+// the DPP lane crossbar instead of LDS permutes. After the steps for 1 and 2 (quad
+// permutations) every quad holds its sum; the half-row mirror then pairs each lane
+// with the other quad of its 8 lanes and the row mirror with the other 8 of its 16,
+// so each lane adds the same two partial sums, in the same order (its own first),
+// as the xor-4 and xor-8 steps would.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// Sum of the 32 values of v over each aligned group of G lanes (G a power of two <= 32),
+// left in every lane of the group: the xor butterfly 1, 2, ..., G/2.
+__device__ __forceinline__ void group_sum32(f32x16 (&v)[2], int G) {
+    if (G >= 2)
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[m2][i] = dpp_add<0xB1>(v[m2][i]);  // quad_perm [1,0,3,2]: xor 1
+    if (G >= 4)
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[m2][i] = dpp_add<0x4E>(v[m2][i]);  // quad_perm [2,3,0,1]: xor 2
+    if (G >= 8)
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[m2][i] = dpp_add<0x141>(v[m2][i]);  // row_half_mirror
+    if (G >= 16)
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[m2][i] = dpp_add<0x140>(v[m2][i]);  // row_mirror
+    if (G >= 32)
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[m2][i] += __shfl_xor(v[m2][i], 16, 64);
+}
+
 typedef __attribute__((address_space(3))) bf16x4* kl_lds_bf16x4_ptr;
 
 constexpr int kKlMaxItemEntries = kRowTilesPerItem * kBlock;  // entries of one item when G = 1
@@ -276,11 +316,7 @@ __global__ __launch_bounds__(256, 2) void k_kl_dz(
                         sacc[m2][i] =
                             key <= lim ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[m2][i], c_main, -lm)) : 0.0f;
                     }
-                for (int sft = 1; sft < G; sft <<= 1)
-#pragma unroll
-                    for (int m2 = 0; m2 < 2; ++m2)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) sacc[m2][i] += __shfl_xor(sacc[m2][i], sft, 64);
+                group_sum32(sacc, G);
                 if (valid && hh == 0) {
                     __bf16* dst = dz + (size_t)(ebase + li) * kBlock;
 #pragma unroll
@@ -397,11 +433,7 @@ __global__ __launch_bounds__(256, 2) void k_kl_dz_shared(
                         sacc[m2][i] =
                             key <= lims ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[m2][i], c_main, -lm)) : 0.0f;
                     }
-                for (int sft = 1; sft < G; sft <<= 1)
-#pragma unroll
-                    for (int m2 = 0; m2 < 2; ++m2)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) sacc[m2][i] += __shfl_xor(sacc[m2][i], sft, 64);
+                group_sum32(sacc, G);
                 if (hh == 0 && pslot < P) {
 #pragma unroll
                     for (int m2 = 0; m2 < 2; ++m2)
