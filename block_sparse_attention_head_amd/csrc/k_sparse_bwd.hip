@@ -99,6 +99,8 @@ __global__ __launch_bounds__(256) void k_bwd_delta(const __bf16* __restrict__ o,
 // ---------------------------------------------------------------------------
 constexpr int kBwdRows = 32;                                   // gathered rows per step
 constexpr int kBwdRing = 4;                                    // row-major stages
+constexpr int kBwdThreads = 256;                               // four waves, one per SIMD
+constexpr int kBwdKeysPerWave = 32;                            // keys (and dQ dims) of one wave
 constexpr int kBwdMaxItemEntries = kRowTilesPerItem * kBlock;  // entries of one item when G = 1
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -138,6 +140,19 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
     return (bf16x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// Scheduling: in the region that ends here, alternate M matrix instructions with one LDS
+// read, N times, so the reads of the next group of operands issue while the current
+// group's products run.
+template <int N, int M>
+__device__ __forceinline__ void interleave_mfma_ds_read() {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, M, 0);  // matrix instructions
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS reads
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // s_waitcnt with vmcnt <= n (n < 16) and no wait on the other counters (gfx9 encoding)
 #define MSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8))
 // s_waitcnt lgkmcnt(0) only
@@ -151,24 +166,36 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
 // compiler from moving memory accesses across the barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// A 16-bit LDS store the compiler's wait insertion does not see. A plain LDS
-// store made after global->LDS loads are issued makes the compiler wait for all
-// of them (it cannot tell the destinations apart), which would drain the row
-// prefetch every step. These stores go to a buffer no such load writes; the
-// caller waits on lgkmcnt(0) before the barrier that publishes them.
+// 16-bit LDS stores the compiler's wait insertion does not see. A plain LDS store
+// made after global->LDS loads are issued makes the compiler wait for all of them (it
+// cannot tell the destinations apart), which would drain the row prefetch every step.
+// These stores go to a buffer no such load writes; the caller waits on lgkmcnt(0)
+// before the barrier that publishes them. The _hi form stores the upper half of the
+// register.
 template <int OFF>
-__device__ __forceinline__ void lds_store_b16(uint32_t addr, uint32_t bits) {
+__device__ __forceinline__ void lds_store_lo16(uint32_t addr, uint32_t bits) {
     asm volatile("ds_write_b16 %0, %1 offset:%2" ::"v"(addr), "v"(bits), "i"(OFF) : "memory");
 }
-// The 8 dS values of a lane (register 4mt + i holds row 16mt + 4g + i) into
-// padded dS rows: byte address base + (16mt + i) * 2 * kDsRow, base covering the
-// lane's key and its 4g row offset.
-template <int... I>
-__device__ __forceinline__ void store_ds8(uint32_t base, const uint32_t (&bits)[8], std::integer_sequence<int, I...>) {
-    (lds_store_b16<(16 * (I >> 2) + (I & 3)) * 2 * kDsRow>(base, bits[I]), ...);
+template <int OFF>
+__device__ __forceinline__ void lds_store_hi16(uint32_t addr, uint32_t bits) {
+    asm volatile("ds_write_b16_d16_hi %0, %1 offset:%2" ::"v"(addr), "v"(bits), "i"(OFF) : "memory");
+}
+// The 8 bf16 dS values of a lane, as the packed A operand holds them (element e of
+// register pair j: e = 2j + half; element e is row 16 (e / 4) + e % 4 past the lane's 4 g4
+// offset), into padded dS rows at byte address base + row * 2 * kDsRow.
+__device__ __forceinline__ void store_ds8(uint32_t base, bf16x8 v) {
+    const u32x4 w = __builtin_bit_cast(u32x4, v);
+    lds_store_lo16<0 * 2 * kDsRow>(base, w.x);
+    lds_store_hi16<1 * 2 * kDsRow>(base, w.x);
+    lds_store_lo16<2 * 2 * kDsRow>(base, w.y);
+    lds_store_hi16<3 * 2 * kDsRow>(base, w.y);
+    lds_store_lo16<16 * 2 * kDsRow>(base, w.z);
+    lds_store_hi16<17 * 2 * kDsRow>(base, w.z);
+    lds_store_lo16<18 * 2 * kDsRow>(base, w.w);
+    lds_store_hi16<19 * 2 * kDsRow>(base, w.w);
 }
 
-__global__ __launch_bounds__(512, 1) void k_bwd_main(
+__global__ __launch_bounds__(256, 1) void k_bwd_main(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ rowterm, long long rows,
     const int32_t* __restrict__ off, const int32_t* __restrict__ item_off, const int32_t* __restrict__ entries,
@@ -187,10 +214,9 @@ __global__ __launch_bounds__(512, 1) void k_bwd_main(
     const int l16 = lane & 15, g4 = lane >> 4;                   // MFMA lane in its 16-lane group, group
     const int G = 1 << gshift;
     const int P = kBlock >> gshift;
-    const int kw0 = 16 * wave;       // this wave's first key (and first dQ dim)
-    const int my_key = kw0 + l16;    // key of this lane's S column
+    const int kw0 = kBwdKeysPerWave * wave;  // this wave's first key (and first dQ dim)
     const int total_items = item_off[n_tiles];
-    __bf16* ktile = ring[0].q;       // K [key][dim] during the item prologue
+    __bf16* ktile = ring[0].q;  // K [key][dim] during the item prologue
 
     for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
         int lo = 0, hi = n_tiles;  // tile = last index with item_off[tile] <= item
@@ -212,79 +238,94 @@ __global__ __launch_bounds__(512, 1) void k_bwd_main(
         const int kstride = Hkv * kDim;
 
         __syncthreads();  // the previous item's LDS reads are done
-        for (int i = tid; i < ne; i += 512) {
+        for (int i = tid; i < ne; i += kBwdThreads) {
             const int en = entries[e0 + rt0 * P + i], t = en >> 8;
             ent_row[i] = (b * N + t) * Hq + g * G;
             ent_rec[i] = (b * N + t) * top_k + (en & 255);
         }
-        // K tile -> LDS (row-major, swizzled through the source chunk): 4 x 4 rows per wave
+        // K tile -> LDS (row-major, swizzled through the source chunk): 8 x 4 rows per wave
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 32 * i + 4 * wave + (lane >> 4);
+        for (int i = 0; i < 8; ++i) {
+            const int r0 = 32 * (i >> 1) + 8 * wave + 4 * (i & 1);
+            const int row = r0 + (lane >> 4);
             const int ch = (lane & 15) ^ rsw(row);
             __builtin_amdgcn_global_load_lds((const void*)(k + tile_off + (size_t)row * kstride + ch * 8),
-                                             (lds_ptr)(ktile + (32 * i + 4 * wave) * kDim), 16, 0, 0);
+                                             (lds_ptr)(ktile + r0 * kDim), 16, 0, 0);
         }
-        // own keys as B operands of S, dP: lane holds K[my_key][32 kk + 8 g4 + e], same for V
-        bf16x8 kf[4], vf[4];
-        {
-            const size_t krow = tile_off + (size_t)my_key * kstride + 8 * g4;
+        // own keys as B operands of S, dP: for key tile kt, lane holds K[kw0 + 16 kt + l16][32 kk + 8 g4 + e]
+        bf16x8 kf[2][4], vf[2][4];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            const size_t krow = tile_off + (size_t)(kw0 + 16 * kt + l16) * kstride + 8 * g4;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                kf[kk] = *(const bf16x8*)(k + krow + kk * 32);
-                vf[kk] = *(const bf16x8*)(v + krow + kk * 32);
+                kf[kt][kk] = *(const bf16x8*)(k + krow + kk * 32);
+                vf[kt][kk] = *(const bf16x8*)(v + krow + kk * 32);
             }
         }
-        f32x4 dk[8], dv[8];
+        f32x4 dk[2][8], dv[2][8];
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dk[nt][i] = dv[nt][i] = 0.0f;
+            for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dk[kt][nt][i] = dv[kt][nt][i] = 0.0f;
         MSA_WAIT_VMCNT(0);
         __syncthreads();  // ent, K tile
-        // K^T fragments, A operands of dQ^T: lane holds K[32 kk + 8 g4 + e][16 wave + l16]
-        bf16x8 ktf[4];
+        // K^T fragments, A operands of dQ^T for dim tile dt: lane holds K[32 kk + 8 g4 + e][kw0 + 16 dt + l16]
+        bf16x8 ktf[2][4];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            ktf[kk] = cat8(tr_rows4(ktile, 32 * kk + 8 * g4, kw0, l16), tr_rows4(ktile, 32 * kk + 8 * g4 + 4, kw0, l16));
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                ktf[dt][kk] = cat8(tr_rows4(ktile, 32 * kk + 8 * g4, kw0 + 16 * dt, l16),
+                                   tr_rows4(ktile, 32 * kk + 8 * g4 + 4, kw0 + 16 * dt, l16));
         __syncthreads();  // the K tile is read; the ring may be refilled
 
-        // Gathered row r of this item: its (b, t, head) row index into Q, dO and the row terms
-        // (rows past the end read entry 0's first row), and its entry
-        auto row_index = [&](int r, bool& ok) -> int {
-            ok = r < nrows;
-            return ok ? ent_row[r >> gshift] + (r & (G - 1)) : ent_row[0];
-        };
-        // Step j's rows into ring[j % kBwdRing]: wave w loads rows 4w .. 4w+3 of Q and of
+        // Entry value (ent_row) of gathered row r, clamped to the item's last row: rows past
+        // the end read a valid row (their P is 0 through the pad row term below).
+        auto row_entry = [&](int r) -> int { return ent_row[min(r, nrows - 1) >> gshift]; };
+        // Step j's rows into ring[j % kBwdRing]: wave w loads rows 8w .. 8w+7 of Q and of
         // dO, one 16-byte chunk per lane, the swizzle applied through the source chunk;
-        // wave 0 then loads the rows' LSE * log2(e) and D. Every wave issues exactly 2
-        // vector-memory operations here, wave 0 one more.
-        auto issue_step = [&](int j) {
+        // wave 0 then loads the rows' LSE * log2(e) and D. Every wave issues exactly 4
+        // vector-memory operations here, wave 0 one more. `ent` holds row_entry of the
+        // lane's rows (h = 0, 1; then wave 0's row lane & 31), read beforehand.
+        auto issue_step = [&](int j, const int (&ent)[3]) {
             BwdRowStage& R = ring[j % kBwdRing];
-            const int rr = 4 * wave + (lane >> 4);
-            bool ok;
-            const int ri = row_index(j * kBwdRows + rr, ok);
-            const int ch = (lane & 15) ^ rsw(rr);
-            const size_t src = ((size_t)(uint32_t)ri << 7) + ch * 8;
-            __builtin_amdgcn_global_load_lds((const void*)(q + src), (lds_ptr)(R.q + 4 * wave * kDim), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(d_o + src), (lds_ptr)(R.d + 4 * wave * kDim), 16, 0, 0);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int r0 = 8 * wave + 4 * h;
+                const int rr = r0 + (lane >> 4);
+                const int r = min(j * kBwdRows + rr, nrows - 1);
+                const int ri = ent[h] + (r & (G - 1));
+                const int ch = (lane & 15) ^ rsw(rr);
+                const size_t src = ((size_t)(uint32_t)ri << 7) + ch * 8;
+                __builtin_amdgcn_global_load_lds((const void*)(q + src), (lds_ptr)(R.q + r0 * kDim), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void*)(d_o + src), (lds_ptr)(R.d + r0 * kDim), 16, 0, 0);
+            }
             if (wave == 0) {
-                const int ri2 = row_index(j * kBwdRows + (lane & 31), ok);
-                const long long rt2 = ok ? (long long)ri2 : rows;  // padded rows: the pad row
+                const int r = j * kBwdRows + (lane & 31);
+                const long long rt2 = r < nrows ? (long long)(ent[2] + (r & (G - 1))) : rows;  // padding: the pad row
                 __builtin_amdgcn_global_load_lds((const void*)(rowterm + (lane >> 5) * (rows + 1) + rt2),
                                                  (lds_ptr)R.lse, 4, 0, 0);
             }
         };
+        auto read_entries = [&](int j, int (&ent)[3]) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) ent[h] = row_entry(j * kBwdRows + 8 * wave + 4 * h + (lane >> 4));
+            ent[2] = row_entry(j * kBwdRows + (lane & 31));  // used by wave 0
+        };
         // Last key offset of the block that row j*32 + lane attends: its own position when the
         // row's query lies in this block (the causal diagonal), 127 otherwise (padding rows
         // need no limit: their P is 0). diagf[j & 1] says whether any row of step j is diagonal.
-        auto fill_lims = [&](int j) {
+        // `ent` is row_entry of that row (wave 0, lanes < 32), read beforehand.
+        auto fill_lims = [&](int j, int ent) {
             if (wave == 0) {
                 int lim = kBlock - 1;
                 if (lane < kBwdRows) {
                     const int r = j * kBwdRows + lane;
                     if (r < nrows) {
-                        const int t = ent_row[r >> gshift] / Hq - b * N;
+                        const int t = ent / Hq - b * N;
                         if ((t >> 7) == c) lim = t - c * kBlock;
                     }
                     lims[j & 1][lane] = lim;
@@ -293,161 +334,256 @@ __global__ __launch_bounds__(512, 1) void k_bwd_main(
                 if (lane == 0) diagf[j & 1] = m != 0ull;
             }
         };
+        // The LDS reads of a step go in groups of at most eight operations, each issued one
+        // group ahead of the products that use it (the compiler's wait before a use can only
+        // leave 15 later LDS operations in flight).
+        // Row operands of S (Q rows) and dP (dO rows) for row tile mt: rows 16 mt + l16,
+        // dims 32 kk + 8 g4 + e
+        auto load_rows = [&](const BwdRowStage& R, int mt, bf16x8 (&aq)[4], bf16x8 (&ad)[4]) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int o2 = ring_off(16 * mt + l16, 4 * kk + g4);
+                aq[kk] = *(const bf16x8*)(R.q + o2);
+                ad[kk] = *(const bf16x8*)(R.d + o2);
+            }
+        };
+        // The rows' LSE * log2(e), D and causal limits (rows 16 mt + 4 g4 .. +3), and the
+        // diagonal flag of step j
+        struct RowTerms {
+            f32x4 l4[2], d4[2];
+            int4 m4[2];
+            int diag;
+        };
+        auto load_terms = [&](int j, RowTerms& rt) {
+            const BwdRowStage& R = ring[j % kBwdRing];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                rt.l4[mt] = *(const f32x4*)(R.lse + 16 * mt + 4 * g4);
+                rt.d4[mt] = *(const f32x4*)(R.dlt + 16 * mt + 4 * g4);
+                rt.m4[mt] = *(const int4*)(lims[j & 1] + 16 * mt + 4 * g4);
+            }
+            rt.diag = diagf[j & 1];
+        };
+        // B operands of dV, dK for dim tiles n0, n0 + 1: the rows 4 g4 .. +3 and 16 + 4 g4 .. +3
+        // of dO / Q at dim 16 n + l16, read transposed
+        auto load_cols = [&](const BwdRowStage& R, int n0, bf16x8 (&bd)[2], bf16x8 (&bq)[2]) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int c0 = 16 * (n0 + u);
+                bd[u] = cat8(tr_rows4(R.d, 4 * g4, c0, l16), tr_rows4(R.d, 16 + 4 * g4, c0, l16));
+                bq[u] = cat8(tr_rows4(R.q, 4 * g4, c0, l16), tr_rows4(R.q, 16 + 4 * g4, c0, l16));
+            }
+        };
 
         const int ahead = min(kBwdRing - 1, nsteps);
-        for (int j = 0; j < ahead; ++j) issue_step(j);
-        fill_lims(0);
+        int ent[3];
+        for (int j = 0; j < ahead; ++j) {
+            read_entries(j, ent);
+            issue_step(j, ent);
+        }
+        fill_lims(0, row_entry(lane & 31));
         MSA_WAIT_VMCNT(0);
         __syncthreads();
 
+        // step s's row terms, its first row tile's operands, the entries of step s + 3's rows
+        // and of step s + 1's limits are read at the end of step s - 1
+        RowTerms rtm;
+        bf16x8 aq0[4], ad0[4], aq1[4], ad1[4];
+        load_terms(0, rtm);
+        read_entries(ahead, ent);
+        int lim_ent = row_entry(kBwdRows + (lane & 31));
+        load_rows(ring[0], 0, aq0, ad0);
         for (int s = 0; s < nsteps; ++s) {
             const bool more = s + kBwdRing - 1 < nsteps;
-            if (more) issue_step(s + kBwdRing - 1);  // (a)
-            if (s + 1 < nsteps) fill_lims(s + 1);
-
-            // (c) S = Q K^T, dP = dO V^T: 32 rows x this wave's 16 keys;
-            // register 4 mt + i holds row 16 mt + 4 g4 + i, column key my_key
+            if (more) issue_step(s + kBwdRing - 1, ent);  // (a)
+            if (s + 1 < nsteps) fill_lims(s + 1, lim_ent);
             const BwdRowStage& R = ring[s % kBwdRing];
             __bf16* ds_s = dsl[s & 1];
-            f32x4 sa[2], pa[2];
+
+            // (c) S = Q K^T, dP = dO V^T: 32 rows x this wave's 32 keys; for key tile kt,
+            // register 4 mt + i holds row 16 mt + 4 g4 + i, column key kw0 + 16 kt + l16.
+            // Row tile 0's operands were read at the end of the previous step; row tile 1's
+            // are read during tile 0's products, the first dim tiles of (d) during tile 1's.
+            f32x4 sa[2][2], pa[2][2];
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sa[mt][i] = pa[mt][i] = 0.0f;
+                for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                bf16x8 aq[4], ad[4];
+                    for (int i = 0; i < 4; ++i) sa[mt][kt][i] = pa[mt][kt][i] = 0.0f;
+            __builtin_amdgcn_sched_barrier(0);
+            load_rows(R, 1, aq1, ad1);
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int o2 = ring_off(16 * mt + l16, 4 * kk + g4);
-                    aq[kk] = *(const bf16x8*)(R.q + o2);
-                    ad[kk] = *(const bf16x8*)(R.d + o2);
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    sa[0][kt] = mfma16(aq0[kk], kf[kt][kk], sa[0][kt]);
+                    pa[0][kt] = mfma16(ad0[kk], vf[kt][kk], pa[0][kt]);
                 }
-                __builtin_amdgcn_sched_barrier(0);  // all operand loads in flight before the MFMAs
+            interleave_mfma_ds_read<8, 2>();
+            bf16x8 bd0[2], bq0[2];
+            load_cols(R, 0, bd0, bq0);
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    sa[mt] = mfma16(aq[kk], kf[kk], sa[mt]);
-                    pa[mt] = mfma16(ad[kk], vf[kk], pa[mt]);
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    sa[1][kt] = mfma16(aq1[kk], kf[kt][kk], sa[1][kt]);
+                    pa[1][kt] = mfma16(ad1[kk], vf[kt][kk], pa[1][kt]);
                 }
-            }
-            float pv[8];
+            interleave_mfma_ds_read<8, 2>();
+            float pv[2][8];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const f32x4 l4 = *(const f32x4*)(R.lse + 16 * mt + 4 * g4);
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    pv[4 * mt + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[mt][i], scale_log2, -l4[i]));
-            }
-            if (__builtin_amdgcn_readfirstlane(diagf[s & 1])) {  // causal mask on the diagonal rows
+                for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    const int4 m4 = *(const int4*)(lims[s & 1] + 16 * mt + 4 * g4);
-                    if (my_key > m4.x) pv[4 * mt + 0] = 0.0f;
-                    if (my_key > m4.y) pv[4 * mt + 1] = 0.0f;
-                    if (my_key > m4.z) pv[4 * mt + 2] = 0.0f;
-                    if (my_key > m4.w) pv[4 * mt + 3] = 0.0f;
-                }
+                    for (int i = 0; i < 4; ++i)
+                        pv[kt][4 * mt + i] =
+                            __builtin_amdgcn_exp2f(__builtin_fmaf(sa[mt][kt][i], scale_log2, -rtm.l4[mt][i]));
+            if (__builtin_amdgcn_readfirstlane(rtm.diag)) {  // causal mask on the diagonal rows
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt) {
+                        const int my_key = kw0 + 16 * kt + l16;
+                        if (my_key > rtm.m4[mt].x) pv[kt][4 * mt + 0] = 0.0f;
+                        if (my_key > rtm.m4[mt].y) pv[kt][4 * mt + 1] = 0.0f;
+                        if (my_key > rtm.m4[mt].z) pv[kt][4 * mt + 2] = 0.0f;
+                        if (my_key > rtm.m4[mt].w) pv[kt][4 * mt + 3] = 0.0f;
+                    }
             }
             // P^T, dS^T as A operands of dV, dK: k index 8 g4 + e is row 4 g4 + e (e < 4)
             // and row 16 + 4 g4 + e - 4 (e >= 4), exactly the rows this lane holds
-            bf16x8 pb, db;
-            uint32_t dsbits[8];
+            bf16x8 pb[2], db[2];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const f32x4 d4 = *(const f32x4*)(R.dlt + 16 * mt + 4 * g4);
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const __bf16 dsv = (__bf16)(pv[4 * mt + i] * (pa[mt][i] - d4[i]));
-                    pb[4 * mt + i] = (__bf16)pv[4 * mt + i];
-                    db[4 * mt + i] = dsv;
-                    dsbits[4 * mt + i] = (uint32_t)__builtin_bit_cast(uint16_t, dsv);
-                }
-            }
-            store_ds8((uint32_t)(uintptr_t)(lds_ptr)(ds_s + 4 * g4 * kDsRow + my_key), dsbits,
-                      std::make_integer_sequence<int, 8>{});
-            // (d) dV += P^T dO, dK += dS^T Q: own 16 keys x 128 dims; B operands are the rows
-            // 4 g4 .. +3 and 16 + 4 g4 .. +3 of dO / Q at dim 16 nt + l16, read transposed
+                for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                bf16x8 bd[4], bq[4];
+                    for (int i = 0; i < 4; ++i) {
+                        pb[kt][4 * mt + i] = (__bf16)pv[kt][4 * mt + i];
+                        db[kt][4 * mt + i] = (__bf16)(pv[kt][4 * mt + i] * (pa[mt][kt][i] - rtm.d4[mt][i]));
+                    }
+            __builtin_amdgcn_sched_barrier(0);
+            const uint32_t ds_base = (uint32_t)(uintptr_t)(lds_ptr)(ds_s + 4 * g4 * kDsRow + kw0 + l16);
+            store_ds8(ds_base, db[0]);
+            store_ds8(ds_base + 32, db[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            // (d) dV += P^T dO, dK += dS^T Q: own 32 keys x 128 dims, two dim tiles per group,
+            // each group's operands read during the previous group's products
+            auto dkv_group = [&](int n0, const bf16x8 (&bd)[2], const bf16x8 (&bq)[2]) {
 #pragma unroll
-                for (int n4 = 0; n4 < 4; ++n4) {
-                    const int c0 = 16 * (4 * half + n4);
-                    bd[n4] = cat8(tr_rows4(R.d, 4 * g4, c0, l16), tr_rows4(R.d, 16 + 4 * g4, c0, l16));
-                    bq[n4] = cat8(tr_rows4(R.q, 4 * g4, c0, l16), tr_rows4(R.q, 16 + 4 * g4, c0, l16));
-                }
-                __builtin_amdgcn_sched_barrier(0);
+                for (int u = 0; u < 2; ++u)
 #pragma unroll
-                for (int n4 = 0; n4 < 4; ++n4) {
-                    dv[4 * half + n4] = mfma16(pb, bd[n4], dv[4 * half + n4]);
-                    dk[4 * half + n4] = mfma16(db, bq[n4], dk[4 * half + n4]);
-                }
-            }
+                    for (int kt = 0; kt < 2; ++kt) {
+                        dv[kt][n0 + u] = mfma16(pb[kt], bd[u], dv[kt][n0 + u]);
+                        dk[kt][n0 + u] = mfma16(db[kt], bq[u], dk[kt][n0 + u]);
+                    }
+            };
+            bf16x8 bd1[2], bq1[2];
+            load_cols(R, 2, bd1, bq1);
+            dkv_group(0, bd0, bq0);
+            interleave_mfma_ds_read<8, 1>();
+            load_cols(R, 4, bd0, bq0);
+            dkv_group(2, bd1, bq1);
+            interleave_mfma_ds_read<8, 1>();
+            load_cols(R, 6, bd1, bq1);
+            dkv_group(4, bd0, bq0);
+            interleave_mfma_ds_read<8, 1>();
+            dkv_group(6, bd1, bq1);
+            __builtin_amdgcn_sched_barrier(0);
             // (e) step s+1's rows have landed: every memory operation before the loads of steps
             // s+2 and s+3 (issued in the last two (a) phases) is complete; then the barrier makes
-            // all waves' LDS writes visible
-            // Issued after those loads: the loads of (a) of step s-1, the two dQ stores of (f) of
+            // all waves' LDS writes visible.
+            // Issued after those loads: the loads of (a) of step s-1, the four dQ stores of (f) of
             // step s-1, the loads of (a) of step s; they may stay in flight. The empty asm keeps the
             // compiler from sinking any of them below the wait.
             asm volatile("" ::: "memory");
             {
-                const int per = wave == 0 ? 3 : 2;
-                const int after = (s >= 1 && s + kBwdRing - 2 < nsteps ? per : 0) + (s >= 1 ? 2 : 0) + (more ? per : 0);
+                const int per = wave == 0 ? 5 : 4;
+                const int after = (s >= 1 && s + kBwdRing - 2 < nsteps ? per : 0) + (s >= 1 ? 4 : 0) + (more ? per : 0);
                 switch (after) {
                     case 0: MSA_WAIT_VMCNT(0); break;
-                    case 2: MSA_WAIT_VMCNT(2); break;
-                    case 3: MSA_WAIT_VMCNT(3); break;
                     case 4: MSA_WAIT_VMCNT(4); break;
                     case 5: MSA_WAIT_VMCNT(5); break;
-                    case 6: MSA_WAIT_VMCNT(6); break;
-                    case 7: MSA_WAIT_VMCNT(7); break;
-                    default: MSA_WAIT_VMCNT(8); break;
+                    case 8: MSA_WAIT_VMCNT(8); break;
+                    case 9: MSA_WAIT_VMCNT(9); break;
+                    case 12: MSA_WAIT_VMCNT(12); break;
+                    case 14: MSA_WAIT_VMCNT(14); break;
+                    default: MSA_WAIT_VMCNT(0); break;
                 }
             }
             MSA_WAIT_LGKM0();  // this lane's dS stores (not tracked by the compiler) are done
             lds_barrier();
 
-            // (f) dQ^T (unscaled) = K^T dS^T for dims 16 wave .. +15 and the 32 rows;
-            // register i holds dim 16 wave + 4 g4 + i of row 16 rt + l16
+            // (f) dQ^T (unscaled) = K^T dS^T for dims kw0 .. kw0 + 31 and the 32 rows; the next
+            // step's row terms and first row tile (its rows landed before the barrier) are read
+            // during the products
+            bf16x8 bs[2][4];
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                f32x4 qa = {0.0f, 0.0f, 0.0f, 0.0f};
-                bf16x8 bs[4];
+            for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
-                    bs[kk] = *(const bf16x8*)(ds_s + (16 * rt + l16) * kDsRow + 32 * kk + 8 * g4);
-                __builtin_amdgcn_sched_barrier(0);
+                    bs[rt][kk] = *(const bf16x8*)(ds_s + (16 * rt + l16) * kDsRow + 32 * kk + 8 * g4);
+            int rec[2];  // the dQ partial records of this step's rows
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) qa = mfma16(ktf[kk], bs[kk], qa);
-                // chunk-major partial record: [(b*N + t)*top_k + slot][16 chunks][Hq][8 dims]. Rows
-                // past the end store to the sink, so every step issues exactly two stores per lane
-                // and the vmcnt accounting above stays exact.
-                const int r = s * kBwdRows + 16 * rt + l16;
-                const int dim = kw0 + 4 * g4;
-                const int head = g * G + (r & (G - 1));
-                __bf16* dst = r < nrows ? dq_part + ((size_t)ent_rec[r >> gshift] * 16 + (dim >> 3)) * Hq * 8 +
-                                              head * 8 + (dim & 7)
-                                        : dq_sink;
-                bf16x4 w4;
+            for (int rt = 0; rt < 2; ++rt) rec[rt] = ent_rec[min(s * kBwdRows + 16 * rt + l16, nrows - 1) >> gshift];
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 qa[2][2];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) w4[i] = (__bf16)qa[i];
-                __builtin_nontemporal_store(w4, (bf16x4*)dst);  // read once, by k_bwd_dq_sum
-            }
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) qa[rt][dt][i] = 0.0f;
+            // (read unconditionally, so the reads share the products' scheduling region; after the
+            // last step they read stale LDS that is not used)
+            load_rows(ring[(s + 1) % kBwdRing], 0, aq0, ad0);
+            load_terms(s + 1, rtm);
+            read_entries(s + kBwdRing, ent);
+            lim_ent = row_entry((s + 2) * kBwdRows + (lane & 31));
+            // register i of qa[rt][dt] holds dim kw0 + 16 dt + 4 g4 + i of row 16 rt + l16
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int dt = 0; dt < 2; ++dt) qa[rt][dt] = mfma16(ktf[dt][kk], bs[rt][kk], qa[rt][dt]);
+            interleave_mfma_ds_read<16, 1>();
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int dt = 0; dt < 2; ++dt) {
+                    // chunk-major partial record: [(b*N + t)*top_k + slot][16 chunks][Hq][8 dims]. Rows
+                    // past the end store to the sink, so every step issues exactly four stores per lane
+                    // and the vmcnt accounting above stays exact.
+                    const int r = s * kBwdRows + 16 * rt + l16;
+                    const int dim = kw0 + 16 * dt + 4 * g4;
+                    const int head = g * G + (r & (G - 1));
+                    __bf16* dst = r < nrows ? dq_part + ((size_t)rec[rt] * 16 + (dim >> 3)) * Hq * 8 + head * 8 + (dim & 7)
+                                            : dq_sink;
+                    bf16x4 w4;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w4[i] = (__bf16)qa[rt][dt][i];
+                    __builtin_nontemporal_store(w4, (bf16x4*)dst);  // read once, by k_bwd_dq_sum
+                }
         }
 
         // item partials [item][dK, dV][key][dim], fp32; dK carries the softmax scale;
-        // register i of tile nt holds key kw0 + 4 g4 + i, dim 16 nt + l16. Like the dQ
-        // partials they are read once, by a later kernel: nontemporal stores.
+        // register i of tile (kt, nt) holds key kw0 + 16 kt + 4 g4 + i, dim 16 nt + l16. Like
+        // the dQ partials they are read once, by a later kernel: nontemporal stores.
         float* pk = dkv_part + (size_t)item * 2 * kBlock * kDim;
         float* pv2 = pk + (size_t)kBlock * kDim;
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = kw0 + 4 * g4 + i, dim = 16 * nt + l16;
-                __builtin_nontemporal_store(dk[nt][i] * scale, pk + key * kDim + dim);
-                __builtin_nontemporal_store(dv[nt][i], pv2 + key * kDim + dim);
-            }
+            for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = kw0 + 16 * kt + 4 * g4 + i, dim = 16 * nt + l16;
+                    __builtin_nontemporal_store(dk[kt][nt][i] * scale, pk + key * kDim + dim);
+                    __builtin_nontemporal_store(dv[kt][nt][i], pv2 + key * kDim + dim);
+                }
     }
 }
 
@@ -544,7 +680,7 @@ hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const vo
     const int n = d.B * d.Hkv * d.nblk;
     const int grid = device_cu_count();
     const float log2e = 1.4426950408889634f;
-    hipLaunchKernelGGL(k_bwd_main, dim3(grid), dim3(512), 0, stream, (const __bf16*)q, (const __bf16*)k,
+    hipLaunchKernelGGL(k_bwd_main, dim3(grid), dim3(kBwdThreads), 0, stream, (const __bf16*)q, (const __bf16*)k,
                        (const __bf16*)v, (const __bf16*)d_o, ws.rowterm, (long long)d.B * d.N * d.Hq, ws.plan.off,
                        ws.plan.item_off,
                        ws.plan.entries, (__bf16*)ws.dq_part,
