@@ -285,30 +285,42 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
         // Entry value (ent_row) of gathered row r, clamped to the item's last row: rows past
         // the end read a valid row (their P is 0 through the pad row term below).
         auto row_entry = [&](int r) -> int { return ent_row[min(r, nrows - 1) >> gshift]; };
-        // Step j's rows into ring[j % kBwdRing]: wave w loads rows 8w .. 8w+7 of Q and of
-        // dO, one 16-byte chunk per lane, the swizzle applied through the source chunk;
-        // wave 0 then loads the rows' LSE * log2(e) and D. Every wave issues exactly 4
-        // vector-memory operations here, wave 0 one more. `ent` holds row_entry of the
-        // lane's rows (h = 0, 1; then wave 0's row lane & 31), read beforehand.
-        auto issue_step = [&](int j, const int (&ent)[3]) {
-            BwdRowStage& R = ring[j % kBwdRing];
+        // Step j's rows: wave w fetches rows 8w .. 8w+7 of Q and of dO into registers, one
+        // 16-byte chunk per lane, and wave 0 the rows' LSE * log2(e) and D (fetch_step); a
+        // step later they are stored into ring[j % kBwdRing], the swizzle applied on the LDS
+        // side (stash_step). Global->LDS loads are not used here: LDS reads issued after
+        // them wait until they have written LDS. `ent` holds row_entry of the lane's rows
+        // (h = 0, 1; then wave 0's row lane & 31), read beforehand.
+        struct RowFetch {
+            u32x4 q[2], d[2];
+            float term;
+        };
+        auto fetch_step = [&](int j, const int (&ent)[3], RowFetch& f) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int r0 = 8 * wave + 4 * h;
-                const int rr = r0 + (lane >> 4);
+                const int rr = 8 * wave + 4 * h + (lane >> 4);
                 const int r = min(j * kBwdRows + rr, nrows - 1);
                 const int ri = ent[h] + (r & (G - 1));
-                const int ch = (lane & 15) ^ rsw(rr);
-                const size_t src = ((size_t)(uint32_t)ri << 7) + ch * 8;
-                __builtin_amdgcn_global_load_lds((const void*)(q + src), (lds_ptr)(R.q + r0 * kDim), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const void*)(d_o + src), (lds_ptr)(R.d + r0 * kDim), 16, 0, 0);
+                const size_t src = ((size_t)(uint32_t)ri << 7) + (lane & 15) * 8;
+                f.q[h] = *(const u32x4*)(q + src);
+                f.d[h] = *(const u32x4*)(d_o + src);
             }
             if (wave == 0) {
                 const int r = j * kBwdRows + (lane & 31);
                 const long long rt2 = r < nrows ? (long long)(ent[2] + (r & (G - 1))) : rows;  // padding: the pad row
-                __builtin_amdgcn_global_load_lds((const void*)(rowterm + (lane >> 5) * (rows + 1) + rt2),
-                                                 (lds_ptr)R.lse, 4, 0, 0);
+                f.term = rowterm[(lane >> 5) * (rows + 1) + rt2];
             }
+        };
+        auto stash_step = [&](int j, const RowFetch& f) {
+            BwdRowStage& R = ring[j % kBwdRing];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int rr = 8 * wave + 4 * h + (lane >> 4);
+                const int o2 = ring_off(rr, lane & 15);
+                *(u32x4*)(R.q + o2) = f.q[h];
+                *(u32x4*)(R.d + o2) = f.d[h];
+            }
+            if (wave == 0) R.lse[lane] = f.term;  // lse[32] then dlt[32]
         };
         auto read_entries = [&](int j, int (&ent)[3]) {
 #pragma unroll
@@ -375,27 +387,31 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
             }
         };
 
-        const int ahead = min(kBwdRing - 1, nsteps);
+        // Step s + 1's rows are stored at the top of step s, from registers fetched at the top
+        // of step s - 1 (or in the prologue)
         int ent[3];
-        for (int j = 0; j < ahead; ++j) {
-            read_entries(j, ent);
-            issue_step(j, ent);
+        RowFetch rf;
+        read_entries(0, ent);
+        fetch_step(0, ent, rf);
+        stash_step(0, rf);
+        if (nsteps > 1) {
+            read_entries(1, ent);
+            fetch_step(1, ent, rf);
         }
         fill_lims(0, row_entry(lane & 31));
-        MSA_WAIT_VMCNT(0);
         __syncthreads();
 
-        // step s's row terms, its first row tile's operands, the entries of step s + 3's rows
+        // step s's row terms, its first row tile's operands, the entries of step s + 2's rows
         // and of step s + 1's limits are read at the end of step s - 1
         RowTerms rtm;
         bf16x8 aq0[4], ad0[4], aq1[4], ad1[4];
         load_terms(0, rtm);
-        read_entries(ahead, ent);
+        read_entries(2, ent);
         int lim_ent = row_entry(kBwdRows + (lane & 31));
         load_rows(ring[0], 0, aq0, ad0);
         for (int s = 0; s < nsteps; ++s) {
-            const bool more = s + kBwdRing - 1 < nsteps;
-            if (more) issue_step(s + kBwdRing - 1, ent);  // (a)
+            if (s + 1 < nsteps) stash_step(s + 1, rf);  // (a)
+            if (s + 2 < nsteps) fetch_step(s + 2, ent, rf);
             if (s + 1 < nsteps) fill_lims(s + 1, lim_ent);
             const BwdRowStage& R = ring[s % kBwdRing];
             __bf16* ds_s = dsl[s & 1];
@@ -492,27 +508,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
             interleave_mfma_ds_read<8, 1>();
             dkv_group(6, bd1, bq1);
             __builtin_amdgcn_sched_barrier(0);
-            // (e) step s+1's rows have landed: every memory operation before the loads of steps
-            // s+2 and s+3 (issued in the last two (a) phases) is complete; then the barrier makes
-            // all waves' LDS writes visible.
-            // Issued after those loads: the loads of (a) of step s-1, the four dQ stores of (f) of
-            // step s-1, the loads of (a) of step s; they may stay in flight. The empty asm keeps the
-            // compiler from sinking any of them below the wait.
-            asm volatile("" ::: "memory");
-            {
-                const int per = wave == 0 ? 5 : 4;
-                const int after = (s >= 1 && s + kBwdRing - 2 < nsteps ? per : 0) + (s >= 1 ? 4 : 0) + (more ? per : 0);
-                switch (after) {
-                    case 0: MSA_WAIT_VMCNT(0); break;
-                    case 4: MSA_WAIT_VMCNT(4); break;
-                    case 5: MSA_WAIT_VMCNT(5); break;
-                    case 8: MSA_WAIT_VMCNT(8); break;
-                    case 9: MSA_WAIT_VMCNT(9); break;
-                    case 12: MSA_WAIT_VMCNT(12); break;
-                    case 14: MSA_WAIT_VMCNT(14); break;
-                    default: MSA_WAIT_VMCNT(0); break;
-                }
-            }
+            // (e) the barrier makes all waves' LDS writes of this step (dS, step s + 1's rows)
+            // visible
             MSA_WAIT_LGKM0();  // this lane's dS stores (not tracked by the compiler) are done
             lds_barrier();
 
@@ -540,7 +537,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
             // last step they read stale LDS that is not used)
             load_rows(ring[(s + 1) % kBwdRing], 0, aq0, ad0);
             load_terms(s + 1, rtm);
-            read_entries(s + kBwdRing, ent);
+            read_entries(s + 3, ent);  // fetched at the top of step s + 1
             lim_ent = row_entry((s + 2) * kBwdRows + (lane & 31));
             // register i of qa[rt][dt] holds dim kw0 + 16 dt + 4 g4 + i of row 16 rt + l16
 #pragma unroll
