@@ -26,8 +26,8 @@
 //                                                   the row-major tiles with
 //                                                   ds_read_b64_tr_b16)
 //                       dQ^T = K^T dS^T            (all 128 keys, own 16 dims)
-//                     dQ rows go to bf16 per-(t, slot, head) partials (the
-//                     forward's chunk-major record layout); dK, dV to one fp32
+//                     dQ rows go to bf16 per-(t, slot, head) partials, grouped
+//                     by KV head; dK, dV to one fp32
 //                     partial per work item.
 //   k_bwd_dq_sum      dQ = scale * sum of the valid slots' partials, to bf16.
 //   k_bwd_dkdv_reduce dK, dV of each key block = sum of its items' partials, to
@@ -205,8 +205,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
     __shared__ __attribute__((aligned(16))) __bf16 dsl[2][kBwdRows * kDsRow];  // dS [row][key], padded rows
     __shared__ int32_t ent_row[kBwdMaxItemEntries];  // per entry: (b*N + t)*Hq + g*G, the row of its first head
     __shared__ int32_t ent_rec[kBwdMaxItemEntries];  // per entry: (b*N + t)*top_k + slot, its dQ partial record
-    __shared__ __attribute__((aligned(16))) int32_t lims[2][kBwdRows];          // per step: last attended key per row
-    __shared__ int32_t diagf[2];                                                // per step: some row is on the diagonal
+    __shared__ int32_t ent_lim[kBwdMaxItemEntries];  // per entry: last key of the block its query attends
     static_assert(2 * sizeof(BwdRowStage) >= kBlock * kDim * sizeof(__bf16), "K tile must fit in two stages");
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -242,6 +241,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
             const int en = entries[e0 + rt0 * P + i], t = en >> 8;
             ent_row[i] = (b * N + t) * Hq + g * G;
             ent_rec[i] = (b * N + t) * top_k + (en & 255);
+            // the query's own position when it lies in this block (the causal diagonal), else 127
+            ent_lim[i] = (t >> 7) == c ? t - c * kBlock : kBlock - 1;
         }
         // K tile -> LDS (row-major, swizzled through the source chunk): 8 x 4 rows per wave
 #pragma unroll
@@ -327,25 +328,6 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
             for (int h = 0; h < 2; ++h) ent[h] = row_entry(j * kBwdRows + 8 * wave + 4 * h + (lane >> 4));
             ent[2] = row_entry(j * kBwdRows + (lane & 31));  // used by wave 0
         };
-        // Last key offset of the block that row j*32 + lane attends: its own position when the
-        // row's query lies in this block (the causal diagonal), 127 otherwise (padding rows
-        // need no limit: their P is 0). diagf[j & 1] says whether any row of step j is diagonal.
-        // `ent` is row_entry of that row (wave 0, lanes < 32), read beforehand.
-        auto fill_lims = [&](int j, int ent) {
-            if (wave == 0) {
-                int lim = kBlock - 1;
-                if (lane < kBwdRows) {
-                    const int r = j * kBwdRows + lane;
-                    if (r < nrows) {
-                        const int t = ent / Hq - b * N;
-                        if ((t >> 7) == c) lim = t - c * kBlock;
-                    }
-                    lims[j & 1][lane] = lim;
-                }
-                const uint64_t m = __ballot(lim < kBlock - 1);
-                if (lane == 0) diagf[j & 1] = m != 0ull;
-            }
-        };
         // The LDS reads of a step go in groups of at most eight operations, each issued one
         // group ahead of the products that use it (the compiler's wait before a use can only
         // leave 15 later LDS operations in flight).
@@ -359,12 +341,11 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
                 ad[kk] = *(const bf16x8*)(R.d + o2);
             }
         };
-        // The rows' LSE * log2(e), D and causal limits (rows 16 mt + 4 g4 .. +3), and the
-        // diagonal flag of step j
+        // The rows' LSE * log2(e), D and causal limits (rows 16 mt + 4 g4 .. +3) of step j;
+        // padding rows take the last entry's limit (their P is 0 anyway)
         struct RowTerms {
             f32x4 l4[2], d4[2];
-            int4 m4[2];
-            int diag;
+            int lim[2][4];
         };
         auto load_terms = [&](int j, RowTerms& rt) {
             const BwdRowStage& R = ring[j % kBwdRing];
@@ -372,9 +353,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
             for (int mt = 0; mt < 2; ++mt) {
                 rt.l4[mt] = *(const f32x4*)(R.lse + 16 * mt + 4 * g4);
                 rt.d4[mt] = *(const f32x4*)(R.dlt + 16 * mt + 4 * g4);
-                rt.m4[mt] = *(const int4*)(lims[j & 1] + 16 * mt + 4 * g4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) rt.lim[mt][i] = ent_lim[min(j * kBwdRows + 16 * mt + 4 * g4 + i, nrows - 1) >> gshift];
             }
-            rt.diag = diagf[j & 1];
         };
         // B operands of dV, dK for dim tiles n0, n0 + 1: the rows 4 g4 .. +3 and 16 + 4 g4 .. +3
         // of dO / Q at dim 16 n + l16, read transposed
@@ -387,8 +368,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
             }
         };
 
-        // Step s + 1's rows are stored at the top of step s, from registers fetched at the top
-        // of step s - 1 (or in the prologue)
+        // Step s + 1's rows are stored late in step s (before its barrier), from registers
+        // fetched at the same point of step s - 1 (or in the prologue)
         int ent[3];
         RowFetch rf;
         read_entries(0, ent);
@@ -398,7 +379,6 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
             read_entries(1, ent);
             fetch_step(1, ent, rf);
         }
-        fill_lims(0, row_entry(lane & 31));
         __syncthreads();
 
         // step s's row terms, its first row tile's operands, the entries of step s + 2's rows
@@ -407,12 +387,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
         bf16x8 aq0[4], ad0[4], aq1[4], ad1[4];
         load_terms(0, rtm);
         read_entries(2, ent);
-        int lim_ent = row_entry(kBwdRows + (lane & 31));
         load_rows(ring[0], 0, aq0, ad0);
         for (int s = 0; s < nsteps; ++s) {
-            if (s + 1 < nsteps) stash_step(s + 1, rf);  // (a)
-            if (s + 2 < nsteps) fetch_step(s + 2, ent, rf);
-            if (s + 1 < nsteps) fill_lims(s + 1, lim_ent);
             const BwdRowStage& R = ring[s % kBwdRing];
             __bf16* ds_s = dsl[s & 1];
 
@@ -456,17 +432,20 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
                     for (int i = 0; i < 4; ++i)
                         pv[kt][4 * mt + i] =
                             __builtin_amdgcn_exp2f(__builtin_fmaf(sa[mt][kt][i], scale_log2, -rtm.l4[mt][i]));
-            if (__builtin_amdgcn_readfirstlane(rtm.diag)) {  // causal mask on the diagonal rows
+            // causal mask, only where some row of this wave's lanes lies on the diagonal
+            bool diag = false;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) diag |= rtm.lim[mt][i] < kBlock - 1;
+            if (__ballot(diag) != 0ull) {
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                    for (int kt = 0; kt < 2; ++kt) {
-                        const int my_key = kw0 + 16 * kt + l16;
-                        if (my_key > rtm.m4[mt].x) pv[kt][4 * mt + 0] = 0.0f;
-                        if (my_key > rtm.m4[mt].y) pv[kt][4 * mt + 1] = 0.0f;
-                        if (my_key > rtm.m4[mt].z) pv[kt][4 * mt + 2] = 0.0f;
-                        if (my_key > rtm.m4[mt].w) pv[kt][4 * mt + 3] = 0.0f;
-                    }
+                    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (kw0 + 16 * kt + l16 > rtm.lim[mt][i]) pv[kt][4 * mt + i] = 0.0f;
             }
             // P^T, dS^T as A operands of dV, dK: k index 8 g4 + e is row 4 g4 + e (e < 4)
             // and row 16 + 4 g4 + e - 4 (e >= 4), exactly the rows this lane holds
@@ -508,6 +487,10 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
             interleave_mfma_ds_read<8, 1>();
             dkv_group(6, bd1, bq1);
             __builtin_amdgcn_sched_barrier(0);
+            // (a) step s + 1's rows (fetched a step ago) into LDS, then step s + 2's fetched: late
+            // in the step, so the wait for the fetch also finds the previous step's dQ stores done
+            if (s + 1 < nsteps) stash_step(s + 1, rf);
+            if (s + 2 < nsteps) fetch_step(s + 2, ent, rf);
             // (e) the barrier makes all waves' LDS writes of this step (dS, step s + 1's rows)
             // visible
             MSA_WAIT_LGKM0();  // this lane's dS stores (not tracked by the compiler) are done
@@ -537,8 +520,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
             // last step they read stale LDS that is not used)
             load_rows(ring[(s + 1) % kBwdRing], 0, aq0, ad0);
             load_terms(s + 1, rtm);
-            read_entries(s + 3, ent);  // fetched at the top of step s + 1
-            lim_ent = row_entry((s + 2) * kBwdRows + (lane & 31));
+            read_entries(s + 3, ent);  // fetched late in step s + 1
             // register i of qa[rt][dt] holds dim kw0 + 16 dt + 4 g4 + i of row 16 rt + l16
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
@@ -551,13 +533,13 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                 for (int dt = 0; dt < 2; ++dt) {
-                    // chunk-major partial record: [(b*N + t)*top_k + slot][16 chunks][Hq][8 dims]. Rows
-                    // past the end store to the sink, so every step issues exactly four stores per lane
-                    // and the vmcnt accounting above stays exact.
+                    // partial record [(b*N + t)*top_k + slot][KV head][16 chunks][G heads][8 dims]: the
+                    // four entries of a store each get two whole 128-byte lines (chunks 2i, 2i+1 of
+                    // their group's heads). Rows past the end store to the sink.
                     const int r = s * kBwdRows + 16 * rt + l16;
                     const int dim = kw0 + 16 * dt + 4 * g4;
-                    const int head = g * G + (r & (G - 1));
-                    __bf16* dst = r < nrows ? dq_part + ((size_t)rec[rt] * 16 + (dim >> 3)) * Hq * 8 + head * 8 + (dim & 7)
+                    __bf16* dst = r < nrows ? dq_part + ((((size_t)rec[rt] * Hkv + g) * 16 + (dim >> 3)) * G +
+                                                         (r & (G - 1))) * 8 + (dim & 7)
                                             : dq_sink;
                     bf16x4 w4;
 #pragma unroll
@@ -586,7 +568,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
 
 // ---------------------------------------------------------------------------
 // dQ[b, t, h] = scale * sum over the valid slots of the partials; one workgroup per (b, t).
-// A thread takes (chunk, head) pairs, so the reads of one slot's record are contiguous.
+// Thread j takes the 8 dims at j * 8 of each record ([KV head][chunk][head in group][8]),
+// so the reads of one slot's record are contiguous.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_bwd_dq_sum(const __bf16* __restrict__ dq_part,
                                                     const int32_t* __restrict__ block_idx, __bf16* __restrict__ dq,
@@ -601,9 +584,10 @@ __global__ __launch_bounds__(256) void k_bwd_dq_sum(const __bf16* __restrict__ d
     __syncthreads();
     const size_t slot_stride = (size_t)16 * Hq * 8;
     const __bf16* base = dq_part + (size_t)bt * top_k * slot_stride;
+    const int G = 1 << gshift;
     for (int j = tid; j < Hq * 16; j += 256) {
-        const int chunk = j / Hq, head = j - chunk * Hq;
-        const int32_t* sg = sel + (head >> gshift) * top_k;
+        const int g = j >> (gshift + 4), chunk = (j >> gshift) & 15, head = g * G + (j & (G - 1));
+        const int32_t* sg = sel + g * top_k;
         float acc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
