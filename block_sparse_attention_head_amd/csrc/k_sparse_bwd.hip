@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
     __shared__ __attribute__((aligned(16))) BwdRowStage ring[kBwdRing];         // also holds the K tile at item start
     __shared__ __attribute__((aligned(16))) __bf16 dsl[2][kBwdRows * kDsRow];  // dS [row][key], padded rows
     __shared__ int32_t ent_row[kBwdMaxItemEntries];  // per entry: (b*N + t)*Hq + g*G, the row of its first head
-    __shared__ int32_t ent_rec[kBwdMaxItemEntries];  // per entry: (b*N + t)*top_k + slot, its dQ partial record
+    __shared__ uint32_t ent_rec[kBwdMaxItemEntries];  // per entry: its dQ partial record times Hkv, plus g
     __shared__ int32_t ent_lim[kBwdMaxItemEntries];  // per entry: last key of the block its query attends
     static_assert(2 * sizeof(BwdRowStage) >= kBlock * kDim * sizeof(__bf16), "K tile must fit in two stages");
 
@@ -214,6 +214,14 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
     const int G = 1 << gshift;
     const int P = kBlock >> gshift;
     const int kw0 = kBwdKeysPerWave * wave;  // this wave's first key (and first dQ dim)
+    // within a (record, KV head) dQ partial: dims kw0 + 16 dt + 4 g4 .. +3 of head l16 % G (the
+    // head's multiple of 16, for G > 16, is added per step)
+    int dq_lane[2];
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+        const int dim = kw0 + 16 * dt + 4 * g4;
+        dq_lane[dt] = (((dim >> 3) << gshift) + (l16 & ((1 << gshift) - 1))) * 8 + (dim & 7);
+    }
     const int total_items = item_off[n_tiles];
     __bf16* ktile = ring[0].q;  // K [key][dim] during the item prologue
 
@@ -240,7 +248,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
         for (int i = tid; i < ne; i += kBwdThreads) {
             const int en = entries[e0 + rt0 * P + i], t = en >> 8;
             ent_row[i] = (b * N + t) * Hq + g * G;
-            ent_rec[i] = (b * N + t) * top_k + (en & 255);
+            ent_rec[i] = (uint32_t)((b * N + t) * top_k + (en & 255)) * (uint32_t)Hkv + (uint32_t)g;
             // the query's own position when it lies in this block (the causal diagonal), else 127
             ent_lim[i] = (t >> 7) == c ? t - c * kBlock : kBlock - 1;
         }
@@ -505,7 +513,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
                     bs[rt][kk] = *(const bf16x8*)(ds_s + (16 * rt + l16) * kDsRow + 32 * kk + 8 * g4);
-            int rec[2];  // the dQ partial records of this step's rows
+            uint32_t rec[2];  // the dQ partial records (times Hkv, plus g) of this step's rows
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) rec[rt] = ent_rec[min(s * kBwdRows + 16 * rt + l16, nrows - 1) >> gshift];
             __builtin_amdgcn_sched_barrier(0);
@@ -535,11 +543,11 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
                 for (int dt = 0; dt < 2; ++dt) {
                     // partial record [(b*N + t)*top_k + slot][KV head][16 chunks][G heads][8 dims]: the
                     // four entries of a store each get two whole 128-byte lines (chunks 2i, 2i+1 of
-                    // their group's heads). Rows past the end store to the sink.
+                    // their group's heads). Rows past the end store to the sink. Below the (record,
+                    // KV head) pair the offset is the lane's, plus the head's multiple of 16 (G > 16).
                     const int r = s * kBwdRows + 16 * rt + l16;
-                    const int dim = kw0 + 16 * dt + 4 * g4;
-                    __bf16* dst = r < nrows ? dq_part + ((((size_t)rec[rt] * Hkv + g) * 16 + (dim >> 3)) * G +
-                                                         (r & (G - 1))) * 8 + (dim & 7)
+                    const int hx = (s * kBwdRows + 16 * rt) & (G - 1) & ~15;
+                    __bf16* dst = r < nrows ? dq_part + ((size_t)rec[rt] << (7 + gshift)) + dq_lane[dt] + hx * 8
                                             : dq_sink;
                     bf16x4 w4;
 #pragma unroll
