@@ -556,21 +556,20 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(
                 }
         }
 
-        // item partials [item][dK, dV][key][dim], fp32; dK carries the softmax scale;
-        // register i of tile (kt, nt) holds key kw0 + 16 kt + 4 g4 + i, dim 16 nt + l16. Like
-        // the dQ partials they are read once, by a later kernel: nontemporal stores.
+        // item partials [item][dK, dV][key / 4][dim][key % 4], fp32; dK carries the softmax
+        // scale. Tile (kt, nt) holds keys kw0 + 16 kt + 4 g4 .. +3 (its four registers) of dim
+        // 16 nt + l16: one 16-byte store, and 16 lanes cover 256 contiguous bytes. Like the dQ
+        // partials they are read once, by a later kernel: nontemporal stores.
         float* pk = dkv_part + (size_t)item * 2 * kBlock * kDim;
         float* pv2 = pk + (size_t)kBlock * kDim;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = kw0 + 16 * kt + 4 * g4 + i, dim = 16 * nt + l16;
-                    __builtin_nontemporal_store(dk[kt][nt][i] * scale, pk + key * kDim + dim);
-                    __builtin_nontemporal_store(dv[kt][nt][i], pv2 + key * kDim + dim);
-                }
+            for (int nt = 0; nt < 8; ++nt) {
+                const int o = (((kw0 + 16 * kt + 4 * g4) >> 2) * kDim + 16 * nt + l16) * 4;
+                __builtin_nontemporal_store(dk[kt][nt] * scale, (f32x4*)(pk + o));
+                __builtin_nontemporal_store(dv[kt][nt], (f32x4*)(pv2 + o));
+            }
     }
 }
 
@@ -624,7 +623,8 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv_reduce(const float* __restrict
     const int c = tile % nblk, bg = tile / nblk, g = bg % Hkv, b = bg / Hkv;
     const int i0 = item_off[tile], i1 = item_off[tile + 1];
     const size_t part = (size_t)kBlock * kDim;
-    // a quarter of the block's values per workgroup (blockIdx.y), 4 elements per unit
+    // a quarter of the block's values per workgroup (blockIdx.y), 4 elements per unit; the
+    // partials are [key / 4][dim][key % 4], so unit e is the 16 bytes at e * 4
     const int e_end = (blockIdx.y + 1) * (kBlock * kDim / 16);
     for (int e = blockIdx.y * (kBlock * kDim / 16) + threadIdx.x; e < e_end; e += 256) {
         f32x4 ak = {0.0f, 0.0f, 0.0f, 0.0f}, av = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -632,16 +632,16 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv_reduce(const float* __restrict
             ak += __builtin_nontemporal_load((const f32x4*)(dkv_part + (size_t)it * 2 * part + e * 4));
             av += __builtin_nontemporal_load((const f32x4*)(dkv_part + (size_t)it * 2 * part + part + e * 4));
         }
-        const int key = (e * 4) / kDim, dim = (e * 4) % kDim;
-        const size_t o = (((size_t)b * N + (size_t)c * kBlock + key) * Hkv + g) * kDim + dim;
-        bf16x4 wk, wv;
+        // unit e holds keys 4 (e / 128) .. +3 of dim e % 128; consecutive threads write
+        // consecutive dims of one key
+        const int key0 = 4 * (e / kDim), dim = e % kDim;
+        const size_t o = (((size_t)b * N + (size_t)c * kBlock + key0) * Hkv + g) * kDim + dim;
+        const size_t key_stride = (size_t)Hkv * kDim;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            wk[u] = (__bf16)ak[u];
-            wv[u] = (__bf16)av[u];
+            dk[o + u * key_stride] = (__bf16)ak[u];
+            dv[o + u * key_stride] = (__bf16)av[u];
         }
-        *(bf16x4*)(dk + o) = wk;
-        *(bf16x4*)(dv + o) = wv;
     }
 }
 
