@@ -13,22 +13,21 @@
 //
 // Kernels:
 //   k_bwd_delta       per (b, t, h) row: D and LSE * log2(e).
-//   k_bwd_main        one persistent workgroup of 8 waves per CU walks the
-//                     work items (a chunk of the rows gathered for one
-//                     (key block, KV head) tile). Wave w owns keys 16w .. 16w+15
-//                     of the block and keeps their K, V as MFMA operands in
-//                     registers (16x16x32 bf16 MFMA throughout). Per 32
-//                     gathered rows (a "step", staged row-major in an LDS ring
-//                     by global->LDS loads three steps ahead):
+//   k_bwd_main        one persistent workgroup of 4 waves (one per SIMD) per
+//                     CU walks the work items (a chunk of the rows gathered
+//                     for one (key block, KV head) tile). Wave w owns keys
+//                     32w .. 32w+31 of the block and keeps their K, V as MFMA
+//                     operands in registers (16x16x32 bf16 MFMA throughout).
+//                     Per 32 gathered rows (a "step", fetched into registers a
+//                     step ahead and stored row-major into an LDS ring):
 //                       S = Q K^T, dP = dO V^T    (rows x own keys)
 //                       P, dS                      (bf16, dS also into LDS)
 //                       dV += P^T dO, dK += dS^T Q (transposed operands read from
 //                                                   the row-major tiles with
 //                                                   ds_read_b64_tr_b16)
-//                       dQ^T = K^T dS^T            (all 128 keys, own 16 dims)
+//                       dQ^T = K^T dS^T            (all 128 keys, own 32 dims)
 //                     dQ rows go to bf16 per-(t, slot, head) partials, grouped
-//                     by KV head; dK, dV to one fp32
-//                     partial per work item.
+//                     by KV head; dK, dV to one fp32 partial per work item.
 //   k_bwd_dq_sum      dQ = scale * sum of the valid slots' partials, to bf16.
 //   k_bwd_dkdv_reduce dK, dV of each key block = sum of its items' partials, to
 //                     bf16 (zero for blocks no query selected).
@@ -82,20 +81,22 @@ __global__ __launch_bounds__(256) void k_bwd_delta(const __bf16* __restrict__ o,
 // ---------------------------------------------------------------------------
 // Fused main backward.
 //
-// One workgroup of 8 waves (two per SIMD) per work item; wave w owns keys
-// 16w .. 16w+15 of the block, keeps their K and V rows as MFMA operands in
-// registers, and accumulates their dK, dV. The block's K tile is staged
-// row-major in LDS once per item and each wave reads its K^T fragments (A
-// operands of dQ^T for dims 16w .. 16w+15) from it with transposing LDS loads.
-// Gathered rows go 32 at a time ("steps") through a ring of kBwdRing row-major
-// LDS stages filled by direct global->LDS loads issued kBwdRing - 1 steps
-// ahead (no registers held while they fly). Step s:
-//   (a) issue the loads of step s+3
-//   (c) S = Q K^T, dP = dO V^T (32 rows x 16 keys); P, dS (dS -> LDS)
+// One workgroup of 4 waves (one per SIMD, up to 512 registers each) per work
+// item; wave w owns keys 32w .. 32w+31 of the block, keeps their K and V rows
+// as MFMA operands in registers, and accumulates their dK, dV. Each wave reads
+// the gathered rows once for its 32 keys, half the LDS traffic per key of 16.
+// The block's K tile is staged row-major in LDS once per item and each wave
+// reads its K^T fragments (A operands of dQ^T for dims 32w .. 32w+31) from it
+// with transposing LDS loads. Gathered rows go 32 at a time ("steps"): step
+// j's rows are fetched into registers late in step j - 2 and stored into
+// ring[j % kBwdRing] late in step j - 1, before its barrier. Step s:
+//   (c) S = Q K^T, dP = dO V^T (32 rows x 32 keys); P, dS (dS -> LDS)
 //   (d) dV += P^T dO, dK += dS^T Q, with dO^T, Q^T read transposed from the stage
-//   (e) wait for step s+1's loads; barrier
-//   (f) dQ^T (16 dims x 32 rows) = K^T dS^T over the block's 128 keys -> partials
-// All MFMAs are 16x16x32.
+//   (a) store step s+1's rows into the ring, fetch step s+2's into registers
+//   (e) barrier
+//   (f) dQ^T (32 dims x 32 rows) = K^T dS^T over the block's 128 keys -> partials
+// The LDS reads of each group of products are issued during the previous
+// group's products. All MFMAs are 16x16x32.
 // ---------------------------------------------------------------------------
 constexpr int kBwdRows = 32;                                   // gathered rows per step
 constexpr int kBwdRing = 4;                                    // row-major stages
@@ -106,7 +107,7 @@ constexpr int kBwdMaxItemEntries = kRowTilesPerItem * kBlock;  // entries of one
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(3))) bf16x4* lds_bf16x4_ptr;
 
-// Row-major tiles with 128-element rows filled by global->LDS loads: chunk ch
+// Row-major tiles with 128-element rows: chunk ch
 // (8 elements) of row r sits at chunk slot ch ^ rsw(r), rsw(r) = x ^ (2x & 14)
 // for x = r & 15 (a bijection of 0..15). Chosen by measuring both read patterns
 // of this kernel on the device, eight waves per CU: the 16-byte operand loads
@@ -120,7 +121,7 @@ __device__ __forceinline__ int ring_off(int row, int ch) { return row * kDim + (
 // four banks, and every offset is a per-lane base plus a constant.
 constexpr int kDsRow = kBlock + 8;
 
-struct BwdRowStage {             // written by global->LDS loads
+struct BwdRowStage {             // one step's gathered rows
     __bf16 q[kBwdRows * kDim];   // Q rows [row][dim] (ring_off)
     __bf16 d[kBwdRows * kDim];   // dO rows
     float lse[kBwdRows];         // LSE * log2(e) of the row (+inf for padding rows)
