@@ -34,15 +34,16 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // Stage key block c into LDS buffer `dst` with direct global->LDS loads.
 // Instruction i of wave w fills 16-byte slots p = (4i + w) * 64 + lane, i.e.
-// row p / 16, stored chunk p % 16, which holds logical chunk (p % 16) ^ (row % 16).
+// row p / 16 = 16i + 4w + lane / 16, stored chunk p % 16, which holds logical chunk
+// (p % 16) ^ (row % 16); row % 16 does not depend on i, so one per-lane offset
+// (32-bit) serves all eight loads. `wave` is wave-uniform (a scalar register).
 __device__ __forceinline__ void stage_key_block(const __bf16* __restrict__ src, __bf16* dst, int wave, int lane) {
+    const int row0 = 4 * wave + (lane >> 4);
+    const uint32_t lane_off = (uint32_t)(row0 * kDim + (((lane & 15) ^ (row0 & 15)) * 8));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int p = (i * 4 + wave) * 64 + lane;
-        const int row = p >> 4, logical = (p & 15) ^ (row & 15);
-        __builtin_amdgcn_global_load_lds((const void*)(src + row * kDim + logical * 8),
+    for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(src + lane_off + i * 16 * kDim),
                                          (lds_ptr)(dst + (i * 4 + wave) * 64 * 8), 16, 0, 0);
-    }
 }
 
 // B operand (Q^T) of a wave: lane holds row (r0 + wave*64 + nt*32 + l32), dims kk*16 + 8h .. +7;
@@ -66,45 +67,69 @@ __device__ __forceinline__ void load_q_rows(const __bf16* __restrict__ qb, int r
 }
 
 // Max score of this lane's row (row tile h of the wave) over the visible keys of key
-// block c, staged in LDS at kt.
-__device__ __forceinline__ float block_row_max(const __bf16* kt, const bf16x8 (&qf)[2][8], const int (&trow)[2],
-                                               int c, int h, int l32) {
-    const bool diag0 = (trow[0] >> 7) == c, diag1 = (trow[1] >> 7) == c;
-    const bool any_diag = __any(diag0 || diag1);
-    // key = mt*32 + 8*(i/4) + 4h + i%4 <= lim  <=>  mt*32 + 8*(i/4) + i%4 <= lim - 4h,
-    // so every comparison is against a compile-time constant
-    const int lim0 = (diag0 ? trow[0] - c * kBlock : kBlock - 1) - 4 * h;
-    const int lim1 = (diag1 ? trow[1] - c * kBlock : kBlock - 1) - 4 * h;
+// block c, staged in LDS at kt. DIAG: some row of the wave lies in block c (the causal
+// diagonal), so keys past a row's own position are masked; lim0, lim1 are those
+// positions minus 4h (key = mt*32 + 8*(i/4) + 4h + i%4 <= lim <=> mt*32 + 8*(i/4) + i%4
+// <= lim - 4h, so every comparison is against a compile-time constant).
+// The four 32-key M tiles are software-pipelined: tile mt's products are issued while
+// tile mt - 1's accumulators are reduced (two accumulator sets). The common, unmasked
+// path has no branch, so the reductions interleave with the matrix instructions.
+template <bool DIAG>
+__device__ __forceinline__ float block_row_max_t(const __bf16* kt, const bf16x8 (&qf)[2][8], int lim0, int lim1,
+                                                 int h, int l32) {
     float m0 = -INFINITY, m1 = -INFINITY;
+    f32x16 acc[2][2];
+    auto products = [&](int mt, f32x16 (&a)[2]) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {  // one 32-key M tile at a time keeps the accumulators small
-        f32x16 acc0, acc1;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.0f;
+        for (int i = 0; i < 16; ++i) a[0][i] = a[1][i] = 0.0f;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-            const bf16x8 a = *(const bf16x8*)(kt + swz_chunk_offset(mt * 32 + l32, 2 * kk + h));
-            acc0 = mfma32(a, qf[0][kk], acc0);
-            acc1 = mfma32(a, qf[1][kk], acc1);
+            const bf16x8 k8 = *(const bf16x8*)(kt + swz_chunk_offset(mt * 32 + l32, 2 * kk + h));
+            a[0] = mfma32(k8, qf[0][kk], a[0]);
+            a[1] = mfma32(k8, qf[1][kk], a[1]);
         }
-        if (any_diag) {  // the query's own block: keep keys j <= t only
+    };
+    auto reduce = [&](int mt, const f32x16 (&a)[2]) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 16; ++i) {
+            if (DIAG) {
                 const int key_h0 = mt * 32 + mfma32_row(i, 0);
-                if (key_h0 <= lim0) m0 = fmaxf(m0, acc0[i]);
-                if (key_h0 <= lim1) m1 = fmaxf(m1, acc1[i]);
+                if (key_h0 <= lim0) m0 = fmaxf(m0, a[0][i]);
+                if (key_h0 <= lim1) m1 = fmaxf(m1, a[1][i]);
+            } else {
+                m0 = fmaxf(m0, a[0][i]);
+                m1 = fmaxf(m1, a[1][i]);
             }
-        } else {
+        }
+    };
+    products(0, acc[0]);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                m0 = fmaxf(m0, acc0[i]);
-                m1 = fmaxf(m1, acc1[i]);
+    for (int mt = 1; mt < 4; ++mt) {
+        products(mt, acc[mt & 1]);
+        reduce(mt - 1, acc[(mt - 1) & 1]);
+        if (!DIAG) {
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // an operand read
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two products
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two max steps
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
+    reduce(3, acc[1]);
     m0 = wave_max_xor32(m0);
     m1 = wave_max_xor32(m1);
     return h ? m1 : m0;  // after the exchange lane-half h owns row tile h
+}
+
+__device__ __forceinline__ float block_row_max(const __bf16* kt, const bf16x8 (&qf)[2][8], const int (&trow)[2],
+                                               int c, int h, int l32) {
+    const bool diag0 = (trow[0] >> 7) == c, diag1 = (trow[1] >> 7) == c;
+    const int lim0 = (diag0 ? trow[0] - c * kBlock : kBlock - 1) - 4 * h;
+    const int lim1 = (diag1 ? trow[1] - c * kBlock : kBlock - 1) - 4 * h;
+    return __any(diag0 || diag1) ? block_row_max_t<true>(kt, qf, lim0, lim1, h, l32)
+                                 : block_row_max_t<false>(kt, qf, lim0, lim1, h, l32);
 }
 
 __global__ __launch_bounds__(256, 2) void k_index_pool(const __bf16* __restrict__ q_idx,
@@ -121,7 +146,8 @@ __global__ __launch_bounds__(256, 2) void k_index_pool(const __bf16* __restrict_
 
     __shared__ __attribute__((aligned(16))) __bf16 ks[2][kBlock * kDim];  // double-buffered key block
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const __bf16* qb = q_idx + (size_t)b * R * kDim;
     const __bf16* kb = k_idx + (size_t)b * N * kDim;
 
@@ -187,7 +213,8 @@ __global__ __launch_bounds__(256, 2) void k_index_topk(const __bf16* __restrict_
 
     __shared__ __attribute__((aligned(16))) __bf16 ks[2][kBlock * kDim];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const __bf16* qb = q_idx + (size_t)b * R * kDim;
     const __bf16* kb = k_idx + (size_t)b * N * kDim;
 
