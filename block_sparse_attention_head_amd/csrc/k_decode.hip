@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void k_dec_index(const __bf16* __restrict__ q_
                 if (16 * mt + 4 * q4 + i <= rmax) m = fmaxf(m, acc[i]);
         }
         m = fmaxf(m, __shfl_xor(m, 16, 64));
-        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        m = wave_max_xor32(m);
         if (q4 == 0 && h < H) prow[(size_t)h * nblk] = m;
     }
 }
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(64 * NW) void k_dec_attn(const __bf16* __restrict__
                 mb = fmaxf(mb, sv);
             }
         mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-        mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+        mb = wave_max_xor32(mb);
         const float m_new = fmaxf(m_run, mb);  // finite: key kbase <= t is valid
         const float alpha = exp2f(m_run - m_new);
         float ps = 0.0f;
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(64 * NW) void k_dec_attn(const __bf16* __restrict__
                 pa[4 * mt + i] = (__bf16)p;
             }
         ps += __shfl_xor(ps, 16, 64);
-        ps += __shfl_xor(ps, 32, 64);
+        ps = wave_sum_xor32(ps);
         l_run = l_run * alpha + ps;
         m_run = m_new;
 #pragma unroll

@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void k_kl_lse_part(
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) l += __builtin_amdgcn_exp2f(zacc[mt][i] - m);
-            l += __shfl_xor(l, 32, 64);
+            l = wave_sum_xor32(l);
             if (valid && h == 0)
                 lse_part[(((size_t)b * Hkv + g) * N + t) * top_k + (en & 255)] = make_float2(m, l);
         }

@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_partial(
                     l += pv;
                     pf[mt * 2 + half][e] = (__bf16)pv;
                 }
-        l += __shfl_xor(l, 32, 64);
+        l = wave_sum_xor32(l);
         const float inv = 1.0f / l;
         // partial O record layout: [(b*Nc + t - p0)*top_k + slot][chunk][head][8 dims], chunk = h*8 + dt*2 + i0/8
         const size_t rec2 = ((size_t)b * Nc + (ri.t - p0)) * top_k + ri.slot;

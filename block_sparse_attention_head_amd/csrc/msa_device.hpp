@@ -59,7 +59,17 @@ __device__ __forceinline__ int key_block(uint64_t key) {
     return (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
 }
 
-__device__ __forceinline__ float wave_max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
+// max(x[l], x[l ^ 32]) in every lane l. v_permlane32_swap gives lane l the values of lanes
+// l % 32 and l % 32 + 32 (checked on the device), so no LDS round trip is needed.
+__device__ __forceinline__ float wave_max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// x[l] + x[l ^ 32] in every lane l (the two addends in the same order in both lanes of a pair).
+__device__ __forceinline__ float wave_sum_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
     uint32_t lo = __shfl_xor((uint32_t)x, m, 64);
