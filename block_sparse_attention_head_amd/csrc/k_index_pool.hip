@@ -32,19 +32,35 @@ constexpr int kStreamCap = 16;     // list length of the single-pass selection: 
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// Stage key block c into LDS buffer `dst` with direct global->LDS loads.
-// Instruction i of wave w fills 16-byte slots p = (4i + w) * 64 + lane, i.e.
-// row p / 16 = 16i + 4w + lane / 16, stored chunk p % 16, which holds logical chunk
-// (p % 16) ^ (row % 16); row % 16 does not depend on i, so one per-lane offset
-// (32-bit) serves all eight loads. `wave` is wave-uniform (a scalar register).
-__device__ __forceinline__ void stage_key_block(const __bf16* __restrict__ src, __bf16* dst, int wave, int lane) {
-    const int row0 = 4 * wave + (lane >> 4);
-    const uint32_t lane_off = (uint32_t)(row0 * kDim + (((lane & 15) ^ (row0 & 15)) * 8));
+// Buffer resource word 3 for raw 32-bit accesses on gfx9-family targets.
+constexpr int kIdxRawBufferWord3 = 0x00020000;
+
+// Staging of a key block into an LDS buffer with buffer loads straight to LDS,
+// eight per wave. Instruction i of wave w fills 16-byte slots p = (4i + w) * 64 +
+// lane, i.e. row p / 16 = 16i + 4w + lane / 16, stored chunk p % 16, which holds
+// logical chunk (p % 16) ^ (row % 16); row % 16 does not depend on i, so one
+// per-lane byte offset (computed once) serves every load, and the block and the
+// instruction only move the scalar offset. `wave` is wave-uniform (a scalar
+// register). The resource spans this batch's N index keys (N * 256 bytes < 2^31).
+struct KeyStage {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t lane_off;
+    int wave;
+    __device__ __forceinline__ KeyStage(const __bf16* kb, int N, int wave_, int lane) : wave(wave_) {
+        rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, N * kDim * 2, kIdxRawBufferWord3);
+        const int row0 = 4 * wave_ + (lane >> 4);
+        lane_off = (uint32_t)(row0 * kDim + (((lane & 15) ^ (row0 & 15)) * 8)) * 2u;
+    }
+    // load i of key block `blk` into LDS buffer `dst`
+    __device__ __forceinline__ void load(int blk, __bf16* dst, int i) const {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + (i * 4 + wave) * 64 * 8), 16, lane_off,
+                                                 (blk * kBlock + i * 16) * kDim * 2, 0, 0);
+    }
+    __device__ __forceinline__ void all(int blk, __bf16* dst) const {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(src + lane_off + i * 16 * kDim),
-                                         (lds_ptr)(dst + (i * 4 + wave) * 64 * 8), 16, 0, 0);
-}
+        for (int i = 0; i < 8; ++i) load(blk, dst, i);
+    }
+};
 
 // B operand (Q^T) of a wave: lane holds row (r0 + wave*64 + nt*32 + l32), dims kk*16 + 8h .. +7;
 // rows past R are zero and get query position -1 (never the diagonal block).
@@ -74,9 +90,13 @@ __device__ __forceinline__ void load_q_rows(const __bf16* __restrict__ qb, int r
 // The four 32-key M tiles are software-pipelined: tile mt's products are issued while
 // tile mt - 1's accumulators are reduced (two accumulator sets). The common, unmasked
 // path has no branch, so the reductions interleave with the matrix instructions.
+// The next key block's staging loads (block `nblk_` into the idle buffer `ndst`) are issued
+// from here: spread two per M tile on the common path, so a wave never stalls on a
+// burst of eight loads queued behind the other waves' (all eight at the start on the
+// diagonal path, after the first tile's products).
 template <bool DIAG>
 __device__ __forceinline__ float block_row_max_t(const __bf16* kt, const bf16x8 (&qf)[2][8], int lim0, int lim1,
-                                                 int h, int l32) {
+                                                 int h, int l32, const KeyStage& st, int nblk_, __bf16* ndst) {
     float m0 = -INFINITY, m1 = -INFINITY;
     f32x16 acc[2][2];
     auto products = [&](int mt, f32x16 (&a)[2]) {
@@ -103,16 +123,25 @@ __device__ __forceinline__ float block_row_max_t(const __bf16* kt, const bf16x8 
         }
     };
     products(0, acc[0]);
+    if (DIAG) {
+        st.all(nblk_, ndst);
+    } else {
+        st.load(nblk_, ndst, 0);
+        st.load(nblk_, ndst, 1);
+    }
 #pragma unroll
     for (int mt = 1; mt < 4; ++mt) {
         products(mt, acc[mt & 1]);
         reduce(mt - 1, acc[(mt - 1) & 1]);
         if (!DIAG) {
+            st.load(nblk_, ndst, 2 * mt);
+            st.load(nblk_, ndst, 2 * mt + 1);
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // an operand read
                 __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two products
                 __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two max steps
+                if (kk == 3 || kk == 7) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // a staging load
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -124,12 +153,12 @@ __device__ __forceinline__ float block_row_max_t(const __bf16* kt, const bf16x8 
 }
 
 __device__ __forceinline__ float block_row_max(const __bf16* kt, const bf16x8 (&qf)[2][8], const int (&trow)[2],
-                                               int c, int h, int l32) {
+                                               int c, int h, int l32, const KeyStage& st, int nblk_, __bf16* ndst) {
     const bool diag0 = (trow[0] >> 7) == c, diag1 = (trow[1] >> 7) == c;
     const int lim0 = (diag0 ? trow[0] - c * kBlock : kBlock - 1) - 4 * h;
     const int lim1 = (diag1 ? trow[1] - c * kBlock : kBlock - 1) - 4 * h;
-    return __any(diag0 || diag1) ? block_row_max_t<true>(kt, qf, lim0, lim1, h, l32)
-                                 : block_row_max_t<false>(kt, qf, lim0, lim1, h, l32);
+    return __any(diag0 || diag1) ? block_row_max_t<true>(kt, qf, lim0, lim1, h, l32, st, nblk_, ndst)
+                                 : block_row_max_t<false>(kt, qf, lim0, lim1, h, l32, st, nblk_, ndst);
 }
 
 __global__ __launch_bounds__(256, 2) void k_index_pool(const __bf16* __restrict__ q_idx,
@@ -151,7 +180,8 @@ __global__ __launch_bounds__(256, 2) void k_index_pool(const __bf16* __restrict_
     const __bf16* qb = q_idx + (size_t)b * R * kDim;
     const __bf16* kb = k_idx + (size_t)b * N * kDim;
 
-    stage_key_block(kb + (size_t)c0 * kBlock * kDim, ks[0], wave, lane);
+    const KeyStage st(kb, N, wave, lane);
+    st.all(c0, ks[0]);
     bf16x8 qf[2][8];
     int trow[2];
     load_q_rows(qb, r0, R, H, wave, h, l32, qf, trow);
@@ -165,12 +195,14 @@ __global__ __launch_bounds__(256, 2) void k_index_pool(const __bf16* __restrict_
         const int buf = (c - c0) & 1;
         __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of block c have landed
         __syncthreads();                // ... and everyone's; the other buffer is free again
-        if (c + 1 < c1) stage_key_block(kb + (size_t)(c + 1) * kBlock * kDim, ks[buf ^ 1], wave, lane);
-        const float m = block_row_max(ks[buf], qf, trow, c, h, l32);
+        // the last block stages itself again into the idle buffer (no branch in the loop body)
+        const int cn = c + 1 < c1 ? c + 1 : c;
+        const float m = block_row_max(ks[buf], qf, trow, c, h, l32, st, cn, ks[buf ^ 1]);
 #pragma unroll
         for (int j = 0; j + 1 < kIdxChunk; ++j) pv[j] = pv[j + 1];
         pv[kIdxChunk - 1] = m;
     }
+    __builtin_amdgcn_s_waitcnt(0);  // the last block's repeated staging has landed before the LDS is released
 
     const int row = r0 + wave * 64 + h * 32 + l32;
     if (row < R) {
@@ -218,7 +250,8 @@ __global__ __launch_bounds__(256, 2) void k_index_topk(const __bf16* __restrict_
     const __bf16* qb = q_idx + (size_t)b * R * kDim;
     const __bf16* kb = k_idx + (size_t)b * N * kDim;
 
-    stage_key_block(kb, ks[0], wave, lane);
+    const KeyStage st(kb, N, wave, lane);
+    st.all(0, ks[0]);
     bf16x8 qf[2][8];
     int trow[2];
     load_q_rows(qb, r0, R, H, wave, h, l32, qf, trow);
@@ -238,8 +271,8 @@ __global__ __launch_bounds__(256, 2) void k_index_topk(const __bf16* __restrict_
         const int buf = c & 1;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (c + 1 < nkb) stage_key_block(kb + (size_t)(c + 1) * kBlock * kDim, ks[buf ^ 1], wave, lane);
-        const float m = block_row_max(ks[buf], qf, trow, c, h, l32);
+        const int cn = c + 1 < nkb ? c + 1 : c;  // the last block stages itself again into the idle buffer
+        const float m = block_row_max(ks[buf], qf, trow, c, h, l32, st, cn, ks[buf ^ 1]);
         // insert before the first listed key it exceeds; everything after moves down one
         // slot (comparing the displaced entry instead would reorder equal scores)
         const uint32_t xs = c < cl ? order_key(m) : 0u;
@@ -254,6 +287,7 @@ __global__ __launch_bounds__(256, 2) void k_index_topk(const __bf16* __restrict_
         ls[0] = gt[0] ? xs : ls[0];
         lb[0] = gt[0] ? c : lb[0];
     }
+    __builtin_amdgcn_s_waitcnt(0);  // the last block's repeated staging has landed before the LDS is released
     if (row >= R) return;
 
     const int t = row / H, g = row - t * H;
