@@ -10,7 +10,8 @@
 // layout already is), because every head is scored against the same keys.
 // A workgroup owns 256 of those rows (held in registers as the MFMA B operand)
 // and streams kIdxChunk key blocks through a double-buffered LDS tile filled by
-// direct global->LDS loads. Each wave computes S^T = K_blk * Q^T for its 64
+// buffer loads straight to LDS, the next block's issued during the current
+// block's products. Each wave computes S^T = K_blk * Q^T for its 64
 // rows, so a lane holds one query row and the block max is an in-lane max plus
 // one exchange between the wave's halves. Each lane keeps its row's maxima for
 // the chunk in registers and writes them as one 128-byte run.
