@@ -342,10 +342,19 @@ __global__ __launch_bounds__(256, 2) void k_kl_dz(
     }
 }
 
-// The same result for G >= 4 with the proxy logits computed once per position
-// instead of once per head row: per half of the keys, the lane of head 0 of each
-// position puts the averaged main probabilities in LDS, then waves 0 and 1 compute
-// Z^T for the tile's (at most 32) positions, one 32-key tile each, and write dZ.
+// The same result for G >= 4 with the proxy logits computed once per position and
+// no workgroup barrier inside an item: every wave finishes its own 32 head rows
+// (32 / G positions) alone.
+//  - S = Q K^T on v_mfma_f32_16x16x32_bf16 with the query rows as the A operand,
+//    so a lane holds one key and four consecutive head rows per 16-row tile; the G
+//    rows of a position are then in-lane (G = 4) or at most two lane exchanges away,
+//    and p-bar (position, key) ends in the lanes of that key.
+//  - The wave's proxy logits Z = Q_idx K_idx^T use the same layout: row 4 g + i of
+//    the 16-row proxy tile carries the position of head row 16 i + 4 g (i < 2), so
+//    dZ = w s (px - p-bar) is formed in-lane. A 16-row proxy tile holds 32 / G <= 8
+//    positions: the unused rows are the price of needing no exchange.
+//  - The rows' LSE * log2 e, causal limits and proxy LSE go through a small
+//    per-wave LDS block (written and read by the same wave).
 constexpr int kKlSharedPos = 32;  // positions of a 128-row tile when G >= 4
 
 __global__ __launch_bounds__(256, 2) void k_kl_dz_shared(
@@ -354,18 +363,18 @@ __global__ __launch_bounds__(256, 2) void k_kl_dz_shared(
     const int32_t* __restrict__ off, const int32_t* __restrict__ item_off, const int32_t* __restrict__ entries,
     __bf16* __restrict__ dz, int N, int Hq, int Hkv, int gshift, int nblk, int n_tiles, float c_main,
     float c_idx, float dz_scale) {
-    __shared__ __attribute__((aligned(16))) __bf16 ks[kBlock * kDim];
-    __shared__ __attribute__((aligned(16))) __bf16 kis[kBlock * kDim];
+    __shared__ __attribute__((aligned(16))) __bf16 ks[kBlock * kDim];   // K[key][dim], swizzled
+    __shared__ __attribute__((aligned(16))) __bf16 kis[kBlock * kDim];  // K_idx[key][dim], swizzled
     __shared__ int32_t ent[kRowTilesPerItem * kKlSharedPos];
-    __shared__ __attribute__((aligned(16))) float pbar[kKlSharedPos][64 + 4];  // [position][key of the half]
+    __shared__ __attribute__((aligned(16))) float rterm[4][3][32];  // per wave and row: LSE*log2e, limit, proxy LSE*log2e
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = 1 << gshift;
     const int P = kBlock >> gshift;  // <= 32
-    const int r = wave * 32 + l32;
-    const int pslot = r >> gshift, hh = r & (G - 1);
     const float log2e = 1.4426950408889634f, invG = 1.0f / (float)G;
-    const bool zwave = wave < 2;  // waves 0, 1 compute the proxy logits, lane l32 = position
+    // head row (of the 128-row tile) whose position the proxy tile's A row l16 carries
+    const int zrow = 32 * wave + 16 * ((l16 & 3) < 2 ? (l16 & 3) : 0) + 4 * (l16 >> 2);
     const int total_items = item_off[n_tiles];
 
     for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
@@ -378,107 +387,139 @@ __global__ __launch_bounds__(256, 2) void k_kl_dz_shared(
         const int ne = min(rt1 * P, npos) - rt0 * P;
         const int ebase = e0 + rt0 * P;
 
-        __syncthreads();
+        __syncthreads();  // the previous item's LDS reads are done
         for (int i = tid; i < ne; i += 256) ent[i] = entries[ebase + i];
         kl_stage_rows(k + (((size_t)b * N + (size_t)c * kBlock) * Hkv + g) * kDim, Hkv * kDim, ks, tid);
         kl_stage_rows(k_idx + ((size_t)b * N + (size_t)c * kBlock) * kDim, kDim, kis, tid);
         __syncthreads();
 
-        const int head = g * G + hh;
-        auto load_rows = [&](const __bf16* base, size_t row, bf16x8 (&buf)[8]) {
-            const __bf16* p = base + row * kDim + 8 * h;
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) buf[kk] = *(const bf16x8*)(p + kk * 16);
-        };
-        // this lane's head row (S) and, on waves 0-1, the proxy row of position l32 (Z)
-        auto row_of = [&](int rt, int slot, bool& valid) {
-            const int li = (rt - rt0) * P + slot;
-            valid = slot < P && li < ne;
+        const int head0 = g * G;
+        // query position of head row r (0..127) of row tile rt; rows past the item's
+        // entries read entry 0 and are never written
+        auto pos_of = [&](int rt, int r, bool& valid) {
+            const int li = (rt - rt0) * P + (r >> gshift);
+            valid = li < ne;
             return ent[valid ? li : 0] >> 8;
         };
-        bool svalid, zvalid;
-        int ts = row_of(rt0, pslot, svalid), tz = row_of(rt0, l32, zvalid);
-        bf16x8 qf[8], qif[8];
-        load_rows(q, ((size_t)b * N + ts) * Hq + head, qf);
-        if (zwave) load_rows(q_idx, ((size_t)b * N + tz) * Hkv + g, qif);
-        for (int rt = rt0; rt < rt1; ++rt) {
-            bool nsv = false, nzv = false;
-            const int tsn = rt + 1 < rt1 ? row_of(rt + 1, pslot, nsv) : ts;
-            const int tzn = rt + 1 < rt1 ? row_of(rt + 1, l32, nzv) : tz;
-            const float lm = lse[((size_t)b * Hq + head) * N + ts] * log2e;
-            const int lims = ((ts >> 7) == c ? ts - c * kBlock : kBlock - 1);
-            const float lp = zwave ? lse_px[((size_t)b * Hkv + g) * N + tz] * log2e : 0.0f;
-            const int limz = ((tz >> 7) == c ? tz - c * kBlock : kBlock - 1);
-#pragma unroll 1
-            for (int mh = 0; mh < 2; ++mh) {
-                asm volatile("" ::: "memory");
-                f32x16 sacc[2];
+        // A operands: head rows 32 wave + 16 mt + l16 (S) and the proxy rows (Z), dims 32 kk + 8 g4 .. +7
+        bf16x8 qf[2][4], qif[4];
+        auto load_q = [&](int rt) {
 #pragma unroll
-                for (int m2 = 0; m2 < 2; ++m2)
+            for (int mt = 0; mt < 2; ++mt) {
+                const int r = 32 * wave + 16 * mt + l16;
+                bool v;
+                const int t = pos_of(rt, r, v);
+                const __bf16* p = q + (((size_t)b * N + t) * Hq + head0 + (r & (G - 1))) * kDim + 8 * g4;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) sacc[m2][i] = 0.0f;
-#pragma unroll
-                for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-                    for (int m2 = 0; m2 < 2; ++m2) {
-                        const bf16x8 a = *(const bf16x8*)(ks + swz_chunk_offset((2 * mh + m2) * 32 + l32, 2 * kk + h));
-                        sacc[m2] = mfma32(a, qf[kk], sacc[m2]);
-                    }
-                if (mh == 1 && rt + 1 < rt1) load_rows(q, ((size_t)b * N + tsn) * Hq + head, qf);
-#pragma unroll
-                for (int m2 = 0; m2 < 2; ++m2)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = (2 * mh + m2) * 32 + mfma32_row(i, h);
-                        sacc[m2][i] =
-                            key <= lims ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[m2][i], c_main, -lm)) : 0.0f;
-                    }
-                group_sum32(sacc, G);
-                if (hh == 0 && pslot < P) {
-#pragma unroll
-                    for (int m2 = 0; m2 < 2; ++m2)
-#pragma unroll
-                        for (int i0 = 0; i0 < 16; i0 += 4)
-                            *(f32x4*)&pbar[pslot][m2 * 32 + mfma32_row(i0, h)] =
-                                (f32x4){sacc[m2][i0] * invG, sacc[m2][i0 + 1] * invG, sacc[m2][i0 + 2] * invG,
-                                        sacc[m2][i0 + 3] * invG};
-                }
-                __syncthreads();  // the half's averaged probabilities are in LDS
-                if (zwave) {
-                    const int m2 = wave;
-                    f32x16 zacc;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) zacc[i] = 0.0f;
-#pragma unroll
-                    for (int kk = 0; kk < 8; ++kk) {
-                        const bf16x8 a = *(const bf16x8*)(kis + swz_chunk_offset((2 * mh + m2) * 32 + l32, 2 * kk + h));
-                        zacc = mfma32(a, qif[kk], zacc);
-                    }
-                    if (zvalid) {
-                        __bf16* dst = dz + (size_t)(ebase + (rt - rt0) * P + l32) * kBlock;
-#pragma unroll
-                        for (int i0 = 0; i0 < 16; i0 += 4) {
-                            const int k0 = (2 * mh + m2) * 32 + mfma32_row(i0, h);
-                            const f32x4 pb = *(const f32x4*)&pbar[l32][m2 * 32 + mfma32_row(i0, h)];
-                            bf16x4 w;
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                const float px = k0 + j <= limz
-                                                     ? __builtin_amdgcn_exp2f(__builtin_fmaf(zacc[i0 + j], c_idx, -lp))
-                                                     : 0.0f;
-                                w[j] = (__bf16)(dz_scale * (px - pb[j]));
-                            }
-                            *(bf16x4*)(dst + k0) = w;
-                        }
-                    }
-                    if (mh == 1 && rt + 1 < rt1) load_rows(q_idx, ((size_t)b * N + tzn) * Hkv + g, qif);
-                }
-                __syncthreads();  // pbar is read before the next half overwrites it
+                for (int kk = 0; kk < 4; ++kk) qf[mt][kk] = *(const bf16x8*)(p + 32 * kk);
             }
-            ts = tsn;
-            svalid = nsv;
-            tz = tzn;
-            zvalid = nzv;
+        };
+        auto load_qi = [&](int rt) {
+            bool v;
+            const int t = pos_of(rt, zrow, v);
+            const __bf16* p = q_idx + (((size_t)b * N + t) * Hkv + g) * kDim + 8 * g4;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) qif[kk] = *(const bf16x8*)(p + 32 * kk);
+        };
+        load_q(rt0);
+        load_qi(rt0);
+        for (int rt = rt0; rt < rt1; ++rt) {
+            // the K and K_idx operands are read from LDS in every row tile (not hoisted out of
+            // the loop into registers)
+            asm volatile("" ::: "memory");
+            if (lane < 32) {  // the row terms of head row 32 wave + lane
+                const int r = 32 * wave + lane;
+                bool v;
+                const int t = pos_of(rt, r, v);
+                rterm[wave][0][lane] = lse[((size_t)b * Hq + head0 + (r & (G - 1))) * N + t] * log2e;
+                rterm[wave][1][lane] = __int_as_float((t >> 7) == c ? t - c * kBlock : kBlock - 1);
+                rterm[wave][2][lane] = lse_px[((size_t)b * Hkv + g) * N + t] * log2e;
+            }
+            // S: acc[mt][nt] register i = row 16 mt + 4 g4 + i (of the wave's 32), key 16 nt + l16
+            f32x4 acc[2][8];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) {
+                    const bf16x8 bk = *(const bf16x8*)(ks + swz_chunk_offset(16 * nt + l16, 4 * kk + g4));
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = mfma16(qf[mt][kk], bk, acc[mt][nt]);
+                }
+            if (rt + 1 < rt1) load_q(rt + 1);
+            // P = 2^(s scale log2e - LSE log2e), causal-masked on the diagonal block
+            f32x4 lm4[2], lim4[2];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                lm4[mt] = *(const f32x4*)&rterm[wave][0][16 * mt + 4 * g4];
+                lim4[mt] = *(const f32x4*)&rterm[wave][1][16 * mt + 4 * g4];
+            }
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = 16 * nt + l16;
+                        acc[mt][nt][i] = key <= __float_as_int(lim4[mt][i])
+                                             ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mt][nt][i], c_main, -lm4[mt][i]))
+                                             : 0.0f;
+                    }
+            // p-bar: the sum over a position's G head rows (in-lane for four, then across the
+            // lanes 16 and 32 apart, then across the two row tiles), over G
+            float pb[2][8];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt)
+                    pb[mt][nt] = (acc[mt][nt][0] + acc[mt][nt][1]) + (acc[mt][nt][2] + acc[mt][nt][3]);
+            if (G >= 8)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < 8; ++nt) pb[mt][nt] += __shfl_xor(pb[mt][nt], 16, 64);
+            if (G >= 16)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < 8; ++nt) pb[mt][nt] += __shfl_xor(pb[mt][nt], 32, 64);
+            if (G >= 32)
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) pb[0][nt] = pb[1][nt] = pb[0][nt] + pb[1][nt];
+            // Z: z[nt] register i = proxy row 4 g4 + i, i.e. the position of head row 16 i + 4 g4
+            f32x4 z[8];
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) z[nt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) {
+                    const bf16x8 bk = *(const bf16x8*)(kis + swz_chunk_offset(16 * nt + l16, 4 * kk + g4));
+                    z[nt] = mfma16(qif[kk], bk, z[nt]);
+                }
+            if (rt + 1 < rt1) load_qi(rt + 1);
+            // dZ rows, written by the lane group that holds a position's first head row
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r0 = 32 * wave + 16 * i + 4 * g4;
+                bool v;
+                (void)pos_of(rt, r0, v);
+                if (v && (r0 & (G - 1)) == 0) {
+                    const float lp = rterm[wave][2][16 * i + 4 * g4];
+                    const int limz = __float_as_int(rterm[wave][1][16 * i + 4 * g4]);
+                    __bf16* dst = dz + (size_t)(ebase + (rt - rt0) * P + (r0 >> gshift)) * kBlock;
+#pragma unroll
+                    for (int nt = 0; nt < 8; ++nt) {
+                        const int key = 16 * nt + l16;
+                        const float px =
+                            key <= limz ? __builtin_amdgcn_exp2f(__builtin_fmaf(z[nt][i], c_idx, -lp)) : 0.0f;
+                        dst[key] = (__bf16)(dz_scale * (px - pb[i][nt] * invG));
+                    }
+                }
+            }
         }
     }
 }
