@@ -576,20 +576,33 @@ __global__ __launch_bounds__(256, 2) void k_kl_grad(
 #pragma unroll
             for (int i = 0; i < 16; ++i) dk[dt][i] = 0.0f;
 
-        for (int cb = 0; cb < ne; cb += kKlChunk) {
-            __syncthreads();  // kit and ent are written; the previous chunk's reads are done
+        // A chunk's dZ and proxy rows (thread: rows tid / 16 and + 16, chunk tid % 16) are
+        // loaded into registers one chunk ahead and stored into LDS at the chunk's start.
+        u32x4 pz[2], pq[2];
+        auto load_chunk = [&](int cb0) {
 #pragma unroll
             for (int it = 0; it < 2; ++it) {
                 const int row = (tid >> 4) + 16 * it, ch = tid & 15;
-                uint4 vz = {0u, 0u, 0u, 0u}, vq = {0u, 0u, 0u, 0u};
-                if (cb + row < ne) {
-                    const int t = ent[cb + row] >> 8;
-                    vz = *(const uint4*)(dz + (size_t)(ebase + cb + row) * kBlock + ch * 8);
-                    vq = *(const uint4*)(q_idx + (((size_t)b * N + t) * Hkv + g) * kDim + ch * 8);
+                pz[it] = (u32x4){0u, 0u, 0u, 0u};
+                pq[it] = (u32x4){0u, 0u, 0u, 0u};
+                if (cb0 + row < ne) {
+                    const int t = ent[cb0 + row] >> 8;
+                    pz[it] = *(const u32x4*)(dz + (size_t)(ebase + cb0 + row) * kBlock + ch * 8);
+                    pq[it] = *(const u32x4*)(q_idx + (((size_t)b * N + t) * Hkv + g) * kDim + ch * 8);
                 }
-                *(uint4*)(dzs + kl_row_off(row, ch)) = vz;
-                *(uint4*)(qis + kl_row_off(row, ch)) = vq;
             }
+        };
+        __syncthreads();  // kit and ent are written
+        load_chunk(0);
+        for (int cb = 0; cb < ne; cb += kKlChunk) {
+            if (cb > 0) __syncthreads();  // the previous chunk's reads are done
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                const int row = (tid >> 4) + 16 * it, ch = tid & 15;
+                *(u32x4*)(dzs + kl_row_off(row, ch)) = pz[it];
+                *(u32x4*)(qis + kl_row_off(row, ch)) = pq[it];
+            }
+            if (cb + kKlChunk < ne) load_chunk(cb + kKlChunk);
             __syncthreads();
             // dq_idx^T for dims 32 wave .. +31 and the chunk's 32 entries, over the 128 keys
             {
