@@ -660,12 +660,23 @@ __global__ __launch_bounds__(256) void k_kl_dq_sum(const int32_t* __restrict__ b
     const int g = (int)(bg % Hkv);
     const long long b = bg / Hkv;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int s = 0; s < top_k; ++s) {
-        const int c = block_idx[row * top_k + s];
-        if (c < 0 || c > (t >> 7)) continue;
-        const bf16x8 v = *(const bf16x8*)(dq_part + (row * top_k + s) * kDim + ch * 8);
+    // eight slots at a time: their block indices and records are all requested before any
+    // is used (a record of a slot that is not attended is read but not added), then added
+    // in slot order
+    for (int s0 = 0; s0 < top_k; s0 += 8) {
+        int c[8];
+        bf16x8 v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += (float)v[e];
+        for (int u = 0; u < 8; ++u) {
+            const int s = s0 + u < top_k ? s0 + u : top_k - 1;
+            c[u] = block_idx[row * top_k + s];
+            v[u] = *(const bf16x8*)(dq_part + (row * top_k + s) * kDim + ch * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < top_k && c[u] >= 0 && c[u] <= (t >> 7))
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += (float)v[u][e];
     }
     bf16x8 out;
 #pragma unroll
@@ -685,8 +696,17 @@ __global__ __launch_bounds__(256) void k_kl_dk_reduce(const float* __restrict__ 
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int g = 0; g < Hkv; ++g) {
             const int tile = (b * Hkv + g) * nblk + c;
-            for (int it = item_off[tile]; it < item_off[tile + 1]; ++it)
-                acc += *(const f32x4*)(dk_part + (size_t)it * part + e * 4);
+            const int i0 = item_off[tile], i1 = item_off[tile + 1];
+            int it = i0;
+            // four items' partials requested at once, added in item order
+            for (; it + 4 <= i1; it += 4) {
+                f32x4 x[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) x[u] = *(const f32x4*)(dk_part + (size_t)(it + u) * part + e * 4);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc += x[u];
+            }
+            for (; it < i1; ++it) acc += *(const f32x4*)(dk_part + (size_t)it * part + e * 4);
         }
         const bf16x4 w = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
         *(bf16x4*)(dk_idx + ((size_t)b * N + (size_t)c * kBlock) * kDim + e * 4) = w;
