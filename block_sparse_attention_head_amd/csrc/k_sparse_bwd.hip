@@ -629,7 +629,22 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv_reduce(const float* __restrict
     const int e_end = (blockIdx.y + 1) * (kBlock * kDim / 16);
     for (int e = blockIdx.y * (kBlock * kDim / 16) + threadIdx.x; e < e_end; e += 256) {
         f32x4 ak = {0.0f, 0.0f, 0.0f, 0.0f}, av = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int it = i0; it < i1; ++it) {
+        int it = i0;
+        // four items' partials requested at once, added in item order
+        for (; it + 4 <= i1; it += 4) {
+            f32x4 xk[4], xv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                xk[u] = __builtin_nontemporal_load((const f32x4*)(dkv_part + (size_t)(it + u) * 2 * part + e * 4));
+                xv[u] = __builtin_nontemporal_load((const f32x4*)(dkv_part + (size_t)(it + u) * 2 * part + part + e * 4));
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                ak += xk[u];
+                av += xv[u];
+            }
+        }
+        for (; it < i1; ++it) {
             ak += __builtin_nontemporal_load((const f32x4*)(dkv_part + (size_t)it * 2 * part + e * 4));
             av += __builtin_nontemporal_load((const f32x4*)(dkv_part + (size_t)it * 2 * part + part + e * 4));
         }
