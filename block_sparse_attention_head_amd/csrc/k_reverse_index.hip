@@ -215,6 +215,51 @@ __global__ __launch_bounds__(kRevThreads) void k_rev_scatter_any(const int32_t* 
     }
 }
 
+// The same placement for key blocks up to kRevMaskBins (nblk <= 1024): a thread's rank
+// among the chunk's threads that chose the same block for the same slot is the
+// popcount of a per-block bit mask of thread indices below its own (set with LDS
+// atomics, read after a barrier, cleared after the next one), instead of a scan over
+// the lower threads' choices. Same order, so the same entries.
+constexpr int kRevMaskBins = 1024;
+__global__ __launch_bounds__(kRevThreads) void k_rev_scatter_mask(const int32_t* __restrict__ block_idx,
+                                                                  const int32_t* __restrict__ wgoff,
+                                                                  int32_t* __restrict__ entries, int N, int p0, int Nc,
+                                                                  int nblk, int top_k, int ppw) {
+    __shared__ int32_t bins[kRevMaskBins];
+    __shared__ __attribute__((aligned(16))) uint32_t tmask[kRevMaskBins][kRevThreads / 32];
+    const int tid = threadIdx.x;
+    const int bg = blockIdx.y, w = blockIdx.x, nwg = gridDim.x;
+    const int t0 = p0 + w * ppw, t1 = min(p0 + Nc, t0 + ppw);
+    const int32_t* base_off = wgoff + ((size_t)bg * nwg + w) * nblk;
+    for (int i = tid; i < nblk; i += kRevThreads) bins[i] = base_off[i];
+    for (int i = tid; i < nblk * (kRevThreads / 32); i += kRevThreads) (&tmask[0][0])[i] = 0u;
+    __syncthreads();
+    const int word = tid >> 5;
+    const uint32_t bit = 1u << (tid & 31);
+    for (int cb = t0; cb < t1; cb += kRevThreads) {  // uniform trip count
+        const int t = cb + tid;
+        const bool in = t < t1;
+        const int32_t* row = block_idx + ((size_t)bg * N + (in ? t : t0)) * top_k;
+        for (int s = 0; s < top_k; ++s) {
+            const int c = in ? row[s] : -1;
+            const bool ok = in && valid_entry(c, t);
+            if (ok) atomicOr(&tmask[c][word], bit);
+            __syncthreads();
+            if (ok) {
+                int r = __popc(tmask[c][word] & (bit - 1u));
+                for (int j = 0; j < word; ++j) r += __popc(tmask[c][j]);
+                entries[bins[c] + r] = (t << 8) | s;
+            }
+            __syncthreads();  // every rank of this slot is taken from the old offsets and masks
+            if (ok) {
+                atomicAdd(&bins[c], 1);
+                tmask[c][word] = 0u;
+            }
+            __syncthreads();  // the masks are clear for the next slot
+        }
+    }
+}
+
 hipError_t launch_sparse_plan(const int32_t* block_idx, const SparseWs& ws, const Dims& d, bool canonical,
                               hipStream_t stream) {
     const int n = d.B * d.Hkv * d.nblk;
@@ -228,8 +273,12 @@ hipError_t launch_sparse_plan(const int32_t* block_idx, const SparseWs& ws, cons
     if (canonical) {
         hipLaunchKernelGGL(k_rev_wgoff, dim3((n + 255) / 256), dim3(256), 0, stream, ws.off, ws.wgoff, n, d.nblk,
                            nwg);
-        hipLaunchKernelGGL(k_rev_scatter, rgrid, dim3(kRevThreads), 0, stream, block_idx, ws.wgoff, ws.entries, d.N,
-                           d.p0, d.Nc, d.nblk, d.top_k, ppw);
+        if (d.nblk <= kRevMaskBins)
+            hipLaunchKernelGGL(k_rev_scatter_mask, rgrid, dim3(kRevThreads), 0, stream, block_idx, ws.wgoff,
+                               ws.entries, d.N, d.p0, d.Nc, d.nblk, d.top_k, ppw);
+        else
+            hipLaunchKernelGGL(k_rev_scatter, rgrid, dim3(kRevThreads), 0, stream, block_idx, ws.wgoff, ws.entries,
+                               d.N, d.p0, d.Nc, d.nblk, d.top_k, ppw);
     } else {
         hipLaunchKernelGGL(k_rev_scatter_any, rgrid, dim3(kRevThreads), 0, stream, block_idx, ws.cursor, ws.entries,
                            d.N, d.p0, d.Nc, d.nblk, d.top_k, ppw);
