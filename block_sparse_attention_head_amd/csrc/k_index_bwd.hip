@@ -116,7 +116,7 @@ __device__ __forceinline__ void kl_stage_rows(const __bf16* __restrict__ src, in
 // 32 w + l32, keys mt*32 + mfma32_row(i, h)): per entry the max of the logits
 // over the block's attended keys and the sum of 2^(logit - max), both in log2
 // units, to the (t, slot) record.
-__global__ __launch_bounds__(256, 2) void k_kl_lse_part(
+__global__ __launch_bounds__(256, 4) void k_kl_lse_part(
     const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx, const int32_t* __restrict__ off,
     const int32_t* __restrict__ item_off, const int32_t* __restrict__ entries, float2* __restrict__ lse_part,
     int N, int Hkv, int gshift, int nblk, int top_k, int n_tiles, float c_idx) {
@@ -150,36 +150,46 @@ __global__ __launch_bounds__(256, 2) void k_kl_lse_part(
             const __bf16* qirow = q_idx + (((size_t)b * N + t) * Hkv + g) * kDim + 8 * h;
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) qf[kk] = *(const bf16x8*)(qirow + kk * 16);
-            asm volatile("" ::: "memory");
-            f32x16 zacc[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) zacc[mt][i] = 0.0f;
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    const bf16x8 a = *(const bf16x8*)(kis + swz_chunk_offset(mt * 32 + l32, 2 * kk + h));
-                    zacc[mt] = mfma32(a, qf[kk], zacc[mt]);
-                }
+            // the keys in two halves of 64 (half the accumulators live, so four workgroups fit a
+            // CU), merged as a running max and sum
             const int lim = ((t >> 7) == c ? t - c * kBlock : kBlock - 1);
-            float m = -INFINITY;
+            float m = -INFINITY, l = 0.0f;
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+            for (int mh = 0; mh < 2; ++mh) {
+                asm volatile("" ::: "memory");
+                f32x16 zacc[2];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float zz = mt * 32 + mfma32_row(i, h) <= lim ? zacc[mt][i] * c_idx : -INFINITY;
-                    zacc[mt][i] = zz;
-                    m = fmaxf(m, zz);
-                }
-            m = wave_max_xor32(m);  // key 128 c <= t is always attended, so m is finite
-            float l = 0.0f;
+                for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+                    for (int i = 0; i < 16; ++i) zacc[m2][i] = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) l += __builtin_amdgcn_exp2f(zacc[mt][i] - m);
-            l = wave_sum_xor32(l);
+                for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                    for (int m2 = 0; m2 < 2; ++m2) {
+                        const bf16x8 a =
+                            *(const bf16x8*)(kis + swz_chunk_offset((2 * mh + m2) * 32 + l32, 2 * kk + h));
+                        zacc[m2] = mfma32(a, qf[kk], zacc[m2]);
+                    }
+                float mx = -INFINITY;
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const float zz =
+                            (2 * mh + m2) * 32 + mfma32_row(i, h) <= lim ? zacc[m2][i] * c_idx : -INFINITY;
+                        zacc[m2][i] = zz;
+                        mx = fmaxf(mx, zz);
+                    }
+                mx = wave_max_xor32(mx);  // half 0 holds key 128 c <= t, always attended: finite from there on
+                const float mnew = fmaxf(m, mx);
+                float lh = 0.0f;
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) lh += __builtin_amdgcn_exp2f(zacc[m2][i] - mnew);
+                l = (mh == 0 ? 0.0f : l * __builtin_amdgcn_exp2f(m - mnew)) + wave_sum_xor32(lh);
+                m = mnew;
+            }
             if (valid && h == 0)
                 lse_part[(((size_t)b * Hkv + g) * N + t) * top_k + (en & 255)] = make_float2(m, l);
         }
@@ -717,7 +727,7 @@ __global__ __launch_bounds__(256) void k_kl_dk_reduce(const float* __restrict__ 
 hipError_t launch_kl_lse(const void* q_idx, const void* k_idx, const int32_t* block_idx, const SparseWs& plan,
                          float2* lse_part, float* lse_px, float index_scale, const Dims& d, hipStream_t stream) {
     const int n = d.B * d.Hkv * d.nblk;
-    hipLaunchKernelGGL(k_kl_lse_part, dim3(2 * device_cu_count()), dim3(256), 0, stream, (const __bf16*)q_idx,
+    hipLaunchKernelGGL(k_kl_lse_part, dim3(4 * device_cu_count()), dim3(256), 0, stream, (const __bf16*)q_idx,
                        (const __bf16*)k_idx, plan.off, plan.item_off, plan.entries, lse_part, d.N, d.Hkv, d.gshift,
                        d.nblk, d.top_k, n, index_scale * 1.4426950408889634f);
     hipError_t e = hipGetLastError();
