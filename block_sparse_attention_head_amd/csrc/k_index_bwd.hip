@@ -20,7 +20,10 @@
 //               keys (MFMA), then merged over the slots;
 //   k_kl_dz     per 128-row tile (positions x G heads): S^T = K Q^T and the proxy
 //               Z^T = K_idx Q_idx^T on MFMA, p averaged over the G heads of a
-//               position by lane exchanges, dZ rows to the workspace in bf16;
+//               position by lane exchanges, dZ rows to the workspace in bf16
+//               (G <= 2); k_kl_dz_shared for G >= 4: each wave its own 32 rows,
+//               S = Q K^T so the head average is in-lane, the proxy logits once
+//               per position in the same layout, no workgroup barrier;
 //   k_kl_grad   per chunk of 32 entries: dq_idx^T = K_idx^T dZ^T (one record per
 //               (t, slot)) and dk_idx += dZ^T Q_idx (per item), on MFMA;
 //   k_kl_dq_sum, k_kl_dk_reduce  the sums over slots, and over items and groups
