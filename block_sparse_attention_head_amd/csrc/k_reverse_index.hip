@@ -17,7 +17,9 @@
 //            cut into items of up to kRowTilesPerItem row tiles);
 //   wgoff:   in place, wgcnt[bg][w][c] -> off[tile] + sum over w' < w;
 //   scatter: each range writes its entries from its own offsets, ranking equal
-//            tiles inside a chunk by thread index (no atomics decide a slot).
+//            tiles inside a chunk by thread index (no atomics decide a slot): a
+//            popcount of per-tile bit masks of thread indices up to kRevMaskBins
+//            tiles, a scan over the lower threads' choices beyond (same order).
 // Bins beyond the LDS capacity are handled in chunks of kRevLdsBins tiles.
 //
 // The forward does not need that order (every query row of a tile is computed
