@@ -512,7 +512,7 @@ def main(argv=None) -> int:
         msa.sparse_attn_partial(shape, xg["q"], xg["k"], xg["v"], ws)
         if ev is not None:
             ev[3].record()
-        msa.sparse_attn_combine(shape, block_idx, o, lse, ws)
+        msa.sparse_attn_combine(shape, xg["q"], xg["k"], xg["v"], block_idx, o, lse, ws)
         if ev is not None:
             ev[4].record()
 

@@ -25,7 +25,9 @@
 // The forward does not need that order (every query row of a tile is computed
 // on its own, so its results do not depend on where the row sits), and uses a
 // cheaper unordered scatter: each range reserves one sub-range per touched tile
-// with a single global atomic and hands out places from LDS counters.
+// with a single global atomic and hands out places from LDS counters. When the
+// forward's combine computes each query's own block (combine_folds_local), the
+// forward plan leaves those entries out.
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 
@@ -40,6 +42,8 @@ __global__ __launch_bounds__(256) void k_fill_i32(int32_t* __restrict__ p, int32
 }
 
 __device__ __forceinline__ bool valid_entry(int c, int t) { return c >= 0 && c <= (t >> 7); }
+// With skip = 1 the query's own block is left out (the combine computes it).
+__device__ __forceinline__ bool valid_entry(int c, int t, int skip) { return c >= 0 && c <= (t >> 7) - skip; }
 
 int rev_positions_per_group(int N) {
     // 1024 positions per range, or more so that ranges <= 256 (at least one range)
@@ -51,7 +55,8 @@ int rev_groups(int N) { return (N + rev_positions_per_group(N) - 1) / rev_positi
 // wgcnt[(bg*nwg + w)*nblk + c] = entries of range w selecting tile c; cnt[bg*nblk + c] += the same.
 __global__ __launch_bounds__(kRevThreads) void k_rev_count(const int32_t* __restrict__ block_idx,
                                                            int32_t* __restrict__ cnt, int32_t* __restrict__ wgcnt,
-                                                           int N, int p0, int Nc, int nblk, int top_k, int ppw) {
+                                                           int N, int p0, int Nc, int nblk, int top_k, int ppw,
+                                                           int skip) {
     __shared__ int32_t hist[kRevLdsBins];
     const int bg = blockIdx.y, w = blockIdx.x, nwg = gridDim.x;
     const int t0 = p0 + w * ppw, t1 = min(p0 + Nc, t0 + ppw);
@@ -64,7 +69,7 @@ __global__ __launch_bounds__(kRevThreads) void k_rev_count(const int32_t* __rest
             const int32_t* row = block_idx + ((size_t)bg * N + t) * top_k;
             for (int s = 0; s < top_k; ++s) {
                 const int c = row[s];
-                if (valid_entry(c, t) && c >= c0 && c < c0 + nb) atomicAdd(&hist[c - c0], 1);
+                if (valid_entry(c, t, skip) && c >= c0 && c < c0 + nb) atomicAdd(&hist[c - c0], 1);
             }
         }
         __syncthreads();
@@ -183,7 +188,7 @@ __global__ __launch_bounds__(kRevThreads) void k_rev_scatter(const int32_t* __re
 __global__ __launch_bounds__(kRevThreads) void k_rev_scatter_any(const int32_t* __restrict__ block_idx,
                                                                  int32_t* __restrict__ cursor,
                                                                  int32_t* __restrict__ entries, int N, int p0,
-                                                                 int Nc, int nblk, int top_k, int ppw) {
+                                                                 int Nc, int nblk, int top_k, int ppw, int skip) {
     __shared__ int32_t bins[kRevLdsBins];
     const bool use_lds = nblk <= kRevLdsBins;
     const int bg = blockIdx.y, w = blockIdx.x;
@@ -196,7 +201,7 @@ __global__ __launch_bounds__(kRevThreads) void k_rev_scatter_any(const int32_t* 
             const int32_t* row = block_idx + ((size_t)bg * N + t) * top_k;
             for (int s = 0; s < top_k; ++s) {
                 const int c = row[s];
-                if (valid_entry(c, t)) atomicAdd(&bins[c], 1);
+                if (valid_entry(c, t, skip)) atomicAdd(&bins[c], 1);
             }
         }
         __syncthreads();
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(kRevThreads) void k_rev_scatter_any(const int32_t* 
         const int32_t* row = block_idx + ((size_t)bg * N + t) * top_k;
         for (int s = 0; s < top_k; ++s) {
             const int c = row[s];
-            if (!valid_entry(c, t)) continue;
+            if (!valid_entry(c, t, skip)) continue;
             const int p = use_lds ? atomicAdd(&bins[c], 1) : atomicAdd(&cur[c], 1);
             entries[p] = (t << 8) | s;
         }
@@ -265,11 +270,12 @@ __global__ __launch_bounds__(kRevThreads) void k_rev_scatter_mask(const int32_t*
 hipError_t launch_sparse_plan(const int32_t* block_idx, const SparseWs& ws, const Dims& d, bool canonical,
                               hipStream_t stream) {
     const int n = d.B * d.Hkv * d.nblk;
+    const int skip = (!canonical && combine_folds_local(d)) ? 1 : 0;  // the forward combine computes the local block
     const int ppw = rev_positions_per_group(d.Nc), nwg = rev_groups(d.Nc);
     hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, stream, ws.cnt, 0, (long long)n);
     const dim3 rgrid(nwg, d.B * d.Hkv);
     hipLaunchKernelGGL(k_rev_count, rgrid, dim3(kRevThreads), 0, stream, block_idx, ws.cnt, ws.wgoff, d.N, d.p0, d.Nc,
-                       d.nblk, d.top_k, ppw);
+                       d.nblk, d.top_k, ppw, skip);
     hipLaunchKernelGGL(k_rev_scan, dim3(1), dim3(1024), 0, stream, ws.cnt, ws.off, ws.item_off, ws.cursor, n,
                        kBlock >> d.gshift);
     if (canonical) {
@@ -283,7 +289,7 @@ hipError_t launch_sparse_plan(const int32_t* block_idx, const SparseWs& ws, cons
                                d.N, d.p0, d.Nc, d.nblk, d.top_k, ppw);
     } else {
         hipLaunchKernelGGL(k_rev_scatter_any, rgrid, dim3(kRevThreads), 0, stream, block_idx, ws.cursor, ws.entries,
-                           d.N, d.p0, d.Nc, d.nblk, d.top_k, ppw);
+                           d.N, d.p0, d.Nc, d.nblk, d.top_k, ppw, skip);
     }
     return hipGetLastError();
 }

@@ -13,22 +13,17 @@
 // tile, and for each 128-row tile of gathered queries computes S^T = K Q^T (one
 // lane per query row), the row max, P in bf16, O^T = V^T P^T, and writes
 // O / sum(P) (bf16) and m*scale + ln(sum P) (fp32) to the (t, slot, head) slot.
-// A partial record stores chunk-major over heads ([t, slot][16 chunks][H_q][8
-// dims]) so one store instruction writes G heads' chunks contiguously and the
-// combine reads whole runs. Queries are loaded one row tile ahead (across item
-// and tile boundaries), their entries two row tiles ahead.
+// A partial record stores each group's heads chunk-major ([t, slot][H_kv][16
+// chunks][G][8 dims]): one store instruction writes G heads' chunks contiguously,
+// and a group's part of a record is one contiguous G x 256-byte run for the
+// combine. Queries are loaded one row tile ahead (across item and tile
+// boundaries), their entries two row tiles ahead. When the combine folds in the
+// query's own block, the plan leaves those (row, block) pairs out of this kernel.
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 
 namespace msa {
 
-
-// Position p of a key inside a V^T row in LDS: bits 2 and 3 of the key index
-// are swapped, so that the 8 keys a lane feeds to one PV MFMA step (the keys
-// its S^T registers hold) sit in one 16-byte chunk. The map is its own inverse.
-__device__ __forceinline__ int vt_pos(int key) {
-    return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
 
 struct RowInfo {
     int t, slot;
@@ -95,33 +90,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_partial(
     // Stage K (row-major) and V^T of a tile in LDS; the caller has synchronised.
     auto stage_kv = [&](int tile) {
         const int c = tile % nblk, bg = tile / nblk, g = bg % Hkv, b = bg / Hkv;
-        const size_t tile_off = (((size_t)b * N + (size_t)c * kBlock) * Hkv + g) * kDim;
-        const __bf16* kbase = k + tile_off;
-        const __bf16* vbase = v + tile_off;
-        const int kstride = Hkv * kDim;
-        const int key0 = tid >> 4, ch = tid & 15;
-        const int koff = key0 * kstride + ch * 8;
-        uint4 kv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) kv[i] = *(const uint4*)(kbase + koff + i * 16 * kstride);  // keys key0 + 16 i
-        const int voff = key0 * 4 * kstride + ch * 8;  // 4 keys 4*key0 + 64 i .. +3, dims 8 ch .. +7
-        const int vp = vt_pos(key0 * 4);               // < 64, a multiple of 4
-        bf16x8 rows[2][4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) rows[i][rr] = *(const bf16x8*)(vbase + voff + (64 * i + rr) * kstride);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) *(uint4*)(ks + swz_chunk_offset(key0 + 16 * i, ch)) = kv[i];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                bf16x4 w;
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) w[rr] = rows[i][rr][e];
-                *(bf16x4*)(vts + swz_chunk_offset(ch * 8 + e, (vp >> 3) + 8 * i) + (vp & 7)) = w;
-            }
+        stage_kv_tile(k, v, ks, vts, b, g, c, N, Hkv, tid);
     };
     // Queries of one row tile: row t of the lane's head. Rows past the tile's
     // last entry read position c*128 (a valid row) and are never written.
@@ -215,10 +184,11 @@ __global__ __launch_bounds__(256, 2) void k_sparse_partial(
                 }
         l = wave_sum_xor32(l);
         const float inv = 1.0f / l;
-        // partial O record layout: [(b*Nc + t - p0)*top_k + slot][chunk][head][8 dims], chunk = h*8 + dt*2 + i0/8
+        // partial O record layout: [(b*Nc + t - p0)*top_k + slot][g][chunk][G heads][8 dims],
+        // chunk = h*8 + dt*2 + i0/8
         const size_t rec2 = ((size_t)b * Nc + (ri.t - p0)) * top_k + ri.slot;
-        __bf16* dst = part_o + ((rec2 * 16 + h * 8) * Hq + qhead) * 8;
-        const size_t chunk_stride = (size_t)Hq * 8;
+        __bf16* dst = part_o + rec2 * 16 * Hq * 8 + ((size_t)(g * 16 + h * 8) * G + hh) * 8;
+        const size_t chunk_stride = (size_t)G * 8;
 
         // O^T = V^T P^T, 64 dims at a time: 128 dims x 32 rows per wave. The records
         // are read once, by the combine after this kernel, so they are written with

@@ -309,7 +309,7 @@ hipError_t run_sparse_attn(const void* q, const void* k, const void* v, const in
         c.Nc = d.N - p0 < chunk ? d.N - p0 : chunk;
         e = launch_sparse_plan(block_idx, ws, c, false, stream);
         if (e == hipSuccess) e = launch_sparse_partial(q, k, v, ws, c, stream);
-        if (e == hipSuccess) e = launch_sparse_combine(block_idx, o, lse, ws, c, stream);
+        if (e == hipSuccess) e = launch_sparse_combine(q, k, v, block_idx, o, lse, ws, c, stream);
     }
     return e;
 }
@@ -410,15 +410,16 @@ msa_status msa_sparse_attn_partial(const msa_shape* shape, const void* q, const 
     return hip_status(launch_sparse_partial(q, k, v, carve_sparse_ws(workspace, d), d, stream));
 }
 
-msa_status msa_sparse_attn_combine(const msa_shape* shape, const int32_t* block_idx, void* o, float* lse,
-                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+msa_status msa_sparse_attn_combine(const msa_shape* shape, const void* q, const void* k, const void* v,
+                                   const int32_t* block_idx, void* o, float* lse, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
     Dims d;
     const msa_status st = check_shape(shape, &d);
     if (st != MSA_OK) return st;
-    if (!block_idx || !o || !lse) return MSA_ERR_INVALID_ARG;
+    if (!q || !k || !v || !block_idx || !o || !lse) return MSA_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < sparse_ws_bytes(d)) return MSA_ERR_WORKSPACE;
     (void)hipGetLastError();
-    return hip_status(launch_sparse_combine(block_idx, o, lse, carve_sparse_ws(workspace, d), d, stream));
+    return hip_status(launch_sparse_combine(q, k, v, block_idx, o, lse, carve_sparse_ws(workspace, d), d, stream));
 }
 
 msa_status msa_fwd(const msa_shape* shape, const void* q_idx, const void* k_idx, const void* q, const void* k,

@@ -71,6 +71,61 @@ __device__ __forceinline__ float wave_sum_xor32(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Position p of a key inside a V^T row in LDS: bits 2 and 3 of the key index are
+// swapped, so that the 8 keys a lane feeds to one PV MFMA step (the keys its S^T
+// registers hold) sit in one 16-byte chunk. The map is its own inverse.
+__device__ __forceinline__ int vt_pos(int key) {
+    return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
+// Stage key block c of KV head g of batch b in LDS for the 32x32 MFMA attention step:
+// K row-major (ks[key][dim]) and V transposed (vts[dim][vt_pos(key)]), both with
+// swz_chunk_offset. K and V are [B, N, H_kv, 128] bf16. Threads tid = 0..255 take part
+// (each loads 8 K chunks and 8 V chunks); the caller synchronises before and after.
+__device__ __forceinline__ void stage_kv_tile(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+                                              __bf16* ks, __bf16* vts, int b, int g, int c, int N, int Hkv,
+                                              int tid) {
+    const size_t tile_off = (((size_t)b * N + (size_t)c * kBlock) * Hkv + g) * kDim;
+    const __bf16* kbase = k + tile_off;
+    const __bf16* vbase = v + tile_off;
+    const int kstride = Hkv * kDim;
+    const int key0 = tid >> 4, ch = tid & 15;
+    const int koff = key0 * kstride + ch * 8;
+    uint4 kv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kv[i] = *(const uint4*)(kbase + koff + i * 16 * kstride);  // keys key0 + 16 i
+    const int voff = key0 * 4 * kstride + ch * 8;  // 4 keys 4*key0 + 64 i .. +3, dims 8 ch .. +7
+    const int vp = vt_pos(key0 * 4);               // < 64, a multiple of 4
+    bf16x8 rows[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) rows[i][rr] = *(const bf16x8*)(vbase + voff + (64 * i + rr) * kstride);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *(uint4*)(ks + swz_chunk_offset(key0 + 16 * i, ch)) = kv[i];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            bf16x4 w;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) w[rr] = rows[i][rr][e];
+            *(bf16x4*)(vts + swz_chunk_offset(ch * 8 + e, (vp >> 3) + 8 * i) + (vp & 7)) = w;
+        }
+}
+
+// A raw buffer descriptor over `bytes` bytes at p (p and bytes the same in every lane;
+// they are read from the first lane so that the descriptor sits in scalar registers).
+// Loads at offsets past `bytes` return 0 without touching memory.
+constexpr int kRawBufferFlags = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int bytes) {
+    const uint64_t a = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0,
+                                             __builtin_amdgcn_readfirstlane(bytes), kRawBufferFlags);
+}
+
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
     uint32_t lo = __shfl_xor((uint32_t)x, m, 64);
     uint32_t hi = __shfl_xor((uint32_t)(x >> 32), m, 64);

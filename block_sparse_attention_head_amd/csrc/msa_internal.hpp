@@ -61,7 +61,7 @@ struct SparseWs {
     int32_t* cursor;    // [B*Hkv*nblk]    next free place per tile (unordered scatter)
     int32_t* wgoff;     // [B*Hkv, rev_groups(N), nblk] per position range: entries, then first entry
     int32_t* entries;   // [B*Hkv*N*top_k] (t << 8 | slot), grouped by tile
-    void* part_o;       // bf16 [B, N, top_k, Hq, 128] normalised partial outputs (lane order)
+    void* part_o;       // bf16 [B, N, top_k, Hkv, 16, G, 8] normalised partial outputs (lane order)
     float* part_lse;    // fp32 [B, N, top_k, Hq]      partial log-sum-exp
 };
 // Position ranges (workgroups) per (b, g) of the reverse-index scatter.
@@ -69,16 +69,22 @@ int rev_groups(int N);
 size_t sparse_ws_bytes(const Dims& d);
 SparseWs carve_sparse_ws(void* base, const Dims& d);
 
+// Whether the forward's combine computes the (row, own block) pairs itself (then the
+// unordered plan leaves them out and the partial kernel never sees them).
+bool combine_folds_local(const Dims& d);
 // Reverse index and work list. `canonical`: the entry order inside a tile is a
-// function of block_idx alone (the backward needs it); otherwise it is unordered.
+// function of block_idx alone and every valid entry is listed (the backward needs
+// both); otherwise it is unordered and leaves out the local block when
+// combine_folds_local(d).
 hipError_t launch_sparse_plan(const int32_t* block_idx, const SparseWs& ws, const Dims& d, bool canonical,
                               hipStream_t stream);
 hipError_t launch_sparse_partial(const void* q, const void* k, const void* v, const SparseWs& ws, const Dims& d,
                                  hipStream_t stream);
-// Dynamic LDS bytes of the combine kernel (must stay within 64 KB).
+// Dynamic LDS bytes of the records-only combine kernel (must stay within 64 KB).
 size_t combine_lds_bytes(const Dims& d);
-hipError_t launch_sparse_combine(const int32_t* block_idx, void* o, float* lse, const SparseWs& ws, const Dims& d,
-                                 hipStream_t stream);
+// The combine; reads q, k and v when combine_folds_local(d) (the local block's attention).
+hipError_t launch_sparse_combine(const void* q, const void* k, const void* v, const int32_t* block_idx, void* o,
+                                 float* lse, const SparseWs& ws, const Dims& d, hipStream_t stream);
 
 // Workspace of the sparse attention backward: the forward's plan (reverse index
 // and work items, part_o / part_lse unused) followed by the backward's buffers.

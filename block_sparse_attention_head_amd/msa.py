@@ -58,7 +58,7 @@ _SIGNATURES = {
     "msa_sparse_attn_fwd": [_S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "msa_sparse_attn_plan": [_S, _P, _P, ctypes.c_size_t, _P],
     "msa_sparse_attn_partial": [_S, _P, _P, _P, _P, ctypes.c_size_t, _P],
-    "msa_sparse_attn_combine": [_S, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "msa_sparse_attn_combine": [_S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "msa_fwd": [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "msa_sparse_attn_bwd": [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "msa_index_topk": [_S, _P, _P, _P, _P, ctypes.c_size_t, _P],
@@ -274,10 +274,11 @@ def sparse_attn_partial(shape: MsaShape, q, k, v, workspace: torch.Tensor) -> No
                                          workspace.numel(), _stream(q.device)))
 
 
-def sparse_attn_combine(shape: MsaShape, block_idx, o, lse, workspace: torch.Tensor) -> None:
+def sparse_attn_combine(shape: MsaShape, q, k, v, block_idx, o, lse, workspace: torch.Tensor) -> None:
+    """Merge of the slot partials into o and lse; q, k, v are read for the queries' own blocks."""
     _check("msa_sparse_attn_combine",
-           lib().msa_sparse_attn_combine(ctypes.byref(shape), _ptr(block_idx), _ptr(o), _ptr(lse), _ptr(workspace),
-                                         workspace.numel(), _stream(o.device)))
+           lib().msa_sparse_attn_combine(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(o),
+                                         _ptr(lse), _ptr(workspace), workspace.numel(), _stream(o.device)))
 
 
 def msa_fwd(q_idx, k_idx, q, k, v, top_k: int, softmax_scale: float, block_idx=None, o=None, lse=None,

@@ -13,6 +13,10 @@ work the method needs, not what a particular kernel happens to do:
                    K and V of the block once; read the reverse-index entries
   combine          read every partial O row and LSE, read the selection rows,
                    write O (bf16) and LSE (fp32)
+  with the local block in the combine (top_k <= 16, as the library does): the
+                   (row, own block) pairs leave the partial phase (every query
+                   has exactly one); the combine reads the query rows and K and
+                   V of every block once instead of their records
 
 Decode (one query per sequence, length L, t = L - 1, c_loc = t // B_k):
   index            read the L cached index keys (bf16) and the H_idx index
@@ -129,18 +133,33 @@ def pair_rows(s: Shape) -> int:
     return s.batch * s.h_kv * sum_valid_blocks(s.seqlen, s.top_k, s.block) * s.group
 
 
+FOLD_MAX_TOP_K = 16  # the library's combine computes the local block for top_k up to this
+
+
+def folds_local(s: Shape) -> bool:
+    return s.top_k <= FOLD_MAX_TOP_K
+
+
 def partial_bytes(s: Shape) -> float:
     rows = pair_rows(s)
     tiles = s.batch * s.h_kv * s.nblk
     entries = s.batch * s.h_kv * sum_valid_blocks(s.seqlen, s.top_k, s.block)
+    if folds_local(s):
+        rows -= s.batch * s.h_q * s.seqlen
+        entries -= s.batch * s.h_kv * s.seqlen
     return (rows * (s.head_dim * BF16 + s.head_dim * BF16 + FP32)
             + tiles * 2 * s.block * s.head_dim * BF16 + entries * INT32)
 
 
 def combine_bytes(s: Shape) -> float:
     rows = pair_rows(s)
+    extra = 0
+    if folds_local(s):
+        rows -= s.batch * s.h_q * s.seqlen
+        extra = (s.batch * s.seqlen * s.h_q * s.head_dim * BF16
+                 + s.batch * s.h_kv * s.nblk * 2 * s.block * s.head_dim * BF16)
     return (rows * (s.head_dim * BF16 + FP32) + s.batch * s.h_kv * s.seqlen * s.top_k * INT32
-            + s.batch * s.seqlen * s.h_q * s.head_dim * BF16 + s.batch * s.h_q * s.seqlen * FP32)
+            + s.batch * s.seqlen * s.h_q * s.head_dim * BF16 + s.batch * s.h_q * s.seqlen * FP32 + extra)
 
 
 def per_token_compute_ratio(N: int, h_q: int, h_idx: int, d: int, d_idx: int, top_k: int, block: int) -> float:

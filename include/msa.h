@@ -179,13 +179,20 @@ msa_status msa_sparse_attn_fwd(const msa_shape* shape, const void* q, const void
  *   partial: per (key block, KV head) tile, softmax attention of the gathered
  *            queries over that block, written to per-slot partial outputs;
  *   combine: merge of the partials into o and lse ([MSA summary] "GPU kernel
- *            co-design": two-phase forward with a global softmax combine). */
+ *            co-design": two-phase forward with a global softmax combine).
+ * With top_k <= 16 the combine also computes each query's attention to its own
+ * (local) block, the causal block that every position of a block shares, from
+ * q, k and v: the plan then leaves those (query, block) pairs out of the
+ * partial phase. q, k and v are the tensors msa_sparse_attn_fwd takes (device,
+ * not modified); the combine requires them non-null for every top_k
+ * (MSA_ERR_INVALID_ARG otherwise). */
 msa_status msa_sparse_attn_plan(const msa_shape* shape, const int32_t* block_idx, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 msa_status msa_sparse_attn_partial(const msa_shape* shape, const void* q, const void* k, const void* v,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
-msa_status msa_sparse_attn_combine(const msa_shape* shape, const int32_t* block_idx, void* o, float* lse,
-                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+msa_status msa_sparse_attn_combine(const msa_shape* shape, const void* q, const void* k, const void* v,
+                                   const int32_t* block_idx, void* o, float* lse, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 /* The whole forward: msa_index_topk into `block_idx`, then msa_sparse_attn_fwd
  * into `o` and `lse` ([Flash-MSA] "Forward": index branch

@@ -145,8 +145,10 @@ int main() {
     EXPECT_EQ(msa_sparse_attn_plan(&ok, PI, P, fwd_ws - 1, S), MSA_ERR_WORKSPACE);
     EXPECT_EQ(msa_sparse_attn_partial(&ok, P, nullptr, P, P, fwd_ws, S), MSA_ERR_INVALID_ARG);
     EXPECT_EQ(msa_sparse_attn_partial(&ok, P, P, P, nullptr, fwd_ws, S), MSA_ERR_WORKSPACE);
-    EXPECT_EQ(msa_sparse_attn_combine(&ok, PI, nullptr, PF, P, fwd_ws, S), MSA_ERR_INVALID_ARG);
-    EXPECT_EQ(msa_sparse_attn_combine(&ok, PI, P, PF, P, 0, S), MSA_ERR_WORKSPACE);
+    EXPECT_EQ(msa_sparse_attn_combine(&ok, P, P, P, PI, nullptr, PF, P, fwd_ws, S), MSA_ERR_INVALID_ARG);
+    EXPECT_EQ(msa_sparse_attn_combine(&ok, nullptr, P, P, PI, P, PF, P, fwd_ws, S), MSA_ERR_INVALID_ARG);
+    EXPECT_EQ(msa_sparse_attn_combine(&ok, P, P, nullptr, PI, P, PF, P, fwd_ws, S), MSA_ERR_INVALID_ARG);
+    EXPECT_EQ(msa_sparse_attn_combine(&ok, P, P, P, PI, P, PF, P, 0, S), MSA_ERR_WORKSPACE);
     EXPECT_EQ(msa_fwd(&ok, P, P, P, P, P, PI, P, nullptr, P, fwd_ws, S), MSA_ERR_INVALID_ARG);
     EXPECT_EQ(msa_fwd(&ok, P, P, P, P, P, PI, P, PF, nullptr, 0, S), MSA_ERR_WORKSPACE);
     EXPECT_EQ(msa_fwd(&ok, P, P, P, P, P, PI, P, PF, P, 255, S), MSA_ERR_WORKSPACE);

@@ -119,7 +119,11 @@ def test_null_pointers_rejected_before_any_launch(m):
     assert lib.msa_fwd(ctypes.byref(s), one, one, one, one, one, one, one, one, one, 10, P(0)) == 3
     assert lib.msa_sparse_attn_plan(ctypes.byref(s), one, one, 10, P(0)) == 3
     assert lib.msa_sparse_attn_partial(ctypes.byref(s), one, one, one, one, 10, P(0)) == 3
-    assert lib.msa_sparse_attn_combine(ctypes.byref(s), one, one, one, one, 10, P(0)) == 3
+    assert lib.msa_sparse_attn_combine(ctypes.byref(s), one, one, one, one, one, one, one, 10, P(0)) == 3
+    for i in range(6):  # each of q, k, v, block_idx, o, lse
+        args = [one] * 6
+        args[i] = P(0)
+        assert lib.msa_sparse_attn_combine(ctypes.byref(s), *args, one, 1 << 40, P(0)) == 1
     assert lib.msa_fwd(None, one, one, one, one, one, one, one, one, one, 10, P(0)) == 1
     assert lib.msa_index_topk(ctypes.byref(s), P(0), one, one, one, 1 << 40, P(0)) == 1
     big = m.make_shape(batch=1, seqlen=4096, h_q=4, h_kv=1, top_k=18, softmax_scale=0.1)

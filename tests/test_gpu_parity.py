@@ -453,6 +453,25 @@ def test_invalid_and_empty_selections(msa):
     check_attn(og, lg, ro, rl, "invalid-entries")
 
 
+def test_sparse_attention_past_sixteen_slots(msa):
+    # top_k > 16: every slot, the query's own block included, goes through the partial
+    # phase and the records-only combine (the local block is computed in the combine only
+    # up to 16 slots); caller selections with padding and repeats, against the oracle
+    w = small_workload(4096, 16, 2, 20, seed=11)
+    x = make_inputs(w)
+    rng = np.random.default_rng(3)
+    t = np.arange(w.seqlen)
+    sel = rng.integers(-2, w.nblk, size=(1, 2, w.seqlen, 20)).astype(np.int32)
+    sel[..., 0] = t // 128  # the local block, as the method's selections hold it
+    sel[0, 1, 2000, 5] = sel[0, 1, 2000, 6] = 3  # a repeated block counts twice
+    xg = _gpu(x)
+    _say(w.name, "20 slots")
+    o, lse = msa.sparse_attn_fwd(xg["q"], xg["k"], xg["v"], torch.from_numpy(sel).to(DEV), w.softmax_scale)
+    torch.cuda.synchronize()
+    ro, rl = O.sparse_attention(x["q"], x["k"], x["v"], sel, w.softmax_scale)
+    check_attn(to_np(o), to_np(lse), ro, rl, "20-slots")
+
+
 def test_deterministic_and_stage_calls_match(msa):
     w = WORKLOADS["n8k"]
     x = make_inputs(w)
@@ -466,7 +485,7 @@ def test_deterministic_and_stage_calls_match(msa):
     lse3 = torch.empty_like(r1[2])
     msa.sparse_attn_plan(shape, r1[0], ws)
     msa.sparse_attn_partial(shape, xg["q"], xg["k"], xg["v"], ws)
-    msa.sparse_attn_combine(shape, r1[0], o3, lse3, ws)
+    msa.sparse_attn_combine(shape, xg["q"], xg["k"], xg["v"], r1[0], o3, lse3, ws)
     torch.cuda.synchronize()
     for a, b in zip(r1, r2):
         assert torch.equal(a, b)

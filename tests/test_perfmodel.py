@@ -41,6 +41,24 @@ def test_flops_of_the_128k_workload():
     assert P.pair_rows(s) == 4 * 16 * sum(min(16, t // 128 + 1) for t in range(131072))
 
 
+def test_stage_bytes_with_the_local_block_in_the_combine():
+    # top_k <= 16: each query's own block leaves the partial phase (one row per query
+    # head and position), and the combine reads the query rows and each block's K/V once
+    s = P.Shape(batch=1, seqlen=4096, h_q=8, h_kv=2, top_k=4)
+    pairs = 8 * sum(min(4, t // 128 + 1) for t in range(4096))
+    entries = 2 * sum(min(4, t // 128 + 1) for t in range(4096))
+    kv = 2 * 32 * 2 * 128 * 128 * 2
+    local = 8 * 4096
+    assert P.partial_bytes(s) == (pairs - local) * (256 + 256 + 4) + kv + (entries - 2 * 4096) * 4
+    out = 4096 * 8 * (256 + 4)
+    sel = 2 * 4096 * 4 * 4
+    assert P.combine_bytes(s) == (pairs - local) * (256 + 4) + sel + out + 4096 * 8 * 256 + kv
+    # past 16 slots every pair goes through the partial phase and its record
+    t = P.Shape(batch=1, seqlen=4096, h_q=8, h_kv=2, top_k=17)
+    pt = 8 * sum(min(17, u // 128 + 1) for u in range(4096))
+    assert P.combine_bytes(t) == pt * (256 + 4) + 2 * 4096 * 17 * 4 + out
+
+
 def test_decode_bytes_closed_form():
     from block_sparse_attention_head_amd.perfmodel import decode_bytes
 
