@@ -567,7 +567,7 @@ def main(argv=None) -> int:
             r.update({"achieved": round(ach, 2), "unit": unit, "peak": peak, "frac": round(ach / peak, 4),
                       "kernel": STAGE_KERNEL[name][0]})
         stage_report[name] = r
-    stage_report["partial"]["tflops"] = round(main_f / 1e12 / (stage_ms["partial"] / 1e3), 2)
+    stage_report["partial"]["tflops"] = round(P.partial_flops(s) / 1e12 / (stage_ms["partial"] / 1e3), 2)
     main_ms = stage_ms["plan"] + stage_ms["partial"] + stage_ms["combine"]
 
     dom = max(work, key=lambda n: stage_ms[n])

@@ -140,6 +140,18 @@ def folds_local(s: Shape) -> bool:
     return s.top_k <= FOLD_MAX_TOP_K
 
 
+def local_block_flops(s: Shape) -> float:
+    """The main attention's FLOP on each query's own block: 4 d per query head and key of
+    that block up to the position."""
+    keys = sum(r * (r + 1) // 2 for r in (min(s.block, s.seqlen - c * s.block) for c in range(s.nblk)))
+    return 4.0 * s.head_dim * s.h_q * s.batch * keys
+
+
+def partial_flops(s: Shape) -> float:
+    """The main attention's FLOP in the partial phase (all of it unless the combine takes the local block)."""
+    return main_flops(s) - (local_block_flops(s) if folds_local(s) else 0.0)
+
+
 def partial_bytes(s: Shape) -> float:
     rows = pair_rows(s)
     tiles = s.batch * s.h_kv * s.nblk

@@ -53,10 +53,14 @@ def test_stage_bytes_with_the_local_block_in_the_combine():
     out = 4096 * 8 * (256 + 4)
     sel = 2 * 4096 * 4 * 4
     assert P.combine_bytes(s) == (pairs - local) * (256 + 4) + sel + out + 4096 * 8 * 256 + kv
+    # the own block's keys up to each position: 128 * 129 / 2 per block of positions
+    assert P.local_block_flops(s) == 4 * 128 * 8 * 32 * (128 * 129 // 2)
+    assert P.partial_flops(s) == P.main_flops(s) - P.local_block_flops(s)
     # past 16 slots every pair goes through the partial phase and its record
     t = P.Shape(batch=1, seqlen=4096, h_q=8, h_kv=2, top_k=17)
     pt = 8 * sum(min(17, u // 128 + 1) for u in range(4096))
     assert P.combine_bytes(t) == pt * (256 + 4) + 2 * 4096 * 17 * 4 + out
+    assert P.partial_flops(t) == P.main_flops(t)
 
 
 def test_decode_bytes_closed_form():
