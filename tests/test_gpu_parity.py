@@ -441,6 +441,9 @@ def test_invalid_and_empty_selections(msa):
     sel = rng.integers(-3, 10, size=(1, 2, w.seqlen, 4)).astype(np.int32)
     sel[0, 0, 300] = -1
     sel[0, 1, 900] = [7, 100, -1, -5]
+    sel[0, 0, 500] = [3, 3, 1, -1]  # the query's own block (500 // 128 = 3) twice
+    sel[0, 1, 640] = [2, 0, 2, 4]   # an earlier block twice; its own block (5) absent, 4 is
+    sel[0, 0, 130] = [9, 8, 2, 1]   # only later blocks and its own (1): one valid entry
     xg = _gpu(x)
     _say(w.name, "invalid entries")
     o, lse = msa.sparse_attn_fwd(xg["q"], xg["k"], xg["v"], torch.from_numpy(sel).to(DEV), w.softmax_scale)
