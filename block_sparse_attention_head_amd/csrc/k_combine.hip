@@ -324,16 +324,18 @@ __global__ __launch_bounds__(512) void k_combine(
         // both lanes of a row hold the same values: lane half h writes half of them
 #pragma unroll
         for (int e = 0; e < kFoldWts / 2; ++e) ww[l32 * kFoldWts + h * (kFoldWts / 2) + e] = wv[h * (kFoldWts / 2) + e];
-        lse[((size_t)b * Hq + qhead) * N + t] = M + logf(L);
+        lse[((size_t)b * Hq + qhead) * N + t] = M + logf(L);  // both lanes of the row: the same value
+        // LDS operations of one wave complete in order; the fences keep the compiler from
+        // moving this wave's LDS accesses across the hand-over between lanes
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // ---- B: piece p = it * 64 + lane is (row, chunk): the wave's rows come in runs
-        // of 2^gw heads of one position (all G heads, or 32 of them when G > 32), and
-        // p takes a run's heads fastest, then the chunks, then the runs
-        // the record loads of piece it + 1 are issued before piece it is summed; a piece's
-        // weights are read from LDS when it is summed
+        // ---- B: piece p = it * 64 + lane is (row, chunk). The wave's rows come in runs
+        // of 2^gw heads of one position (all G heads, or 32 of them when G > 32), and p
+        // takes a run's heads fastest, then the chunks, then the runs. The record loads of
+        // piece it + 1 are issued before piece it is summed; a piece's weights are read
+        // from LDS when it is summed.
         bf16x8 x[2][kFoldSlots];
         auto issue = [&](int it, bf16x8 (&xb)[kFoldSlots]) {
             const int pc = it * 64 + lane;
