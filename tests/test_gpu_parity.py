@@ -475,6 +475,25 @@ def test_sparse_attention_past_sixteen_slots(msa):
     check_attn(to_np(o), to_np(lse), ro, rl, "20-slots")
 
 
+def test_own_block_in_the_combine_matches_the_records_path(msa):
+    # the same selection through the two combine paths: 16 slots (the combine computes each
+    # query's own block) and the same 16 plus one padding slot (every slot through the
+    # partial phase and its record); both round per-slot outputs to bf16 and merge in fp32
+    w = small_workload(4096, 32, 2, 16, seed=23)
+    x = make_inputs(w)
+    xg = _gpu(x)
+    _say(w.name, "own block: combine against records")
+    bi = msa.index_topk(xg["q_idx"], xg["k_idx"], 16)
+    o1, l1 = msa.sparse_attn_fwd(xg["q"], xg["k"], xg["v"], bi, w.softmax_scale)
+    pad = torch.full(bi.shape[:-1] + (1,), -1, dtype=torch.int32, device=DEV)
+    o2, l2 = msa.sparse_attn_fwd(xg["q"], xg["k"], xg["v"], torch.cat([bi, pad], -1).contiguous(), w.softmax_scale)
+    torch.cuda.synchronize()
+    assert (o1.float() - o2.float()).abs().max().item() <= 1e-2
+    assert (l1 - l2).abs().max().item() <= 1e-5
+    ro, rl = O.sparse_attention(x["q"], x["k"], x["v"], to_np(bi), w.softmax_scale)
+    check_attn(to_np(o1), to_np(l1), ro, rl, "own-block")
+
+
 def test_deterministic_and_stage_calls_match(msa):
     w = WORKLOADS["n8k"]
     x = make_inputs(w)
