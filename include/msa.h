@@ -158,7 +158,9 @@ msa_status msa_index_topk(const msa_shape* shape, const void* q_idx, const void*
  * with no valid entry gives o = 0 and lse = -inf. Runs KV-outer: each
  * (key block, KV head) tile gathers the queries that selected it ([MSA summary]
  * "GPU kernel co-design"), writes per-slot partial results into the workspace,
- * and a combine pass merges them. Deterministic (no floating-point atomics).
+ * and a combine pass merges them; with top_k <= 16 the combine itself computes
+ * each query's attention to its own block (the causal block every position of
+ * a block shares). Deterministic (no floating-point atomics).
  * Any workspace that holds the partials of at least 128 query positions is
  * accepted: the positions are then processed in as many chunks as it takes
  * (each chunk reads only its rows' block indices; all K/V stay where they are),
